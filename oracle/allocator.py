@@ -1,0 +1,145 @@
+"""Reference model of the refcounted block manager and slot bookkeeping.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+What the pages fix ([P2]):
+
+* "PagedAttention：把操作系统的虚拟内存搬进 GPU": blocks have one fixed size,
+  are handed out on demand as tokens are generated (so a sequence of length L
+  holds ceil(L / BS) blocks), suffer no external fragmentation (any free block
+  serves any request, so a request for n blocks can succeed exactly when n are
+  free), and one physical block may back logical blocks of several sequences
+  (beam search, shared prompt prefixes / prefix caching).
+* "连续批处理：别再等最慢的那个请求了": every scheduler iteration frees the
+  block tables of finished requests, reads the number of free blocks, admits
+  waiting requests while they can be allocated, then runs one decode step.
+
+What the pages leave open, and the reading taken (this library's policy):
+
+* free ids sit on a LIFO stack that starts as [N-1, ..., 1, 0], so the first
+  allocations return 0, 1, 2, ...; alloc pops, a block whose count reaches 0 is
+  pushed back in argument order;
+* sharing is a reference count per block: alloc sets it to 1, incref adds 1,
+  free subtracts 1;
+* every call validates all of its arguments before it changes anything, and
+  fails as a whole: INVALID (bad argument), OOM (too few free blocks), STATE
+  (freeing a free block, sharing a free block, appending into a block that is
+  shared - there is no copy-on-write);
+* a sequence grows one token at a time: the token at position pos goes to slot
+  table[pos // BS] * BS + pos % BS, and a new block is taken from the stack
+  when pos % BS == 0; sequences of one call are served in index order.
+"""
+
+OK, INVALID, OOM, STATE = 0, -1, -2, -3
+
+
+class AllocError(Exception):
+    def __init__(self, code, msg):
+        super().__init__(msg)
+        self.code = code
+
+
+class AllocatorModel:
+    def __init__(self, num_blocks: int, block_size: int = 16):
+        if num_blocks < 0 or block_size <= 0:
+            raise AllocError(INVALID, "bad pool size")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free_stack = list(range(num_blocks - 1, -1, -1))
+        self.ref = [0] * num_blocks
+
+    # -- block manager -------------------------------------------------------
+    def num_free(self) -> int:
+        return len(self.free_stack)
+
+    def refcount(self, block_id: int) -> int:
+        if 0 <= block_id < self.num_blocks:
+            return self.ref[block_id]
+        return -1
+
+    def alloc(self, n: int) -> list:
+        if n < 0:
+            raise AllocError(INVALID, "negative count")
+        if n > len(self.free_stack):
+            raise AllocError(OOM, "not enough free blocks")
+        ids = []
+        for _ in range(n):
+            b = self.free_stack.pop()
+            self.ref[b] = 1
+            ids.append(b)
+        return ids
+
+    def _check_ids(self, ids):
+        for b in ids:
+            if not 0 <= b < self.num_blocks:
+                raise AllocError(INVALID, "block id out of range")
+
+    def free(self, ids) -> None:
+        ids = [int(b) for b in ids]
+        self._check_ids(ids)
+        need = {}
+        for b in ids:
+            need[b] = need.get(b, 0) + 1
+        for b, c in need.items():
+            if self.ref[b] < c:
+                raise AllocError(STATE, "freeing a block more times than it is held")
+        for b in ids:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free_stack.append(b)
+
+    def incref(self, ids) -> None:
+        ids = [int(b) for b in ids]
+        self._check_ids(ids)
+        for b in ids:
+            if self.ref[b] == 0:
+                raise AllocError(STATE, "sharing a free block")
+        for b in ids:
+            self.ref[b] += 1
+
+    # -- per-sequence bookkeeping -------------------------------------------
+    def fork(self, src_row, dst_row, n_blocks: int) -> None:
+        """dst_row[:n] = src_row[:n] and take one more reference on each id."""
+        if n_blocks < 0 or n_blocks > len(src_row) or n_blocks > len(dst_row):
+            raise AllocError(INVALID, "bad block count")
+        ids = [int(b) for b in src_row[:n_blocks]]
+        self.incref(ids)
+        for j, b in enumerate(ids):
+            dst_row[j] = b
+
+    def extend(self, tables, cur_lens, new_lens) -> list:
+        """Grow sequence i from cur_lens[i] to new_lens[i] tokens.
+
+        tables: list of mutable rows (one per sequence, all of the same width).
+        Returns the slots of the new tokens, sequence by sequence, in position
+        order. Fails as a whole (INVALID, STATE or OOM) with nothing changed.
+        """
+        bs = self.block_size
+        num_seqs = len(tables)
+        if len(cur_lens) != num_seqs or len(new_lens) != num_seqs:
+            raise AllocError(INVALID, "length arrays do not match")
+        needed = 0
+        for i in range(num_seqs):
+            cur, new = int(cur_lens[i]), int(new_lens[i])
+            width = len(tables[i])
+            if cur < 0 or new < cur or -(-new // bs) > width:
+                raise AllocError(INVALID, "bad lengths")
+            if new > cur and cur % bs != 0:
+                b = int(tables[i][cur // bs])
+                if not 0 <= b < self.num_blocks:
+                    raise AllocError(INVALID, "block id out of range")
+                if self.ref[b] != 1:
+                    raise AllocError(STATE, "appending into a free or shared block")
+            needed += -(-new // bs) - (-(-cur // bs))
+        if needed > len(self.free_stack):
+            raise AllocError(OOM, "not enough free blocks")
+        slots = []
+        for i in range(num_seqs):
+            row = tables[i]
+            for pos in range(int(cur_lens[i]), int(new_lens[i])):
+                if pos % bs == 0:
+                    b = self.free_stack.pop()
+                    self.ref[b] = 1
+                    row[pos // bs] = b
+                slots.append(int(row[pos // bs]) * bs + pos % bs)
+        return slots
