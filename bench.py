@@ -1,0 +1,357 @@
+"""Benchmark of the paged decode step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload llama13b_layer]
+                    [--partition-size PS] [--replicas R] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch: append each
+sequence's new token into its slot (kv_cache_append), decode attention over
+the paged cache (paged_attn_decode) and, when partitioned, the split-K merge
+(paged_attn_reduce); for a multi-layer workload, all layers. Inputs are
+seeded synthetic tensors already resident in HBM. Steps rotate over R
+independent replicas of the workload (each with its own pool, tables and
+inputs) so that the KV a step reads was not read by the previous R-1 steps:
+with R * (pool bytes) well above the 256 MB last-level cache, no step is
+served from cache.
+
+Prints one JSON line. `value` is the whole step's KV-read throughput
+(algorithmic K+V bytes of the attended tokens / step time); `roofline` is the
+decode kernel alone, timed with HIP events on the stream it is launched on;
+`cpu_baseline` is the fp64 oracle on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+BS = 16
+
+
+# ------------------------------------------------------------- workload ----
+class Workload:
+    """One decode-step workload, product side: pool, tables, inputs, batch."""
+
+    def __init__(self, cfg, seed=0, device="cuda", partition_size=None, fill_byte=None,
+                 placement_seed=None, keep_cached_inputs=True):
+        import torch
+
+        import workloads as W
+        from paged_kv_cache_450_amd.runtime import DecodeBatch, PagedKVCache
+
+        self.cfg = cfg
+        self.seed = seed
+        lens = W.context_lengths(cfg, seed)
+        self.lens = lens
+        self.cached = lens - 1
+        nb = cfg.pool_blocks or blocks_needed(cfg, lens)
+        maxb = -(-int(lens.max()) // BS)
+        self.cache = PagedKVCache(cfg.layers, nb, cfg.kv_heads, cfg.head_dim, cfg.kv_dtype,
+                                  device, fill_byte=fill_byte)
+        pseed = seed if placement_seed is None else placement_seed
+        self.cache.permute_free_list(W.free_order(nb, cfg.name, pseed))
+        share_from, share_blocks = share_spec(cfg)
+        self.tables, self.start, self.slots_cached = self.cache.admit(
+            self.cached, maxb, share_from, share_blocks)
+        self.slots_new = self.cache.grow(self.tables, self.cached, lens)
+        self.partition_size = cfg.partition_size if partition_size is None else partition_size
+        qdt = {"f16": torch.float16, "bf16": torch.bfloat16}[cfg.q_dtype]
+        self.slots_cached_dev = torch.from_numpy(self.slots_cached).to(device)
+        self.slots_new_dev = torch.from_numpy(self.slots_new).to(device)
+        self.q, self.k_new, self.v_new = [], [], []
+        self.k_cached, self.v_cached = [], []
+        self.k_scale, self.v_scale = [], []
+        n_cached = int(self.slots_cached.size)
+        self.batch = DecodeBatch(self.cache, self.tables, lens, cfg.q_heads, qdt,
+                                 self.partition_size, device=device)
+        for layer in range(cfg.layers):
+            kc = W.kv_tokens(cfg, seed, layer, "k", "cached", n_cached, device)
+            vc = W.kv_tokens(cfg, seed, layer, "v", "cached", n_cached, device)
+            kn = W.kv_tokens(cfg, seed, layer, "k", "new", cfg.batch, device)
+            vn = W.kv_tokens(cfg, seed, layer, "v", "new", cfg.batch, device)
+            ks = vs = None
+            if cfg.kv_dtype == "e4m3":
+                ks, vs = W.fp8_scales([kc, kn]), W.fp8_scales([vc, vn])
+            # prefill: the cached tokens go into their slots
+            self.cache.append(layer, kc, vc, self.slots_cached_dev, ks, vs)
+            self.q.append(W.q_tensor(cfg, seed, layer, device))
+            self.k_new.append(kn)
+            self.v_new.append(vn)
+            self.k_scale.append(ks)
+            self.v_scale.append(vs)
+            if keep_cached_inputs:
+                self.k_cached.append(kc)
+                self.v_cached.append(vc)
+            else:
+                del kc, vc
+        self.out = [None] * cfg.layers
+
+    def kv_bytes(self) -> int:
+        """Algorithmic K+V bytes one decode step reads (attended tokens only)."""
+        esz = 1 if self.cfg.kv_dtype == "e4m3" else 2
+        return int(self.lens.astype(np.int64).sum()) * self.cfg.kv_heads * self.cfg.head_dim * \
+            2 * esz * self.cfg.layers
+
+    def append(self, layer, stream=None):
+        self.cache.append(layer, self.k_new[layer], self.v_new[layer], self.slots_new_dev,
+                          self.k_scale[layer], self.v_scale[layer], stream)
+
+    def decode(self, layer, stream=None):
+        self.batch.k_scale, self.batch.v_scale = self.k_scale[layer], self.v_scale[layer]
+        self.batch.decode(layer, self.q[layer], stream)
+
+    def reduce(self, stream=None):
+        self.batch.reduce(stream)
+
+    def step(self, layer=None, stream=None):
+        layers = range(self.cfg.layers) if layer is None else [layer]
+        for l in layers:
+            self.append(l, stream)
+            self.decode(l, stream)
+            self.reduce(stream)
+        return self.batch.out
+
+
+def blocks_needed(cfg, lens) -> int:
+    import workloads as W
+    n = int(sum(-(-int(l) // BS) for l in lens))
+    sh = W.sharers(cfg)
+    if len(sh) > 1:
+        n -= (len(sh) - 1) * (cfg.share_prefix_tokens // BS)
+    return n
+
+
+def share_spec(cfg):
+    import workloads as W
+    sh = W.sharers(cfg)
+    share_from = np.full(cfg.batch, -1, dtype=np.int64)
+    for i in sh[1:]:
+        share_from[i] = sh[0]
+    return share_from, cfg.share_prefix_tokens // BS
+
+
+# ------------------------------------------------------------ oracle side ----
+class OracleBookkeeping:
+    """The same admission procedure run on the oracle's AllocatorModel (used by
+    the CPU baseline and by the tests; never by the timed GPU path)."""
+
+    def __init__(self, cfg, seed=0, placement_seed=None):
+        from oracle import allocator as oalloc
+        import workloads as W
+
+        lens = W.context_lengths(cfg, seed)
+        cached = lens - 1
+        nb = cfg.pool_blocks or blocks_needed(cfg, lens)
+        maxb = -(-int(lens.max()) // BS)
+        model = oalloc.AllocatorModel(nb, BS)
+        model.alloc(nb)
+        pseed = seed if placement_seed is None else placement_seed
+        model.free([int(x) for x in W.free_order(nb, cfg.name, pseed)])
+        share_from, share_blocks = share_spec(cfg)
+        rows = [[-1] * maxb for _ in range(cfg.batch)]
+        start = np.zeros(cfg.batch, dtype=np.int32)
+        slots = []
+        for i in range(cfg.batch):
+            if share_from[i] >= 0:
+                model.fork(rows[share_from[i]], rows[i], share_blocks)
+                start[i] = share_blocks * BS
+            slots += model.extend([rows[i]], [int(start[i])], [int(cached[i])])
+        slots_new = model.extend(rows, [int(c) for c in cached], [int(x) for x in lens])
+        self.model = model
+        self.lens = lens
+        self.tables = np.array(rows, dtype=np.int32)
+        self.start = start
+        self.slots_cached = np.array(slots, dtype=np.int64)
+        self.slots_new = np.array(slots_new, dtype=np.int64)
+
+    def token_offsets(self):
+        """offs[i]:offs[i+1] index the cached-token inputs written for sequence i."""
+        counts = (self.lens.astype(np.int64) - 1 - self.start)
+        return np.concatenate([[0], np.cumsum(counts)])
+
+
+def cpu_baseline(w: Workload, budget_s: float):
+    """The fp64 oracle, as it is, on a bounded sample of the same workload:
+    whole sequences, in order, until about budget_s of CPU work. Only the
+    oracle's decode (gather through the table, softmax, PV) is timed; its
+    host pool is built by the oracle's own append, with the oracle's own
+    bookkeeping, from host copies of the seeded inputs."""
+    import torch
+
+    from oracle import attention as oattn
+    from oracle import pool as opool
+
+    cfg = w.cfg
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    ob = OracleBookkeeping(cfg, w.seed)
+    offs = ob.token_offsets()
+
+    def raw(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    nb = ob.model.num_blocks
+    per_layer = opool.pool_bytes(1, nb, BS, cfg.kv_heads, cfg.head_dim, cfg.kv_dtype)
+    buf = np.zeros(per_layer, dtype=np.uint8)
+    p6 = opool.view_pool(buf, 1, nb, BS, cfg.kv_heads, cfg.head_dim, cfg.kv_dtype)
+    ks = vs = None
+    if cfg.kv_dtype == "e4m3":
+        ks, vs = w.k_scale[0].cpu().numpy(), w.v_scale[0].cpu().numpy()
+    scale = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))
+    elapsed, done_bytes, seqs = 0.0, 0, 0
+    esz = opool.ESIZE[cfg.kv_dtype]
+    for i in range(cfg.batch):
+        if ob.start[i] > 0:
+            continue  # a prefix sharer; its prefix owner's tokens are not in this host pool
+        lo, hi = int(offs[i]), int(offs[i + 1])
+        opool.append(p6, 0, raw(w.k_cached[0][lo:hi]), raw(w.v_cached[0][lo:hi]), cfg.src_dtype,
+                     cfg.kv_dtype, ob.slots_cached[lo:hi], ks, vs)
+        opool.append(p6, 0, raw(w.k_new[0][i:i + 1]), raw(w.v_new[0][i:i + 1]), cfg.src_dtype,
+                     cfg.kv_dtype, ob.slots_new[i:i + 1], ks, vs)
+        q = opool.raw_to_f64(raw(w.q[0][i:i + 1]), cfg.q_dtype)
+        t0 = time.perf_counter()
+        oattn.paged_decode(p6, 0, q, ob.tables[i:i + 1], ob.lens[i:i + 1], scale, cfg.kv_dtype,
+                           ks, vs)
+        elapsed += time.perf_counter() - t0
+        done_bytes += int(ob.lens[i]) * cfg.kv_heads * cfg.head_dim * 2 * esz
+        seqs += 1
+        if elapsed >= budget_s:
+            break
+    return {
+        "value": round(done_bytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{seqs} of {cfg.batch} sequences of {cfg.name} layer 0 "
+                  f"({done_bytes / 1e6:.1f} MB of KV), fp64 numpy decode only, "
+                  f"{elapsed:.1f} s",
+        "seqs_per_s": round(seqs / elapsed, 3),
+    }
+
+
+# ------------------------------------------------------------------ main ----
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama13b_layer")
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--replicas", type=int, default=None,
+                    help="independent copies rotated over (default: enough for >= 2 GB)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the paged decode path has no multi-GPU "
+              "component here (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    cfg = W.CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    first = Workload(cfg, args.seed, "cuda", args.partition_size,
+                     keep_cached_inputs=not args.no_cpu_baseline)
+    pool_bytes = first.cache.nbytes
+    reps = args.replicas or max(1, min(8, math.ceil(2e9 / max(pool_bytes, 1))))
+    ws = [first] + [Workload(cfg, args.seed + r, "cuda", args.partition_size,
+                             keep_cached_inputs=False) for r in range(1, reps)]
+    kv_bytes = [w.kv_bytes() for w in ws]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        ws[i % reps].step(stream=stream)
+    torch.cuda.synchronize()
+
+    nl = cfg.layers
+    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * nl)]
+          for k in ("a0", "d0", "d1", "r1")}
+    t0 = time.perf_counter()
+    bytes_done = 0
+    for i in range(args.steps):
+        w = ws[i % reps]
+        bytes_done += kv_bytes[i % reps]
+        for layer in range(nl):
+            j = i * nl + layer
+            ev["a0"][j].record(stream)
+            w.append(layer, stream)
+            ev["d0"][j].record(stream)
+            w.decode(layer, stream)
+            ev["d1"][j].record(stream)
+            w.reduce(stream)
+            ev["r1"][j].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    n = args.steps * nl
+    append_us = sum(ev["a0"][j].elapsed_time(ev["d0"][j]) for j in range(n)) / n * 1e3
+    decode_us = sum(ev["d0"][j].elapsed_time(ev["d1"][j]) for j in range(n)) / n * 1e3
+    reduce_us = sum(ev["d1"][j].elapsed_time(ev["r1"][j]) for j in range(n)) / n * 1e3
+    ms_per_step = (t1 - t0) / args.steps * 1e3
+    gbs = bytes_done / (t1 - t0) / 1e9
+    per_layer_bytes = sum(kv_bytes) / reps / nl
+    decode_gbs = per_layer_bytes / (decode_us * 1e-6) / 1e9
+
+    result = {
+        "metric": "paged decode-attn KV-read GB/s (% HBM peak) + seqs/s at 13B shape, 1 GPU",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.kv_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "layers": cfg.layers, "batch": cfg.batch, "q_heads": cfg.q_heads,
+            "kv_heads": cfg.kv_heads, "head_dim": cfg.head_dim, "block_size": BS,
+            "kv_dtype": cfg.kv_dtype, "q_dtype": cfg.q_dtype,
+            "context_lens": list(cfg.lengths),
+            "partition_size": first.partition_size,
+            "replicas": reps, "pool_bytes_per_replica": pool_bytes,
+            "kv_bytes_per_step": int(sum(kv_bytes) / reps),
+            "seed": args.seed,
+        },
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(cfg.batch / (ms_per_step * 1e-3), 1),
+        "kernel_us": {"append": round(append_us, 3), "decode": round(decode_us, 3),
+                      "reduce": round(reduce_us, 3)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_kernel",
+            "achieved": round(decode_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

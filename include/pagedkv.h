@@ -1,0 +1,260 @@
+/*
+ * pagedkv.h - C ABI of a paged KV cache and paged decode attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *  [P2] "vLLM 推理加速原理详解：大模型服务吞吐量为何能提升 10 倍"
+ *       (fudengji.cn/article/275)
+ *       - "PagedAttention：把操作系统的虚拟内存搬进 GPU": fixed-size physical
+ *         blocks, a per-sequence page table mapping logically contiguous KV to
+ *         scattered blocks, allocation on demand, no external fragmentation,
+ *         one physical block shared by several sequences (beam search, common
+ *         prompt prefixes), and an attention kernel that reads KV from the
+ *         non-contiguous blocks.
+ *       - "连续批处理：别再等最慢的那个请求了": the block manager calls a
+ *         scheduler makes every iteration (free a finished request's table,
+ *         count free blocks, check and perform allocation).
+ *       - "vLLM 也不是银弹：真实部署中的坑", first pitfall: the cache is one
+ *         pool preallocated from GPU memory; third pitfall: FP8 KV cache.
+ *       - "从零开始：vLLM 部署的实战建议", step four: cache usage is a
+ *         monitored gauge (1 - free / total).
+ *  [P3] "突破大模型推理瓶颈：vLLM框架核心技术深度解剖与实战指南", section 2.4:
+ *       accumulation in FP32.
+ *
+ * Conventions for every call:
+ *  - Device pointers point to memory the caller allocated and owns (for
+ *    example through PyTorch). The library never allocates or frees device
+ *    memory and never synchronises the host with the device.
+ *  - GPU work is enqueued on the given stream and runs asynchronously;
+ *    stream = NULL means the default stream. Launch failures return
+ *    PKV_ERR_HIP.
+ *  - Every call checks all of its host-visible arguments before it changes
+ *    any state or launches anything; a call that fails changes nothing.
+ *    On failure pkv_last_error() describes the cause.
+ *  - No C++ exception crosses this interface.
+ *  - Pool objects are not thread-safe: one scheduler thread owns a pool.
+ *  - The context length L of a sequence counts every cached token, the
+ *    newest one included: a decode step first appends the new token at
+ *    position L-1, then attends over positions [0, L).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#pragma GCC visibility push(default)
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_INVALID = -1, /* bad argument: null pointer, unsupported shape or dtype, bad id */
+    PKV_ERR_OOM = -2,     /* not enough free blocks; nothing was allocated */
+    PKV_ERR_STATE = -3,   /* refcount misuse: freeing a free block, sharing a free block,
+                             appending into a shared block (no copy-on-write) */
+    PKV_ERR_HIP = -4      /* a HIP launch failed */
+} pkv_status;
+
+typedef enum {
+    PKV_F16 = 0,      /* IEEE binary16 */
+    PKV_BF16 = 1,     /* bfloat16 */
+    PKV_FP8_E4M3 = 2  /* OCP E4M3 "fn": bias 7, max 448, NaN = S.1111.111, no inf */
+} pkv_dtype;
+
+/* Block size in tokens. The only supported value. */
+#define PKV_BLOCK_SIZE 16
+
+/*
+ * Pool geometry. [P2] "PagedAttention：...": memory is cut into fixed-size
+ * physical blocks. One block id names the same block in every layer, so one
+ * block table serves all layers of a model.
+ *
+ * Device layout (this library's contract): element (layer l, c in {K=0,V=1},
+ * block b, kv head h, slot t, dim d) is stored at element offset
+ *     ((((l*2 + c)*num_blocks + b)*num_kv_heads + h)*block_size + t)*head_dim + d
+ * so each (l, c, b, h) tile of block_size x head_dim elements is contiguous.
+ *
+ * Supported: block_size == 16; head_dim in {64, 128}; num_kv_heads >= 1;
+ * kv_dtype a pkv_dtype.
+ */
+typedef struct {
+    int32_t num_layers;
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t kv_dtype; /* pkv_dtype */
+} pkv_pool_desc;
+
+typedef struct pkv_pool pkv_pool; /* opaque; holds host metadata only */
+
+/* Bytes of device memory the pool occupies:
+ * num_layers * 2 * num_blocks * num_kv_heads * block_size * head_dim * elem_size.
+ * For one request's ceil(L/16) blocks this is the closed form
+ * 2 x L x layers x heads x head_dim x bytes of [P2] "真正吃显存的是 KV Cache，
+ * 不是模型权重". Returns 0 for an unsupported descriptor. */
+size_t kv_pool_bytes(const pkv_pool_desc* desc);
+
+/* Create the host bookkeeping for a pool whose device memory the caller has
+ * already allocated ([P2] first pitfall: one preallocated pool).
+ * device_base: device pointer to kv_pool_bytes(desc) bytes, 256-byte aligned,
+ *   borrowed (it must outlive the pool); NULL is allowed for a
+ *   bookkeeping-only pool, on which the kernel calls fail with INVALID.
+ * bytes: size of that allocation; must be >= kv_pool_bytes(desc) when
+ *   device_base is not NULL.
+ * All blocks start free; the first allocations return ids 0, 1, 2, ...
+ * Errors: INVALID (bad descriptor, size, alignment, NULL out). */
+pkv_status kv_pool_create(const pkv_pool_desc* desc, void* device_base, size_t bytes,
+                          pkv_pool** out);
+
+/* Destroy the host bookkeeping. Does not touch device memory. NULL is a no-op. */
+void kv_pool_destroy(pkv_pool* pool);
+
+/* Number of free blocks ([P2] "连续批处理": get_num_free_blocks; a request
+ * for n blocks can be served exactly when this is >= n, since blocks are
+ * interchangeable). Returns -1 for a NULL pool. Cache usage = 1 - free/total. */
+int32_t kv_pool_num_free(const pkv_pool* pool);
+
+/* Copy the free-block stack, bottom first, into out[0 .. min(n, cap)) and
+ * return n, the number of free blocks (-1 for bad arguments). The next
+ * allocation pops from the top (out[n-1]). For tests and diagnostics. */
+int32_t kv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap);
+
+/* Allocate n blocks ([P2] "PagedAttention：...": on-demand allocation).
+ * out_ids: host array of n ints, receives the ids in pop order; each gets
+ *   refcount 1.
+ * Errors: INVALID (NULL args, n < 0), OOM (fewer than n free; nothing
+ *   allocated). */
+pkv_status block_alloc(pkv_pool* pool, int32_t n, int32_t* out_ids);
+
+/* Drop one reference on each of ids[0..n) (host array) ([P2] "连续批处理":
+ * a finished request's table is freed). An id whose count reaches 0 is pushed
+ * on the free stack, in argument order (last freed = next allocated).
+ * An id may appear several times if it holds that many references.
+ * Errors: INVALID (NULL, n < 0, id out of range), STATE (an id would drop
+ *   below 0). */
+pkv_status block_free(pkv_pool* pool, int32_t n, const int32_t* ids);
+
+/* Add one reference to each of ids[0..n) (host array): one physical block
+ * backs one more logical block ([P2] "PagedAttention：...": shared blocks for
+ * beam search and common prefixes).
+ * Errors: INVALID (NULL, n < 0, out of range), STATE (an id is free). */
+pkv_status block_incref(pkv_pool* pool, int32_t n, const int32_t* ids);
+
+/* Reference count of one block; -1 if the id is out of range or pool NULL. */
+int32_t block_refcount(const pkv_pool* pool, int32_t id);
+
+/* Share a prefix: dst_row[j] = src_row[j] for j < num_blocks and take one
+ * more reference on each of those ids (host arrays). Used when a sequence
+ * starts with the same full blocks as another (common prompt prefix).
+ * Errors: INVALID (NULL, num_blocks < 0, id out of range), STATE (an id is
+ *   free). */
+pkv_status kv_seq_fork(pkv_pool* pool, const int32_t* src_row, int32_t* dst_row,
+                       int32_t num_blocks);
+
+/* Grow sequence i from cur_lens[i] to new_lens[i] tokens (host arrays) and
+ * emit the slot of every new token ([P2] "PagedAttention：...": a block is
+ * taken when a token opens one).
+ * block_tables: host array [num_seqs][max_blocks_per_seq]; row i holds the ids
+ *   of sequence i's blocks in logical order. For each new token at position
+ *   pos, when pos % 16 == 0 a block is popped and written to
+ *   block_tables[i][pos/16]; the token's slot is
+ *   block_tables[i][pos/16] * 16 + pos % 16.
+ * slot_mapping_out: host array of sum(new_lens - cur_lens) int64, filled
+ *   sequence by sequence, positions in increasing order.
+ * Errors: INVALID (NULL, negative or shrinking lengths, a row too short,
+ *   out-of-range id), STATE (a token would land in a block whose refcount is
+ *   not 1), OOM (not enough free blocks for the whole call). On error nothing
+ *   changes. */
+pkv_status kv_seq_extend(pkv_pool* pool, int32_t num_seqs, int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* cur_lens,
+                         const int32_t* new_lens, int64_t* slot_mapping_out);
+
+/* Write each token's K and V into its slot of one layer ([P2]
+ * "PagedAttention：...": the cache grows by slots as tokens are produced;
+ * third pitfall: FP8 KV cache).
+ * k, v: device [num_tokens][num_kv_heads][head_dim] of src_dtype (F16 or
+ *   BF16), rows contiguous, 16-byte aligned.
+ * slot_mapping: device int64 [num_tokens]; slot = block * 16 + offset. A slot
+ *   < 0 or >= num_blocks*16 is skipped. Slots within one call must be unique
+ *   (otherwise which write lands is unspecified).
+ * 16-bit caches: src_dtype must equal the cache dtype; the bits are copied.
+ * FP8 cache: stores e4m3(fp32(x) / scale[h]) rounded to nearest, ties to even,
+ *   saturating to +-448 (never NaN for finite x). k_scale, v_scale: device
+ *   fp32 [num_kv_heads]; ignored (may be NULL) for 16-bit caches.
+ * Errors: INVALID (NULL pool or base, bad layer, dtype, count), HIP. */
+pkv_status kv_cache_append(const pkv_pool* pool, int32_t layer, const void* k, const void* v,
+                           int32_t src_dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                           const float* k_scale, const float* v_scale, hipStream_t stream);
+
+/* Bytes of workspace a partitioned decode needs: per (sequence, query head,
+ * partition) an fp32 max, an fp32 sum and head_dim fp32 outputs, with
+ * ceil(max_context_len / partition_size) partitions per sequence. 0 when
+ * partition_size == 0 or an argument is out of range. */
+size_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_size);
+
+/* Workspace layout (little-endian fp32, P = ceil(max_context_len / partition_size)):
+ *   ml[num_seqs][num_q_heads][P][2]     at byte 0         (m_p, l_p)
+ *   o [num_seqs][num_q_heads][P][head_dim]  at byte num_seqs*num_q_heads*P*8
+ * For partition p of sequence i (tokens [p*PS, min((p+1)*PS, L))):
+ *   m_p = max_t s_t, l_p = sum_t exp(s_t - m_p), o_p = sum_t exp(s_t - m_p) v_t / l_p,
+ * with s_t = scale * <q, k_t> in natural-log units. */
+
+/* Single-query decode attention over the paged cache of one layer ([P2]
+ * "PagedAttention：...": the attention kernel reads KV from non-contiguous
+ * physical blocks through the page table; [P3] 2.4: FP32 accumulation).
+ * For each sequence i and query head h, with kv head g = h / (num_q_heads /
+ * num_kv_heads):  out[i][h] = softmax(scale * q[i][h] . K_i[g]^T) V_i[g]
+ * over the L_i = context_lens[i] tokens of sequence i.
+ * q: device [num_seqs][num_q_heads][head_dim], q_dtype F16 or BF16; a 16-bit
+ *   cache must have q_dtype equal to the cache dtype; an FP8 cache takes
+ *   either. out: device, same shape and dtype as q (rounded to nearest even).
+ * block_tables: device int32 [num_seqs][max_blocks_per_seq]; entries past
+ *   ceil(L_i/16) are never read. An id outside [0, num_blocks) is not read;
+ *   its 16 tokens are treated as absent.
+ * context_lens: device int32 [num_seqs]. L_i is clamped to
+ *   min(max_context_len, max_blocks_per_seq*16); L_i <= 0 gives zeros.
+ * num_q_heads must be num_kv_heads * G with G in {1, 2, 4, 8}.
+ * k_scale, v_scale: device fp32 [num_kv_heads] for an FP8 cache (value =
+ *   decode(code) * scale), ignored otherwise.
+ * partition_size == 0: one pass over the whole context writes out; workspace
+ *   is unused. partition_size > 0 (a multiple of 16): every partition writes
+ *   its (m_p, l_p, o_p) to workspace (layout above) and out is not touched;
+ *   the caller must then run paged_attn_reduce on the same stream with the
+ *   same shapes. workspace_bytes must be >= paged_attn_workspace_bytes(...).
+ * Errors: INVALID (shapes, dtypes, NULLs, workspace too small), HIP. */
+pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, const void* q, int32_t q_dtype,
+                             void* out, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             float scale, const float* k_scale, const float* v_scale,
+                             int32_t max_context_len, int32_t partition_size, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* Merge the partitions a partitioned paged_attn_decode left in workspace
+ * into out (device [num_seqs][num_q_heads][head_dim] of out_dtype F16 or BF16):
+ *   M = max_p m_p, w_p = l_p exp(m_p - M), out = sum_p w_p o_p / sum_p w_p
+ * over p < ceil(L_i / partition_size) (L_i clamped to max_context_len);
+ * a sequence with no tokens gets zeros.
+ * Errors: INVALID (NULLs, head_dim not 64/128, partition_size <= 0 or not a
+ *   multiple of 16), HIP. */
+pkv_status paged_attn_reduce(const void* workspace, void* out, int32_t out_dtype,
+                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t head_dim, int32_t max_context_len, int32_t partition_size,
+                             hipStream_t stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+#pragma GCC visibility pop
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

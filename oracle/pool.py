@@ -95,9 +95,9 @@ def append(pool6: np.ndarray, layer: int, k_raw: np.ndarray, v_raw: np.ndarray,
     block_size = pool6.shape[4]
     k_codes = encode_for_cache(k_raw, src_dtype, kv_dtype, k_scale)
     v_codes = encode_for_cache(v_raw, src_dtype, kv_dtype, v_scale)
-    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64).tolist()):
-        if slot < 0:
-            continue
-        block, offset = divmod(slot, block_size)
-        pool6[layer, 0, block, :, offset, :] = k_codes[t]
-        pool6[layer, 1, block, :, offset, :] = v_codes[t]
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    keep = slots >= 0
+    block, offset = np.divmod(slots[keep], block_size)
+    # pool6[layer, c, block[t], :, offset[t], :] = codes[t] for every kept t
+    pool6[layer, 0, block, :, offset, :] = k_codes[keep]
+    pool6[layer, 1, block, :, offset, :] = v_codes[keep]

@@ -1,0 +1,275 @@
+"""Python binding of libpagedkv (paged KV cache + paged decode attention, gfx950).
+
+Argument marshalling only: every step of the hot path runs in the HIP library
+(``csrc/``), whose C ABI is ``include/pagedkv.h``. PyTorch tensors supply
+device memory and the current stream; host bookkeeping takes numpy arrays.
+The functions keep the C names. A non-OK status raises ``PkvError``.
+
+The library must have been built (``python -m paged_kv_cache_450_amd.build``
+or ``__graft_entry__.build()``); importing this package fails loudly if it
+was not: there is no fallback implementation.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "PKV_OK", "PKV_ERR_INVALID", "PKV_ERR_OOM", "PKV_ERR_STATE", "PKV_ERR_HIP",
+    "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3", "BLOCK_SIZE", "PkvError", "PoolDesc",
+    "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_num_free",
+    "kv_pool_free_list", "block_alloc", "block_free", "block_incref", "block_refcount",
+    "kv_seq_fork", "kv_seq_extend", "kv_cache_append", "paged_attn_workspace_bytes",
+    "paged_attn_decode", "paged_attn_reduce", "pkv_last_error", "library_path", "lib",
+]
+
+PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_STATE, PKV_ERR_HIP = 0, -1, -2, -3, -4
+PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+BLOCK_SIZE = 16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+
+def _load():
+    # torch ships its own HIP runtime. Load it first so that this library's
+    # libamdhip64.so.7 dependency binds to that same runtime: one process must
+    # never hold two HIP/HSA runtimes.
+    import torch  # noqa: F401
+
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m paged_kv_cache_450_amd.build` "
+            "(there is no fallback path)")
+    L = ctypes.CDLL(_LIB_PATH)
+    i32, i64, sz, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+    p_i32, p_i64 = ctypes.POINTER(i32), ctypes.POINTER(i64)
+    p_desc = ctypes.POINTER(PoolDesc)
+    sig = {
+        "kv_pool_bytes": (sz, [p_desc]),
+        "kv_pool_create": (i32, [p_desc, vp, sz, ctypes.POINTER(vp)]),
+        "kv_pool_destroy": (None, [vp]),
+        "kv_pool_num_free": (i32, [vp]),
+        "kv_pool_free_list": (i32, [vp, p_i32, i32]),
+        "block_alloc": (i32, [vp, i32, p_i32]),
+        "block_free": (i32, [vp, i32, p_i32]),
+        "block_incref": (i32, [vp, i32, p_i32]),
+        "block_refcount": (i32, [vp, i32]),
+        "kv_seq_fork": (i32, [vp, p_i32, p_i32, i32]),
+        "kv_seq_extend": (i32, [vp, i32, p_i32, i32, p_i32, p_i32, p_i64]),
+        "kv_cache_append": (i32, [vp, i32, vp, vp, i32, vp, i32, vp, vp, vp]),
+        "paged_attn_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "paged_attn_decode": (i32, [vp, i32, vp, i32, vp, vp, i32, vp, i32, i32, f32, vp, vp,
+                                    i32, i32, vp, sz, vp]),
+        "paged_attn_reduce": (i32, [vp, vp, i32, vp, i32, i32, i32, i32, i32, vp]),
+        "pkv_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def pkv_last_error() -> str:
+    return lib.pkv_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != PKV_OK:
+        raise PkvError(status, pkv_last_error())
+
+
+def _i32_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _host_i32(a, writable=False) -> np.ndarray:
+    arr = np.asarray(a)
+    if arr.dtype != np.int32 or not arr.flags.c_contiguous or (writable and not arr.flags.writeable):
+        if writable:
+            raise ValueError("expected a writable C-contiguous int32 numpy array")
+        arr = np.ascontiguousarray(arr, dtype=np.int32)
+    return arr
+
+
+# ----------------------------------------------------------------- pool ----
+def kv_pool_bytes(desc: PoolDesc) -> int:
+    return int(lib.kv_pool_bytes(ctypes.byref(desc)))
+
+
+def kv_pool_create(desc: PoolDesc, device_base, nbytes: int):
+    """device_base: a device tensor (its data_ptr is used), an int address, or None."""
+    base = _ptr(device_base)
+    out = ctypes.c_void_p()
+    _check(lib.kv_pool_create(ctypes.byref(desc), base, nbytes, ctypes.byref(out)))
+    return out
+
+
+def kv_pool_destroy(pool) -> None:
+    lib.kv_pool_destroy(pool)
+
+
+def kv_pool_num_free(pool) -> int:
+    return int(lib.kv_pool_num_free(pool))
+
+
+def kv_pool_free_list(pool) -> np.ndarray:
+    n = lib.kv_pool_free_list(pool, None, 0)
+    if n < 0:
+        raise PkvError(PKV_ERR_INVALID, "kv_pool_free_list failed")
+    out = np.empty(n, dtype=np.int32)
+    lib.kv_pool_free_list(pool, _i32_ptr(out), n)
+    return out
+
+
+def block_alloc(pool, n: int) -> np.ndarray:
+    out = np.empty(max(n, 0), dtype=np.int32)
+    _check(lib.block_alloc(pool, n, _i32_ptr(out)))
+    return out
+
+
+def block_free(pool, ids) -> None:
+    a = _host_i32(ids).reshape(-1)
+    _check(lib.block_free(pool, a.size, _i32_ptr(a)))
+
+
+def block_incref(pool, ids) -> None:
+    a = _host_i32(ids).reshape(-1)
+    _check(lib.block_incref(pool, a.size, _i32_ptr(a)))
+
+
+def block_refcount(pool, block_id: int) -> int:
+    return int(lib.block_refcount(pool, block_id))
+
+
+def kv_seq_fork(pool, src_row, dst_row: np.ndarray, num_blocks: int) -> None:
+    src = _host_i32(src_row)
+    dst = _host_i32(dst_row, writable=True)
+    _check(lib.kv_seq_fork(pool, _i32_ptr(src), _i32_ptr(dst), num_blocks))
+
+
+def kv_seq_extend(pool, block_tables: np.ndarray, cur_lens, new_lens) -> np.ndarray:
+    """Grow sequences; block_tables (int32 [B, W]) is updated in place. Returns slots."""
+    bt = _host_i32(block_tables, writable=True)
+    if bt.ndim != 2:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]")
+    cur = _host_i32(cur_lens).reshape(-1)
+    new = _host_i32(new_lens).reshape(-1)
+    if cur.size != bt.shape[0] or new.size != bt.shape[0]:
+        raise ValueError("length arrays do not match block_tables")
+    total = int(new.astype(np.int64).sum() - cur.astype(np.int64).sum())
+    slots = np.empty(max(total, 0), dtype=np.int64)
+    _check(lib.kv_seq_extend(pool, bt.shape[0], _i32_ptr(bt), bt.shape[1], _i32_ptr(cur),
+                             _i32_ptr(new), slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+    return slots
+
+
+# -------------------------------------------------------------- kernels ----
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return PKV_F16
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def kv_cache_append(pool, layer: int, k, v, slot_mapping, k_scale=None, v_scale=None,
+                    stream=None) -> None:
+    """k, v: [T, Hkv, D] fp16/bf16 device tensors; slot_mapping: int64 [T]."""
+    torch = _torch()
+    _dev(k, "k"); _dev(v, "v"); _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(k_scale, "k_scale", torch.float32); _dev(v_scale, "v_scale", torch.float32)
+    if k.dtype != v.dtype or k.shape != v.shape:
+        raise ValueError("k and v must have the same shape and dtype")
+    if slot_mapping.numel() != k.shape[0]:
+        raise ValueError("one slot per token")
+    _check(lib.kv_cache_append(pool, layer, _ptr(k), _ptr(v), _dtype_code(k), _ptr(slot_mapping),
+                               k.shape[0], _ptr(k_scale), _ptr(v_scale), _stream(stream)))
+
+
+def paged_attn_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+                               max_context_len: int, partition_size: int) -> int:
+    return int(lib.paged_attn_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                              partition_size))
+
+
+def paged_attn_decode(pool, layer: int, q, out, block_tables, context_lens, scale: float,
+                      max_context_len: int, partition_size: int = 0, workspace=None,
+                      k_scale=None, v_scale=None, stream=None) -> None:
+    """q, out: [B, Hq, D]; block_tables int32 [B, W]; context_lens int32 [B] (device)."""
+    torch = _torch()
+    _dev(q, "q"); _dev(out, "out"); _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32); _dev(workspace, "workspace")
+    _dev(k_scale, "k_scale", torch.float32); _dev(v_scale, "v_scale", torch.float32)
+    if q.dim() != 3 or block_tables.dim() != 2:
+        raise ValueError("q must be [B, Hq, D] and block_tables [B, W]")
+    if out is not None and (out.shape != q.shape or out.dtype != q.dtype):
+        raise ValueError("out must match q")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.paged_attn_decode(pool, layer, _ptr(q), _dtype_code(q), _ptr(out),
+                                 _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                 q.shape[0], q.shape[1], float(scale), _ptr(k_scale),
+                                 _ptr(v_scale), max_context_len, partition_size, _ptr(workspace),
+                                 ws_bytes, _stream(stream)))
+
+
+def paged_attn_reduce(workspace, out, context_lens, max_context_len: int, partition_size: int,
+                      stream=None) -> None:
+    """out: [B, Hq, D] fp16/bf16 device tensor."""
+    torch = _torch()
+    _dev(workspace, "workspace"); _dev(out, "out"); _dev(context_lens, "context_lens", torch.int32)
+    _check(lib.paged_attn_reduce(_ptr(workspace), _ptr(out), _dtype_code(out), _ptr(context_lens),
+                                 out.shape[0], out.shape[1], out.shape[2], max_context_len,
+                                 partition_size, _stream(stream)))

@@ -1,0 +1,45 @@
+// Internal definitions shared by the library's translation units.
+#pragma once
+
+#include <cstdarg>
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "pagedkv.h"
+
+struct pkv_pool {
+    pkv_pool_desc desc;
+    void* base;          // borrowed device pointer (may be NULL)
+    size_t bytes;
+    std::vector<int32_t> free_stack;  // top = back()
+    std::vector<int32_t> ref;         // per-block reference count
+};
+
+namespace pkv {
+
+// Records a message for pkv_last_error() and returns the status.
+pkv_status fail(pkv_status status, const char* fmt, ...);
+
+inline int elem_size(int32_t dtype) {
+    switch (dtype) {
+        case PKV_F16:
+        case PKV_BF16: return 2;
+        case PKV_FP8_E4M3: return 1;
+        default: return 0;
+    }
+}
+
+inline bool is_16bit(int32_t dtype) { return dtype == PKV_F16 || dtype == PKV_BF16; }
+
+// Byte offset of the (layer, c, block 0, head 0, slot 0, dim 0) tile in the pool.
+inline size_t layer_plane_offset(const pkv_pool_desc& d, int32_t layer, int32_t c) {
+    return (static_cast<size_t>(layer) * 2 + static_cast<size_t>(c)) *
+           static_cast<size_t>(d.num_blocks) * static_cast<size_t>(d.num_kv_heads) *
+           static_cast<size_t>(d.block_size) * static_cast<size_t>(d.head_dim) *
+           static_cast<size_t>(elem_size(d.kv_dtype));
+}
+
+constexpr int kBlockSize = PKV_BLOCK_SIZE;
+
+}  // namespace pkv

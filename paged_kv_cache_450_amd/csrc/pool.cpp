@@ -1,0 +1,230 @@
+// Host-side block manager: one preallocated pool of fixed-size blocks, a LIFO
+// free stack, per-block reference counts, and per-sequence slot bookkeeping.
+//
+// [P2] "vLLM 推理加速原理详解：大模型服务吞吐量为何能提升 10 倍", section
+// "PagedAttention：把操作系统的虚拟内存搬进 GPU": fixed-size blocks handed out on
+// demand, mapped through a per-sequence page table, interchangeable (no
+// external fragmentation) and shareable between sequences. Section
+// "连续批处理：别再等最慢的那个请求了": the calls a scheduler makes each
+// iteration (free a finished table, count free blocks, allocate).
+//
+// Fixed-size blocks make any free block as good as any other, so a stack gives
+// O(1) alloc and free; reference counts give sharing without copies.
+
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <unordered_map>
+
+#include "common.h"
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+namespace pkv {
+
+pkv_status fail(pkv_status status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+}  // namespace pkv
+
+using pkv::fail;
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+static bool desc_valid(const pkv_pool_desc* d) {
+    return d != nullptr && d->num_layers > 0 && d->num_blocks >= 0 &&
+           d->block_size == PKV_BLOCK_SIZE && d->num_kv_heads > 0 &&
+           (d->head_dim == 64 || d->head_dim == 128) && pkv::elem_size(d->kv_dtype) > 0;
+}
+
+size_t kv_pool_bytes(const pkv_pool_desc* d) {
+    if (!desc_valid(d)) return 0;
+    return static_cast<size_t>(d->num_layers) * 2 * static_cast<size_t>(d->num_blocks) *
+           static_cast<size_t>(d->num_kv_heads) * static_cast<size_t>(d->block_size) *
+           static_cast<size_t>(d->head_dim) * static_cast<size_t>(pkv::elem_size(d->kv_dtype));
+}
+
+pkv_status kv_pool_create(const pkv_pool_desc* desc, void* device_base, size_t bytes,
+                          pkv_pool** out) {
+    if (out == nullptr) return fail(PKV_ERR_INVALID, "kv_pool_create: out is NULL");
+    if (!desc_valid(desc))
+        return fail(PKV_ERR_INVALID,
+                    "kv_pool_create: unsupported descriptor (block_size must be 16, head_dim "
+                    "64 or 128, layers/heads > 0, blocks >= 0, known dtype)");
+    const size_t need = kv_pool_bytes(desc);
+    if (device_base != nullptr) {
+        if (bytes < need)
+            return fail(PKV_ERR_INVALID, "kv_pool_create: %zu bytes given, %zu needed", bytes,
+                        need);
+        if (reinterpret_cast<uintptr_t>(device_base) % 256 != 0)
+            return fail(PKV_ERR_INVALID, "kv_pool_create: device_base not 256-byte aligned");
+    }
+    pkv_pool* p = new (std::nothrow) pkv_pool;
+    if (p == nullptr) return fail(PKV_ERR_OOM, "kv_pool_create: host allocation failed");
+    try {
+        p->desc = *desc;
+        p->base = device_base;
+        p->bytes = bytes;
+        p->free_stack.resize(desc->num_blocks);
+        for (int32_t i = 0; i < desc->num_blocks; ++i)
+            p->free_stack[i] = desc->num_blocks - 1 - i;  // top = 0
+        p->ref.assign(desc->num_blocks, 0);
+    } catch (...) {
+        delete p;
+        return fail(PKV_ERR_OOM, "kv_pool_create: host allocation failed");
+    }
+    *out = p;
+    return PKV_OK;
+}
+
+void kv_pool_destroy(pkv_pool* pool) { delete pool; }
+
+int32_t kv_pool_num_free(const pkv_pool* pool) {
+    if (pool == nullptr) return -1;
+    return static_cast<int32_t>(pool->free_stack.size());
+}
+
+int32_t kv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap) {
+    if (pool == nullptr || cap < 0 || (cap > 0 && out == nullptr)) return -1;
+    const int32_t n = static_cast<int32_t>(pool->free_stack.size());
+    const int32_t m = n < cap ? n : cap;
+    if (m > 0) std::memcpy(out, pool->free_stack.data(), sizeof(int32_t) * m);
+    return n;
+}
+
+pkv_status block_alloc(pkv_pool* pool, int32_t n, int32_t* out_ids) {
+    if (pool == nullptr) return fail(PKV_ERR_INVALID, "block_alloc: pool is NULL");
+    if (n < 0) return fail(PKV_ERR_INVALID, "block_alloc: negative count %d", n);
+    if (n > 0 && out_ids == nullptr) return fail(PKV_ERR_INVALID, "block_alloc: out_ids is NULL");
+    if (static_cast<size_t>(n) > pool->free_stack.size())
+        return fail(PKV_ERR_OOM, "block_alloc: %d blocks requested, %zu free", n,
+                    pool->free_stack.size());
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t b = pool->free_stack.back();
+        pool->free_stack.pop_back();
+        pool->ref[b] = 1;
+        out_ids[i] = b;
+    }
+    return PKV_OK;
+}
+
+static pkv_status check_ids(const pkv_pool* pool, int32_t n, const int32_t* ids, const char* who) {
+    if (pool == nullptr) return fail(PKV_ERR_INVALID, "%s: pool is NULL", who);
+    if (n < 0) return fail(PKV_ERR_INVALID, "%s: negative count %d", who, n);
+    if (n > 0 && ids == nullptr) return fail(PKV_ERR_INVALID, "%s: ids is NULL", who);
+    for (int32_t i = 0; i < n; ++i)
+        if (ids[i] < 0 || ids[i] >= pool->desc.num_blocks)
+            return fail(PKV_ERR_INVALID, "%s: block id %d out of range", who, ids[i]);
+    return PKV_OK;
+}
+
+pkv_status block_free(pkv_pool* pool, int32_t n, const int32_t* ids) {
+    pkv_status st = check_ids(pool, n, ids, "block_free");
+    if (st != PKV_OK) return st;
+    // An id may appear several times; it must hold at least that many references.
+    std::unordered_map<int32_t, int32_t> need;
+    need.reserve(static_cast<size_t>(n) * 2);
+    for (int32_t i = 0; i < n; ++i) need[ids[i]] += 1;
+    for (const auto& kv : need)
+        if (pool->ref[kv.first] < kv.second)
+            return fail(PKV_ERR_STATE, "block_free: block %d holds %d references, %d released",
+                        kv.first, pool->ref[kv.first], kv.second);
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t b = ids[i];
+        if (--pool->ref[b] == 0) pool->free_stack.push_back(b);
+    }
+    return PKV_OK;
+}
+
+pkv_status block_incref(pkv_pool* pool, int32_t n, const int32_t* ids) {
+    pkv_status st = check_ids(pool, n, ids, "block_incref");
+    if (st != PKV_OK) return st;
+    for (int32_t i = 0; i < n; ++i)
+        if (pool->ref[ids[i]] == 0)
+            return fail(PKV_ERR_STATE, "block_incref: block %d is free", ids[i]);
+    for (int32_t i = 0; i < n; ++i) pool->ref[ids[i]] += 1;
+    return PKV_OK;
+}
+
+int32_t block_refcount(const pkv_pool* pool, int32_t id) {
+    if (pool == nullptr || id < 0 || id >= pool->desc.num_blocks) return -1;
+    return pool->ref[id];
+}
+
+pkv_status kv_seq_fork(pkv_pool* pool, const int32_t* src_row, int32_t* dst_row,
+                       int32_t num_blocks) {
+    if (num_blocks > 0 && dst_row == nullptr)
+        return fail(PKV_ERR_INVALID, "kv_seq_fork: dst_row is NULL");
+    pkv_status st = block_incref(pool, num_blocks, src_row);
+    if (st != PKV_OK) return st;
+    for (int32_t j = 0; j < num_blocks; ++j) dst_row[j] = src_row[j];
+    return PKV_OK;
+}
+
+pkv_status kv_seq_extend(pkv_pool* pool, int32_t num_seqs, int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* cur_lens,
+                         const int32_t* new_lens, int64_t* slot_mapping_out) {
+    if (pool == nullptr) return fail(PKV_ERR_INVALID, "kv_seq_extend: pool is NULL");
+    if (num_seqs < 0 || max_blocks_per_seq < 0)
+        return fail(PKV_ERR_INVALID, "kv_seq_extend: negative size");
+    if (num_seqs == 0) return PKV_OK;
+    if (block_tables == nullptr || cur_lens == nullptr || new_lens == nullptr)
+        return fail(PKV_ERR_INVALID, "kv_seq_extend: NULL array");
+    const int32_t bs = pool->desc.block_size;
+    int64_t needed = 0, tokens = 0;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+        const int64_t cur = cur_lens[i], nw = new_lens[i];
+        if (cur < 0 || nw < cur)
+            return fail(PKV_ERR_INVALID, "kv_seq_extend: seq %d: lengths %lld -> %lld", i,
+                        static_cast<long long>(cur), static_cast<long long>(nw));
+        const int64_t nb_new = (nw + bs - 1) / bs, nb_cur = (cur + bs - 1) / bs;
+        if (nb_new > max_blocks_per_seq)
+            return fail(PKV_ERR_INVALID, "kv_seq_extend: seq %d needs %lld blocks, row holds %d",
+                        i, static_cast<long long>(nb_new), max_blocks_per_seq);
+        if (nw > cur && cur % bs != 0) {
+            const int32_t b = block_tables[static_cast<int64_t>(i) * max_blocks_per_seq + cur / bs];
+            if (b < 0 || b >= pool->desc.num_blocks)
+                return fail(PKV_ERR_INVALID, "kv_seq_extend: seq %d: block id %d out of range", i,
+                            b);
+            if (pool->ref[b] != 1)
+                return fail(PKV_ERR_STATE,
+                            "kv_seq_extend: seq %d: block %d has refcount %d (free or shared)", i,
+                            b, pool->ref[b]);
+        }
+        needed += nb_new - nb_cur;
+        tokens += nw - cur;
+    }
+    if (tokens > 0 && slot_mapping_out == nullptr)
+        return fail(PKV_ERR_INVALID, "kv_seq_extend: slot_mapping_out is NULL");
+    if (needed > static_cast<int64_t>(pool->free_stack.size()))
+        return fail(PKV_ERR_OOM, "kv_seq_extend: %lld blocks needed, %zu free",
+                    static_cast<long long>(needed), pool->free_stack.size());
+    int64_t k = 0;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+        int32_t* row = block_tables + static_cast<int64_t>(i) * max_blocks_per_seq;
+        for (int32_t pos = cur_lens[i]; pos < new_lens[i]; ++pos) {
+            if (pos % bs == 0) {
+                const int32_t b = pool->free_stack.back();
+                pool->free_stack.pop_back();
+                pool->ref[b] = 1;
+                row[pos / bs] = b;
+            }
+            slot_mapping_out[k++] = static_cast<int64_t>(row[pos / bs]) * bs + pos % bs;
+        }
+    }
+    return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,151 @@
+"""Host-side orchestration over the C ABI: a pool in device memory with its
+block manager, batch admission, and one decode step (append, decode, reduce).
+
+Every computation is a call into libpagedkv; this module only sequences calls
+and moves small host arrays (block tables, lengths, slots) to the device.
+
+[P2] "vLLM 推理加速原理详解：大模型服务吞吐量为何能提升 10 倍":
+"PagedAttention：把操作系统的虚拟内存搬进 GPU" (blocks on demand, shared
+prefix blocks), "连续批处理：别再等最慢的那个请求了" (per-iteration block
+manager calls followed by one decode step), "vLLM 也不是银弹：真实部署中的坑"
+(first pitfall: one preallocated pool).
+"""
+
+import math
+
+import numpy as np
+import torch
+
+from . import (BLOCK_SIZE, PKV_BF16, PKV_F16, PKV_FP8_E4M3, PoolDesc, block_alloc, block_free,
+               kv_cache_append, kv_pool_bytes, kv_pool_create, kv_pool_destroy,
+               kv_pool_free_list, kv_pool_num_free, kv_seq_extend, kv_seq_fork,
+               paged_attn_decode, paged_attn_reduce, paged_attn_workspace_bytes)
+
+DTYPE_CODES = {"f16": PKV_F16, "bf16": PKV_BF16, "e4m3": PKV_FP8_E4M3}
+
+
+class PagedKVCache:
+    """One KV pool (device bytes owned by torch) plus its block manager."""
+
+    def __init__(self, num_layers: int, num_blocks: int, num_kv_heads: int, head_dim: int,
+                 kv_dtype: str, device="cuda", fill_byte=None):
+        self.desc = PoolDesc(num_layers, num_blocks, BLOCK_SIZE, num_kv_heads, head_dim,
+                             DTYPE_CODES[kv_dtype])
+        self.kv_dtype = kv_dtype
+        self.nbytes = kv_pool_bytes(self.desc)
+        if self.nbytes == 0 and num_blocks > 0:
+            raise ValueError("unsupported pool geometry")
+        if device is None:
+            self.buf = None
+        elif fill_byte is None:
+            self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        else:
+            self.buf = torch.full((self.nbytes,), fill_byte, dtype=torch.uint8, device=device)
+        self.handle = kv_pool_create(self.desc, self.buf, self.nbytes)
+
+    def close(self):
+        if self.handle is not None:
+            kv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        self.close()
+
+    @property
+    def num_blocks(self) -> int:
+        return self.desc.num_blocks
+
+    def num_free(self) -> int:
+        return kv_pool_num_free(self.handle)
+
+    def usage(self) -> float:
+        """Cache usage gauge: 1 - free / total."""
+        return 1.0 - self.num_free() / max(self.num_blocks, 1)
+
+    def free_list(self) -> np.ndarray:
+        return kv_pool_free_list(self.handle)
+
+    def permute_free_list(self, order) -> None:
+        """Return every block to the pool in the given order (the last one is
+        allocated first): a fresh pool then hands out blocks in random places."""
+        ids = block_alloc(self.handle, self.num_blocks)
+        if not np.array_equal(np.sort(np.asarray(order)), np.sort(ids)):
+            block_free(self.handle, ids)
+            raise ValueError("order must be a permutation of all block ids")
+        block_free(self.handle, order)
+
+    def admit(self, cached_lens, max_blocks: int, share_from=None, share_blocks: int = 0):
+        """Allocate block tables for sequences that already hold cached_lens[i] tokens.
+
+        share_from[i] = j (j < i) makes sequence i start with the first
+        share_blocks blocks of sequence j (a common prompt prefix); -1 = none.
+        Returns (tables int32 [B, max_blocks] padded with -1, first written
+        position per sequence, int64 slots of the tokens to write, sequence by
+        sequence).
+        """
+        cached = np.asarray(cached_lens, dtype=np.int32)
+        b = cached.size
+        tables = np.full((b, max_blocks), -1, dtype=np.int32)
+        start = np.zeros(b, dtype=np.int32)
+        slots = []
+        for i in range(b):
+            j = -1 if share_from is None else int(share_from[i])
+            if j >= 0:
+                kv_seq_fork(self.handle, tables[j], tables[i], share_blocks)
+                start[i] = share_blocks * BLOCK_SIZE
+            slots.append(kv_seq_extend(self.handle, tables[i:i + 1], start[i:i + 1],
+                                       cached[i:i + 1]))
+        return tables, start, (np.concatenate(slots) if slots else np.zeros(0, np.int64))
+
+    def grow(self, tables: np.ndarray, cur_lens, new_lens) -> np.ndarray:
+        """One decode step's bookkeeping: extend every sequence; returns slots."""
+        return kv_seq_extend(self.handle, tables, cur_lens, new_lens)
+
+    # -- kernels ------------------------------------------------------------
+    def append(self, layer: int, k, v, slots, k_scale=None, v_scale=None, stream=None):
+        kv_cache_append(self.handle, layer, k, v, slots, k_scale, v_scale, stream)
+
+
+class DecodeBatch:
+    """Device-side state of one batch: tables, lengths, workspace and output.
+
+    run(layer, q) issues paged_attn_decode and, when partitioned, paged_attn_reduce
+    on one stream; the output is self.out.
+    """
+
+    def __init__(self, cache: PagedKVCache, tables: np.ndarray, lens, num_q_heads: int,
+                 q_dtype, partition_size: int = 0, scale=None, k_scale=None, v_scale=None,
+                 max_context_len=None, device="cuda"):
+        self.cache = cache
+        lens = np.asarray(lens, dtype=np.int32)
+        self.num_seqs = lens.size
+        self.tables = torch.from_numpy(np.ascontiguousarray(tables, dtype=np.int32)).to(device)
+        self.lens = torch.from_numpy(lens).to(device)
+        self.max_context_len = int(lens.max()) if max_context_len is None and lens.size else (
+            int(max_context_len or 0))
+        self.num_q_heads = num_q_heads
+        self.head_dim = cache.desc.head_dim
+        self.scale = (1.0 / math.sqrt(self.head_dim)) if scale is None else scale
+        self.partition_size = partition_size
+        self.k_scale, self.v_scale = k_scale, v_scale
+        self.out = torch.empty((self.num_seqs, num_q_heads, self.head_dim), dtype=q_dtype,
+                               device=device)
+        ws = paged_attn_workspace_bytes(self.num_seqs, num_q_heads, self.head_dim,
+                                        self.max_context_len, partition_size)
+        self.workspace = (torch.empty(max(ws, 16) // 4, dtype=torch.float32, device=device)
+                          if partition_size > 0 else None)
+
+    def decode(self, layer: int, q, stream=None):
+        paged_attn_decode(self.cache.handle, layer, q, None if self.partition_size else self.out,
+                          self.tables, self.lens, self.scale, self.max_context_len,
+                          self.partition_size, self.workspace, self.k_scale, self.v_scale, stream)
+
+    def reduce(self, stream=None):
+        if self.partition_size > 0:
+            paged_attn_reduce(self.workspace, self.out, self.lens, self.max_context_len,
+                              self.partition_size, stream)
+
+    def run(self, layer: int, q, stream=None):
+        self.decode(layer, q, stream)
+        self.reduce(stream)
+        return self.out

@@ -1,0 +1,154 @@
+"""Build one decode-step workload twice, product side and oracle side.
+
+Product side: the C ABI through paged_kv_cache_450_amd.runtime (block manager
+on the host, append / decode / reduce kernels on the GPU).
+Oracle side: oracle.allocator.AllocatorModel for the bookkeeping, oracle.pool
+for the append, oracle.attention for the decode, on host copies of the same
+seeded inputs (never on anything the product computed).
+
+Procedure (both sides): a pool of exactly the blocks the batch needs (or the
+configured count) gets all blocks returned in a seeded random order; each
+sequence is admitted holding L-1 cached tokens (prefix sharers fork the first
+sharer's full prefix blocks and write only their private tokens); then the
+decode step grows every sequence to L, appends the new token and attends over
+all L tokens.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+import workloads as W
+from oracle import allocator as oalloc
+from oracle import attention as oattn
+from oracle import pool as opool
+
+BS = 16
+POISON = 0xFF  # fp16 / bf16 0xFFFF and e4m3 0xFF are NaN
+
+
+from bench import BS as _BS, OracleBookkeeping, Workload, blocks_needed, share_spec  # noqa: E402,F401
+
+assert _BS == BS
+
+
+def build_product(cfg, seed=0, device="cuda", partition_size=None, fill_byte=POISON,
+                  run_step=True, placement_seed=None):
+    """Product side: pool, bookkeeping, prefill appends, then (run_step) one
+    decode step per layer whose outputs are kept in side.outputs."""
+    side = Workload(cfg, seed, device, partition_size, fill_byte, placement_seed)
+    if run_step:
+        side.outputs = [step(side, layer).clone() for layer in range(cfg.layers)]
+    return side
+
+
+def step(side, layer: int):
+    """One decode step of one layer on the product side: append + decode (+ reduce)."""
+    return side.step(layer)
+
+
+# ------------------------------------------------------------ oracle side ----
+def raw16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def q_f64(t: torch.Tensor, dtype: str) -> np.ndarray:
+    return opool.raw_to_f64(raw16(t), dtype)
+
+
+def oracle_bookkeeping(cfg, seed=0, placement_seed=None):
+    return OracleBookkeeping(cfg, seed, placement_seed)
+
+
+def token_index(lens, start):
+    """offs[i]:offs[i+1] are the rows of the cached-token inputs written for
+    sequence i (positions start[i] .. lens[i]-2, in order)."""
+    counts = (np.asarray(lens) - 1 - np.asarray(start)).astype(np.int64)
+    return np.concatenate([[0], np.cumsum(counts)])
+
+
+def sample_sequences(cfg, side, max_seqs=None):
+    """All sequences, or the shortest, the longest and a spread of others,
+    plus the first prefix sharer whenever a later sharer is taken."""
+    b = cfg.batch
+    if max_seqs is None or max_seqs >= b:
+        return list(range(b))
+    order = np.argsort(side.lens, kind="stable")
+    pick = {int(order[0]), int(order[-1])}
+    rest = [int(i) for i in np.linspace(0, b - 1, max_seqs).round()]
+    pick.update(rest[: max(0, max_seqs - 2)])
+    sh = W.sharers(cfg)
+    if sh and any(i in sh[1:] for i in pick):
+        pick.add(sh[0])
+    return sorted(pick)
+
+
+def expected_layer_pool(cfg, side, oside, layer: int, seqs,
+                        fill_byte=POISON):
+    """Host pool of one layer ([1, 2, NB, Hkv, BS, D] raw) after the oracle's
+    append of the cached and new tokens of the sequences in seqs. Uses the
+    oracle's own slots; only the seeded inputs come from `side`."""
+    nb = oside.model.num_blocks
+    per_layer = opool.pool_bytes(1, nb, BS, cfg.kv_heads, cfg.head_dim, cfg.kv_dtype)
+    buf = np.full(per_layer, fill_byte, dtype=np.uint8)
+    p6 = opool.view_pool(buf, 1, nb, BS, cfg.kv_heads, cfg.head_dim, cfg.kv_dtype)
+    offs = token_index(side.lens, oside.start)
+    ks = vs = None
+    if cfg.kv_dtype == "e4m3":
+        ks = side.k_scale[layer].cpu().numpy()
+        vs = side.v_scale[layer].cpu().numpy()
+    for i in seqs:
+        lo, hi = int(offs[i]), int(offs[i + 1])
+        if hi > lo:
+            opool.append(p6, 0, raw16(side.k_cached[layer][lo:hi]), raw16(side.v_cached[layer][lo:hi]),
+                         cfg.src_dtype, cfg.kv_dtype, oside.slots_cached[lo:hi], ks, vs)
+        opool.append(p6, 0, raw16(side.k_new[layer][i:i + 1]), raw16(side.v_new[layer][i:i + 1]),
+                     cfg.src_dtype, cfg.kv_dtype, oside.slots_new[i:i + 1], ks, vs)
+    return p6
+
+
+def gpu_layer_blocks(cfg, side, layer: int, ids: np.ndarray) -> np.ndarray:
+    """Raw bytes of the given blocks of one layer, copied from the device: [2, n, Hkv, BS, D]."""
+    nb = side.cache.num_blocks
+    esz = opool.ESIZE[cfg.kv_dtype]
+    per_layer = 2 * nb * cfg.kv_heads * BS * cfg.head_dim * esz
+    lay = side.cache.buf[layer * per_layer:(layer + 1) * per_layer]
+    lay = lay.view(2, nb, cfg.kv_heads * BS * cfg.head_dim * esz)
+    idx = torch.from_numpy(ids.astype(np.int64)).to(lay.device)
+    got = lay[:, idx].cpu().numpy()
+    dt = opool.raw_dtype(cfg.kv_dtype)
+    return got.view(dt).reshape(2, ids.size, cfg.kv_heads, BS, cfg.head_dim)
+
+
+def oracle_outputs(cfg, side, oside, layer: int, p6, seqs) -> np.ndarray:
+    scale = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))
+    q = q_f64(side.q[layer][seqs], cfg.q_dtype)
+    ks = vs = None
+    if cfg.kv_dtype == "e4m3":
+        ks = side.k_scale[layer].cpu().numpy()
+        vs = side.v_scale[layer].cpu().numpy()
+    lens = W.context_lengths(cfg, side.seed)
+    return oattn.paged_decode(p6, 0, q, oside.tables[seqs], lens[seqs], scale, cfg.kv_dtype,
+                              ks, vs)
+
+
+def out_f64(t: torch.Tensor, dtype: str) -> np.ndarray:
+    return opool.raw_to_f64(raw16(t), dtype)
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, kv_dtype: str, what=""):
+    """The tolerance the method states: |gpu - ref| <= atol + rtol*|ref| with
+    atol 2e-3, rtol 1e-2 for 16-bit KV, and atol 3e-2 for FP8 KV."""
+    if kv_dtype == "e4m3":
+        atol, rtol = 3e-2, 0.0
+    else:
+        atol, rtol = 2e-3, 1e-2
+    err = np.abs(got - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - (atol + rtol * np.abs(ref))), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} elements out of tolerance; worst at {i}: "
+                             f"got {got[i]!r} ref {ref[i]!r}; max abs err {err.max():.3e}")
+    return float(err.max()), float((err / np.maximum(np.abs(ref), 1e-30)).max())

@@ -1,0 +1,114 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Append and bookkeeping are compared bit for bit; decode output within the
+method's tolerance (16-bit KV: |d| <= 2e-3 + 1e-2 |ref|; FP8 KV: |d| <= 3e-2,
+both sides dequantising the same stored bytes).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _gpu(require_gpu):
+    yield
+    torch.cuda.synchronize()
+
+
+def check_bookkeeping(side, o):
+    assert np.array_equal(side.tables, o.tables)
+    assert np.array_equal(side.start, o.start)
+    assert np.array_equal(side.slots_cached, o.slots_cached)
+    assert np.array_equal(side.slots_new, o.slots_new)
+
+
+def check_layers(cfg, side, o, seqs, layers, whole_pool):
+    stats = []
+    for layer in layers:
+        p6 = H.expected_layer_pool(cfg, side, o, layer, seqs)
+        if whole_pool:
+            ids = np.arange(o.model.num_blocks)
+        else:
+            ids = np.unique(np.concatenate(
+                [o.tables[i, : -(-int(side.lens[i]) // 16)] for i in seqs]))
+        got = H.gpu_layer_blocks(cfg, side, layer, ids)
+        exp = p6[0][:, ids]
+        if not np.array_equal(got, exp):
+            bad = np.argwhere(got != exp)
+            raise AssertionError(f"layer {layer}: {len(bad)} pool elements differ, first {bad[:3]}")
+        ref = H.oracle_outputs(cfg, side, o, layer, p6, seqs)
+        out = H.out_f64(side.outputs[layer][seqs], cfg.q_dtype)
+        stats.append(H.assert_close(out, ref, cfg.kv_dtype, f"{cfg.name} layer {layer}"))
+    return stats
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_parity_small(name):
+    """Scaled versions of the five workloads: whole pool bytewise after the
+    appends (stray writes included) and every output of every layer."""
+    cfg = W.scaled(name)
+    say(f"parity_small {cfg.name} B={cfg.batch} Hq={cfg.q_heads} Hkv={cfg.kv_heads} "
+        f"D={cfg.head_dim} kv={cfg.kv_dtype} ps={cfg.partition_size}")
+    side = H.build_product(cfg, seed=0)
+    torch.cuda.synchronize()
+    o = H.oracle_bookkeeping(cfg, 0)
+    check_bookkeeping(side, o)
+    check_layers(cfg, side, o, list(range(cfg.batch)), range(cfg.layers), whole_pool=True)
+
+
+@pytest.mark.parametrize("name,max_seqs", [("tiny", None), ("llama13b_layer", 8),
+                                           ("gqa_prefix", 8), ("longctx_fp8", 2)])
+def test_parity_full_size(name, max_seqs):
+    """The workloads at their full sizes, in the launch configuration the
+    benchmark uses; append and output checked on sampled sequences."""
+    cfg = W.CONFIGS[name]
+    say(f"parity_full {cfg.name} B={cfg.batch} ps={cfg.partition_size}")
+    side = H.build_product(cfg, seed=0)
+    torch.cuda.synchronize()
+    o = H.oracle_bookkeeping(cfg, 0)
+    check_bookkeeping(side, o)
+    seqs = H.sample_sequences(cfg, side, max_seqs)
+    check_layers(cfg, side, o, seqs, range(cfg.layers), whole_pool=(max_seqs is None))
+    # Untouched slots keep the poison byte: every block of the pool is in some
+    # table, so look at the tails of the last blocks.
+    per_layer = side.cache.nbytes // cfg.layers
+    for i in range(cfg.batch):
+        n = int(side.lens[i])
+        if n % 16:
+            b = int(o.tables[i, (n - 1) // 16])
+            tail = H.gpu_layer_blocks(cfg, side, 0, np.array([b]))[:, 0, :, n % 16:, :]
+            assert np.all(tail.view(np.uint8) == H.POISON), i
+    del per_layer
+
+
+@pytest.mark.parametrize("ps", [0, 16, 32, 256, 512, 1024, 4096])
+def test_partition_sizes(ps):
+    cfg = W.scaled("llama13b_layer")
+    say(f"partition_size {ps}")
+    side = H.build_product(cfg, seed=1, partition_size=ps)
+    torch.cuda.synchronize()
+    o = H.oracle_bookkeeping(cfg, 1)
+    check_layers(cfg, side, o, list(range(cfg.batch)), [0], whole_pool=False)
+
+
+def test_run_to_run_bitwise_determinism():
+    cfg = W.scaled("gqa_prefix")
+    say("determinism")
+    side = H.build_product(cfg, seed=2)
+    first = side.outputs[0].clone()
+    for _ in range(3):
+        again = H.step(side, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), first.view(torch.int16))
