@@ -5,7 +5,7 @@ Argument marshalling only: every step of the hot path runs in the HIP library
 device memory and the current stream; host bookkeeping takes numpy arrays.
 The functions keep the C names. A non-OK status raises ``PkvError``.
 
-The library must have been built (``python -m paged_kv_cache_450_amd.build``
+The library must have been built (``python paged_kv_cache_450_amd/build.py``
 or ``__graft_entry__.build()``); importing this package fails loudly if it
 was not: there is no fallback implementation.
 """
@@ -56,7 +56,7 @@ def _load():
 
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(
-            f"{_LIB_PATH} is missing: build it with `python -m paged_kv_cache_450_amd.build` "
+            f"{_LIB_PATH} is missing: build it with `python paged_kv_cache_450_amd/build.py` "
             "(there is no fallback path)")
     L = ctypes.CDLL(_LIB_PATH)
     i32, i64, sz, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float

@@ -1,6 +1,9 @@
 """Build libpagedkv.so for gfx950 with hipcc, in-tree.
 
-    python -m paged_kv_cache_450_amd.build [-v]
+    python paged_kv_cache_450_amd/build.py [-v]
+
+It is run as a script (or loaded by file path) so that it does not import
+the package, whose import loads the library it builds.
 
 Objects go to <repo>/_build/, the shared library next to this file.
 """
