@@ -14,9 +14,15 @@ with R * (pool bytes) well above the 256 MB last-level cache, no step is
 served from cache.
 
 Prints one JSON line. `value` is the whole step's KV-read throughput
-(algorithmic K+V bytes of the attended tokens / step time); `roofline` is the
-decode kernel alone, timed with HIP events on the stream it is launched on;
+(algorithmic K+V bytes of the attended tokens / wall time of K back-to-back
+steps, synchronized on both sides). `roofline` is the decode kernel alone:
+the same K launches back to back on the stream they are launched on,
+bracketed by one HIP event pair, give its average duration per launch.
 `cpu_baseline` is the fp64 oracle on a bounded sample of the same workload.
+
+The 13B-shaped layer runs as a single pass (partition_size 0: every
+workgroup covers a whole context, longest sequences first); the long-context
+workloads split the context into partitions and merge them with the reduce.
 """
 
 import argparse
@@ -30,6 +36,37 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 BS = 16
+
+# HBM bytes per decode launch from rocprofv3 counter passes: FETCH_SIZE x 2.000
+# + WRITE_SIZE x 1.000, the factors read off a copy of known size (1 GiB read
+# and written) in the same runs. The figure is reported only while the decode
+# kernel's sources hash to what they were when the counters were taken.
+DECODE_SOURCES = ("paged_kv_cache_450_amd/csrc/decode.hip", "paged_kv_cache_450_amd/csrc/device.h",
+                  "paged_kv_cache_450_amd/csrc/common.h")
+MEASURED_TRAFFIC = {
+    "llama13b_layer": {
+        "sources_sha256": "506182509d3a9feedd23d1eec0da2bb6afafd9ee4211802f15755ac8be611aa1",
+        "bytes": 751_900_000,  # FETCH 367,006.7 KiB x 2 + WRITE 320 KiB
+        "summary": "profiles/decode_kernel_llama13b_layer.md",
+    },
+}
+
+
+def decode_sources_sha256() -> str:
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    entry = MEASURED_TRAFFIC.get(workload)
+    if entry is None or entry["sources_sha256"] != decode_sources_sha256():
+        return None
+    return entry["bytes"]
 
 
 # ------------------------------------------------------------- workload ----
@@ -205,8 +242,9 @@ def cpu_baseline(w: Workload, budget_s: float):
     if cfg.kv_dtype == "e4m3":
         ks, vs = w.k_scale[0].cpu().numpy(), w.v_scale[0].cpu().numpy()
     scale = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))
-    elapsed, done_bytes, seqs = 0.0, 0, 0
     esz = opool.ESIZE[cfg.kv_dtype]
+    # Host pool: the oracle's own append of every private sequence's tokens.
+    todo = []
     for i in range(cfg.batch):
         if ob.start[i] > 0:
             continue  # a prefix sharer; its prefix owner's tokens are not in this host pool
@@ -215,23 +253,28 @@ def cpu_baseline(w: Workload, budget_s: float):
                      cfg.kv_dtype, ob.slots_cached[lo:hi], ks, vs)
         opool.append(p6, 0, raw(w.k_new[0][i:i + 1]), raw(w.v_new[0][i:i + 1]), cfg.src_dtype,
                      cfg.kv_dtype, ob.slots_new[i:i + 1], ks, vs)
-        q = opool.raw_to_f64(raw(w.q[0][i:i + 1]), cfg.q_dtype)
-        t0 = time.perf_counter()
-        oattn.paged_decode(p6, 0, q, ob.tables[i:i + 1], ob.lens[i:i + 1], scale, cfg.kv_dtype,
-                           ks, vs)
-        elapsed += time.perf_counter() - t0
-        done_bytes += int(ob.lens[i]) * cfg.kv_heads * cfg.head_dim * 2 * esz
-        seqs += 1
-        if elapsed >= budget_s:
-            break
+        todo.append((i, opool.raw_to_f64(raw(w.q[0][i:i + 1]), cfg.q_dtype)))
+    # Whole passes over those sequences until about budget_s of oracle decode.
+    elapsed, done_bytes, seqs, passes = 0.0, 0, 0, 0
+    while elapsed < budget_s and todo:
+        for i, q in todo:
+            t0 = time.perf_counter()
+            oattn.paged_decode(p6, 0, q, ob.tables[i:i + 1], ob.lens[i:i + 1], scale,
+                               cfg.kv_dtype, ks, vs)
+            elapsed += time.perf_counter() - t0
+            done_bytes += int(ob.lens[i]) * cfg.kv_heads * cfg.head_dim * 2 * esz
+            seqs += 1
+            if elapsed >= budget_s:
+                break
+        passes += 1
     return {
         "value": round(done_bytes / elapsed / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{seqs} of {cfg.batch} sequences of {cfg.name} layer 0 "
-                  f"({done_bytes / 1e6:.1f} MB of KV), fp64 numpy decode only, "
-                  f"{elapsed:.1f} s",
+        "sample": f"{seqs} sequence decodes ({passes} passes over the {len(todo)} sequences of "
+                  f"{cfg.name} layer 0; {done_bytes / 1e6:.1f} MB of KV), fp64 numpy decode "
+                  f"only, {elapsed:.1f} s",
         "seqs_per_s": round(seqs / elapsed, 3),
     }
 
@@ -249,6 +292,10 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain elementwise copy of this many MiB before warm-up: a "
+                         "kernel of known traffic against which profiler byte counters are "
+                         "calibrated")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -274,38 +321,58 @@ def main(argv=None):
                              keep_cached_inputs=False) for r in range(1, reps)]
     kv_bytes = [w.kv_bytes() for w in ws]
     stream = torch.cuda.current_stream()
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 18  # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)  # reads and writes exactly 4n bytes each
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
         ws[i % reps].step(stream=stream)
     torch.cuda.synchronize()
 
+    # Timed region: exactly K whole steps back to back, synchronized on both
+    # sides; one event pair on the launch stream brackets the region (an event
+    # record between kernels costs a few microseconds of GPU time, so none is
+    # placed inside a step).
     nl = cfg.layers
-    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * nl)]
-          for k in ("a0", "d0", "d1", "r1")}
-    t0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     bytes_done = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(args.steps):
-        w = ws[i % reps]
         bytes_done += kv_bytes[i % reps]
-        for layer in range(nl):
-            j = i * nl + layer
-            ev["a0"][j].record(stream)
-            w.append(layer, stream)
-            ev["d0"][j].record(stream)
-            w.decode(layer, stream)
-            ev["d1"][j].record(stream)
-            w.reduce(stream)
-            ev["r1"][j].record(stream)
+        ws[i % reps].step(stream=stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-
-    n = args.steps * nl
-    append_us = sum(ev["a0"][j].elapsed_time(ev["d0"][j]) for j in range(n)) / n * 1e3
-    decode_us = sum(ev["d0"][j].elapsed_time(ev["d1"][j]) for j in range(n)) / n * 1e3
-    reduce_us = sum(ev["d1"][j].elapsed_time(ev["r1"][j]) for j in range(n)) / n * 1e3
     ms_per_step = (t1 - t0) / args.steps * 1e3
+    gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
     gbs = bytes_done / (t1 - t0) / 1e9
+
+    # Per-kernel durations: each kernel launched K*layers times back to back on
+    # the same stream (same replica rotation and arguments as the steps),
+    # bracketed by one event pair; average duration per launch.
+    def per_launch_us(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(args.steps):
+            for layer in range(nl):
+                fn(ws[i % reps], layer)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (args.steps * nl) * 1e3
+
+    decode_us = per_launch_us(lambda w, l: w.decode(l, stream))
+    append_us = per_launch_us(lambda w, l: w.append(l, stream))
+    reduce_us = (per_launch_us(lambda w, l: w.reduce(stream))
+                 if first.partition_size > 0 else 0.0)
     per_layer_bytes = sum(kv_bytes) / reps / nl
     decode_gbs = per_layer_bytes / (decode_us * 1e-6) / 1e9
 
@@ -335,6 +402,7 @@ def main(argv=None):
         },
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(cfg.batch / (ms_per_step * 1e-3), 1),
+        "gpu_ms_per_step": round(gpu_ms_per_step, 5),
         "kernel_us": {"append": round(append_us, 3), "decode": round(decode_us, 3),
                       "reduce": round(reduce_us, 3)},
         "roofline": {
@@ -344,7 +412,8 @@ def main(argv=None):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(cfg.name),
+            "algorithmic_bytes": int(per_layer_bytes),
         },
     }
     if not args.no_cpu_baseline:

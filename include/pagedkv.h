@@ -194,14 +194,16 @@ pkv_status kv_cache_append(const pkv_pool* pool, int32_t layer, const void* k, c
 
 /* Bytes of workspace a partitioned decode needs: per (sequence, query head,
  * partition) an fp32 max, an fp32 sum and head_dim fp32 outputs, with
- * ceil(max_context_len / partition_size) partitions per sequence. 0 when
+ * ceil(max_context_len / partition_size) partitions per sequence, laid out as
+ * described below (OFF + num_seqs*num_q_heads*P*head_dim*4). 0 when
  * partition_size == 0 or an argument is out of range. */
 size_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_size);
 
 /* Workspace layout (little-endian fp32, P = ceil(max_context_len / partition_size)):
- *   ml[num_seqs][num_q_heads][P][2]     at byte 0         (m_p, l_p)
- *   o [num_seqs][num_q_heads][P][head_dim]  at byte num_seqs*num_q_heads*P*8
+ *   ml[num_seqs][num_q_heads][P][2]         at byte 0   (m_p, l_p)
+ *   o [num_seqs][num_q_heads][P][head_dim]  at byte OFF = num_seqs*num_q_heads*P*8
+ *                                           rounded up to a multiple of 256
  * For partition p of sequence i (tokens [p*PS, min((p+1)*PS, L))):
  *   m_p = max_t s_t, l_p = sum_t exp(s_t - m_p), o_p = sum_t exp(s_t - m_p) v_t / l_p,
  * with s_t = scale * <q, k_t> in natural-log units. */
@@ -212,9 +214,10 @@ size_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * For each sequence i and query head h, with kv head g = h / (num_q_heads /
  * num_kv_heads):  out[i][h] = softmax(scale * q[i][h] . K_i[g]^T) V_i[g]
  * over the L_i = context_lens[i] tokens of sequence i.
- * q: device [num_seqs][num_q_heads][head_dim], q_dtype F16 or BF16; a 16-bit
- *   cache must have q_dtype equal to the cache dtype; an FP8 cache takes
- *   either. out: device, same shape and dtype as q (rounded to nearest even).
+ * q: device [num_seqs][num_q_heads][head_dim], q_dtype F16 or BF16, 16-byte
+ *   aligned; a 16-bit cache must have q_dtype equal to the cache dtype; an FP8
+ *   cache takes either. out: device, same shape and dtype as q (rounded to
+ *   nearest even), 16-byte aligned.
  * block_tables: device int32 [num_seqs][max_blocks_per_seq]; entries past
  *   ceil(L_i/16) are never read. An id outside [0, num_blocks) is not read;
  *   its 16 tokens are treated as absent.
@@ -228,7 +231,9 @@ size_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   its (m_p, l_p, o_p) to workspace (layout above) and out is not touched;
  *   the caller must then run paged_attn_reduce on the same stream with the
  *   same shapes. workspace_bytes must be >= paged_attn_workspace_bytes(...).
- * Errors: INVALID (shapes, dtypes, NULLs, workspace too small), HIP. */
+ * Limits: num_seqs <= 65535; ceil(max_context_len / partition_size) <= 65535.
+ * Errors: INVALID (shapes, dtypes, NULLs, alignment, workspace too small,
+ *   limits), HIP. */
 pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, const void* q, int32_t q_dtype,
                              void* out, const int32_t* block_tables, int32_t max_blocks_per_seq,
                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,

@@ -42,4 +42,11 @@ inline size_t layer_plane_offset(const pkv_pool_desc& d, int32_t layer, int32_t 
 
 constexpr int kBlockSize = PKV_BLOCK_SIZE;
 
+// Workspace of a partitioned decode: (m, l) pairs first, then the partial
+// outputs from the next 256-byte boundary, so their 16-byte rows stay aligned.
+inline size_t ws_o_offset(size_t num_seqs, size_t num_q_heads, size_t parts) {
+    const size_t ml = num_seqs * num_q_heads * parts * 2 * sizeof(float);
+    return (ml + 255) & ~static_cast<size_t>(255);
+}
+
 }  // namespace pkv

@@ -23,14 +23,23 @@
 //    its row, in base-2 with log2(e) folded into the scale; V is
 //    accumulated in fp32. At the end the TPI rows of a wave and the NW waves
 //    are merged with the log-sum-exp rule (shuffles, then LDS);
-//  * block ids for a wave's next 64 blocks are fetched with one vector load
-//    and broadcast with readlane; tiles are loaded in batches whose loads are
-//    all issued before the first tile of the batch is consumed;
+//  * each wave streams its tiles through a ring of NBUF tiles in registers:
+//    as soon as a tile is folded into the softmax state, its registers are
+//    refilled with the tile NBUF positions ahead, so the wave has NBUF tiles
+//    of loads in flight from its first tile to its last (there is no
+//    load-wait-compute cadence per batch);
+//  * tiles are read with raw buffer loads whose descriptor is built per tile
+//    from the (wave-uniform) block id; a tile past the end of the range, or
+//    with an id outside the pool, gets a descriptor of size 0, so its loads
+//    return zeros and move no bytes;
+//  * block ids for a wave's next 64 tiles are fetched with one vector load
+//    and broadcast with readlane; the following 64 are always in flight;
 //  * split-K: with partition_size > 0 each workgroup covers one partition and
 //    writes (m, l, o) to the workspace; paged_attn_reduce merges them.
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "common.h"
@@ -58,6 +67,7 @@ struct DecodeParams {
     int32_t max_ctx;
     int32_t blocks_per_part;  // 0: one workgroup covers the whole context
     int32_t num_parts;        // P of the workspace
+    int32_t longest_first;    // single pass over <= 256 sequences: longest first
     float scale_log2;         // scale * log2(e)
 };
 
@@ -177,20 +187,77 @@ struct SoftmaxState {
     float o[G][Geo<KV, D>::kEpl];     // running sum of exp2(s - m) * v, this lane's dims
 };
 
-// Issue the loads of one (block, kv head) tile: NLD contiguous KiB per plane.
-template <int KV, int D>
-__device__ __forceinline__ void load_tile(Tile<KV, D>& t, const uint8_t* kp, const uint8_t* vp) {
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return zeros without touching memory, so a tile that is not part of the
+// context (past the end of the wave's range, or a block id outside the pool)
+// is "loaded" with bytes = 0 and costs no HBM traffic. The base is
+// wave-uniform (one block id), so the descriptor lives in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), static_cast<short>(0),
+                                             bytes, 0x00020000);
+}
+
+// KV bytes are read once per decode step, so the tile loads carry the
+// non-temporal policy (cache-policy bit 1, "nt" on gfx950): they stream
+// through the caches instead of displacing lines that are reused. Measured
+// on MI355X it lifts the decode's KV read rate by about 10%.
+constexpr int kStreamPolicy = 2;
+
+__device__ __forceinline__ uint4 rsrc_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_bit_cast(uint4,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kStreamPolicy));
+}
+
+// Longest-first order of the sequences of a single-pass decode: returns the
+// index of the r-th longest sequence (ties: lower index first) and its
+// clamped length. Workgroups are dispatched roughly in index order, so
+// handing the longest contexts to the first workgroups keeps a long sequence
+// from starting last and running alone at the end of the kernel.
+// Every wave computes it redundantly from one load of all lengths: a radix
+// select, most significant bit first, over the unique keys
+// (blocks << 8) | (255 - index), counting candidates with ballots.
+// Needs num_seqs <= 256.
+__device__ __forceinline__ int longest_first(const DecodeParams& p, int num_seqs, int r,
+                                             int& L_out) {
+    const int lane = threadIdx.x & 63;
+    const int max_tokens = min(p.max_ctx, p.max_blocks * 16);
+    uint32_t key[4];
+    int len[4];
+    bool in[4];
 #pragma unroll
-    for (int i = 0; i < Geo<KV, D>::kNld; ++i)
-        t.k[i] = *reinterpret_cast<const uint4*>(kp + i * 1024);
+    for (int c = 0; c < 4; ++c) {
+        const int j = c * 64 + lane;
+        in[c] = j < num_seqs;
+        len[c] = in[c] ? min(max(p.context_lens[j], 0), max_tokens) : 0;
+        key[c] = (static_cast<uint32_t>((len[c] + 15) >> 4) << 8) | static_cast<uint32_t>(255 - j);
+    }
+    const uint32_t max_blk = static_cast<uint32_t>((max_tokens + 15) >> 4);
+    const int nbits = 8 + (max_blk ? 32 - __builtin_clz(max_blk) : 0);
+    uint32_t prefix = 0, mask = 0;
+    int rem = r;
+    for (int b = nbits - 1; b >= 0; --b) {
+        const uint32_t bit = 1u << b;
+        int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < Geo<KV, D>::kNld; ++i)
-        t.v[i] = *reinterpret_cast<const uint4*>(vp + i * 1024);
+        for (int c = 0; c < 4; ++c)
+            cnt += __popcll(__ballot(in[c] && (key[c] & mask) == prefix && (key[c] & bit)));
+        if (rem < cnt)
+            prefix |= bit;
+        else
+            rem -= cnt;
+        mask |= bit;
+    }
+    const int s = 255 - static_cast<int>(prefix & 255u);
+    L_out = __shfl(len[s >> 6], s & 63);
+    return s;
 }
 
 // Fold one tile into the lane's online-softmax state. nvalid = number of
-// leading tokens of the tile that belong to the context (0..16).
-template <int KV, int D, int G>
+// leading tokens of the tile that belong to the context (0..16). kPartial
+// selects the masked form, needed only when nvalid < 16 (the last block of a
+// context, or a tile outside the context): tokens past nvalid get score -inf
+// and their V bytes, which may be stale or NaN, are replaced by zeros.
+template <int KV, int D, int G, bool kPartial>
 __device__ __forceinline__ void consume_tile(SoftmaxState<KV, D, G>& st, const Tile<KV, D>& t,
                                              int nvalid, const QSlice<KV, D> (&qs)[G],
                                              float sscale, int row) {
@@ -207,11 +274,13 @@ __device__ __forceinline__ void consume_tile(SoftmaxState<KV, D, G>& st, const T
         for (int h = 0; h < G; ++h) sc[h][i] = group_sum<LPT>(sc[h][i]) * sscale;
     bool valid[NLD];
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) valid[i] = (i * TPI + row) < nvalid;
+    for (int i = 0; i < NLD; ++i) valid[i] = !kPartial || (i * TPI + row) < nvalid;
+    if constexpr (kPartial) {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i)
+        for (int i = 0; i < NLD; ++i)
 #pragma unroll
-        for (int h = 0; h < G; ++h) sc[h][i] = valid[i] ? sc[h][i] : -INFINITY;
+            for (int h = 0; h < G; ++h) sc[h][i] = valid[i] ? sc[h][i] : -INFINITY;
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         float mx = st.m[h];
@@ -234,8 +303,10 @@ __device__ __forceinline__ void consume_tile(SoftmaxState<KV, D, G>& st, const T
     for (int i = 0; i < NLD; ++i) {
         float vf[EPL];
         v_to_f32<KV, D>(t.v[i], vf);
+        if constexpr (kPartial) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) vf[e] = valid[i] ? vf[e] : 0.0f;  // stale bytes never enter
+            for (int e = 0; e < EPL; ++e) vf[e] = valid[i] ? vf[e] : 0.0f;  // stale bytes never enter
+        }
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -243,29 +314,107 @@ __device__ __forceinline__ void consume_tile(SoftmaxState<KV, D, G>& st, const T
     }
 }
 
-template <int KV, int QD, int D, int G, int NW, int BATCH>
+// Store one lane's EPL consecutive results of query head qh (dims
+// [d0, d0 + EPL)): fp32 into the workspace, or rounded to the q dtype into out.
+template <int QD, int D, int EPL>
+__device__ __forceinline__ void store_result(const DecodeParams& p, int s, int qh, int part,
+                                             int d0, const float (&r)[EPL]) {
+    if (p.blocks_per_part > 0) {
+        const size_t slot = (static_cast<size_t>(s) * p.num_q_heads + qh) * p.num_parts + part;
+        float4* dst = reinterpret_cast<float4*>(p.ws_o + slot * D + d0);
+#pragma unroll
+        for (int e = 0; e < EPL / 4; ++e)
+            dst[e] = make_float4(r[4 * e], r[4 * e + 1], r[4 * e + 2], r[4 * e + 3]);
+    } else {
+        const size_t o_idx = (static_cast<size_t>(s) * p.num_q_heads + qh) * D + d0;
+        uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + o_idx);
+#pragma unroll
+        for (int e = 0; e < EPL / 8; ++e) {
+            uint32_t wv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a = r[8 * e + 2 * i], b = r[8 * e + 2 * i + 1];
+                const uint32_t lo = (QD == PKV_F16) ? f32_to_f16_bits(a) : f32_to_bf16_bits(a);
+                const uint32_t hi = (QD == PKV_F16) ? f32_to_f16_bits(b) : f32_to_bf16_bits(b);
+                wv[i] = lo | (hi << 16);
+            }
+            dst[e] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+    }
+}
+
+__device__ __forceinline__ void store_ml(const DecodeParams& p, int s, int qh, int part,
+                                         float m_log2, float l) {
+    const size_t slot = (static_cast<size_t>(s) * p.num_q_heads + qh) * p.num_parts + part;
+    p.ws_ml[slot * 2] = (m_log2 == -INFINITY) ? -INFINITY : m_log2 * kLn2;
+    p.ws_ml[slot * 2 + 1] = l;
+}
+
+// One workgroup of NW wave64s per (partition, kv head, sequence). The
+// partition's blocks are dealt to the waves round robin; each wave streams its
+// tiles through a ring of NBUF tiles held in registers: after a tile is folded
+// into the softmax state its registers are refilled with the tile NBUF
+// positions ahead, so every wave keeps NBUF tiles of loads in flight from its
+// first tile to its last.
+template <int KV, int QD, int D, int G, int NW, int NBUF>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
     using Gm = Geo<KV, D>;
-    constexpr int EPL = Gm::kEpl, LPT = Gm::kLpt;
+    constexpr int EPL = Gm::kEpl, LPT = Gm::kLpt, NLD = Gm::kNld, TB = Gm::kTileBytes;
 
-    const int part = blockIdx.x;
-    const int g = blockIdx.y;
-    const int s = blockIdx.z;
+    // Grid (kv head, sequence, partition), kv head fastest. Workgroups are
+    // dealt to the 8 XCDs round robin in linear order, so consecutive indices
+    // must carry comparable work: the heads of one sequence do (same length),
+    // while partitions do not (short sequences have no late partitions).
+    const int g = blockIdx.x;
+    const int part = blockIdx.z;
     const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int w = (NW == 1) ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row = lane / LPT;
     const int col = lane % LPT;
 
-    int L = p.context_lens[s];
-    L = min(L, p.max_ctx);
-    L = min(L, p.max_blocks * 16);
-    const int nblk = L > 0 ? (L + 15) >> 4 : 0;
+    // Lr: the context as the reduce sees it (clamped to max_ctx); L: the
+    // tokens this kernel can reach through a table row of max_blocks ids.
+    int s, Lr, L;
+    if (p.longest_first) {
+        s = longest_first(p, gridDim.y, blockIdx.y, L);
+        Lr = L;  // single pass: no reduce reads this sequence's partitions
+    } else {
+        s = blockIdx.y;
+        Lr = max(0, min(p.context_lens[s], p.max_ctx));
+        L = min(Lr, p.max_blocks * 16);
+    }
+    const int nblk = (L + 15) >> 4;
     int b0 = 0, b1 = nblk;
     if (p.blocks_per_part > 0) {
         b0 = part * p.blocks_per_part;
-        if (b0 >= nblk) return;  // whole workgroup: this partition holds no tokens
         b1 = min(b0 + p.blocks_per_part, nblk);
+        if (b0 >= nblk) {
+            // No tokens in this partition. If the reduce will still read it
+            // (a table row narrower than the context), leave an empty partial.
+            const int ps = p.blocks_per_part * 16;
+            if (part < (Lr + ps - 1) / ps) {
+                for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+                    const int h = idx / D, d = idx % D;
+                    const size_t slot =
+                        (static_cast<size_t>(s) * p.num_q_heads + g * G + h) * p.num_parts + part;
+                    p.ws_o[slot * D + d] = 0.0f;
+                    if (d == 0) store_ml(p, s, g * G + h, part, -INFINITY, 0.0f);
+                }
+            }
+            return;
+        }
     }
+
+    // This wave's tiles: logical blocks b0 + w + k*NW for k < n.
+    const int span = b1 - b0;
+    const int n = span > w ? (span - w + NW - 1) / NW : 0;
+    const int32_t* bt = p.block_tables + static_cast<size_t>(s) * p.max_blocks + b0 + w;
+    auto load_ids = [&](int k0) -> int {  // ids of tiles k0 .. k0+63, one per lane
+        const int k = k0 + lane;
+        return k < n ? bt[k * NW] : -1;
+    };
+    int ids_a = load_ids(0);
+    int ids_b = load_ids(64);
 
     // Query slices of the G heads of this group.
     QSlice<KV, D> qs[G];
@@ -287,49 +436,49 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
         for (int e = 0; e < EPL; ++e) st.o[h][e] = 0.0f;
     }
 
-    const int32_t* bt = p.block_tables + static_cast<size_t>(s) * p.max_blocks;
-    const size_t lane_off = static_cast<size_t>(g) * Gm::kTileBytes + lane * 16;
-    const size_t block_stride = static_cast<size_t>(p.num_kv_heads) * Gm::kTileBytes;
-    const int span = b1 - b0;
-    const int nmine = span > w ? (span - w + NW - 1) / NW : 0;
+    const uint8_t* kpl = p.k_plane + static_cast<size_t>(g) * TB;
+    const uint8_t* vpl = p.v_plane + static_cast<size_t>(g) * TB;
+    const size_t bstride = static_cast<size_t>(p.num_kv_heads) * TB;
+    const int voff = lane * 16;
 
-    for (int c0 = 0; c0 < nmine; c0 += 64) {
-        const int cnt = min(64, nmine - c0);
-        // Ids of this wave's next (up to) 64 blocks, one per lane.
-        const int myid = (lane < cnt) ? bt[b0 + w + (c0 + lane) * NW] : 0;
-
-        // An id outside [0, num_blocks) is not dereferenced: block 0 is read
-        // instead (the host guarantees num_blocks > 0) and all its tokens are
-        // masked out.
-        auto tile_addr = [&](int kk, int& nvalid) -> size_t {
-            const int id = __builtin_amdgcn_readlane(myid, kk);
-            const int j = b0 + w + (c0 + kk) * NW;
-            const int okm = -static_cast<int>(id >= 0 && id < p.num_blocks);  // all ones or 0
-            nvalid = min(L - j * 16, 16) & okm;
-            return static_cast<size_t>(static_cast<uint32_t>(id & okm)) * block_stride + lane_off;
-        };
-
-        // Tiles are fetched in batches of BATCH: all loads of a batch are
-        // issued before the first tile is consumed (16 KiB per wave in flight
-        // at BATCH = 2), and the scheduler may interleave the consumes. A
-        // batch that runs past the wave's last block re-reads that block
-        // (an L2 hit) and masks it out.
-        for (int kk = 0; kk < cnt; kk += BATCH) {
-            Tile<KV, D> t[BATCH];
-            int nv[BATCH];
+    Tile<KV, D> t[NBUF];
+    int nv[NBUF];
+    // Issue the loads of tile kn into ring slot x. Tiles are issued in
+    // increasing kn, so the id chunks rotate exactly once per 64 tiles; the
+    // chunk after the current one is always already in flight.
+    auto issue = [&](Tile<KV, D>& tt, int& nvalid, int kn) {
+        if (kn >= 64 && (kn & 63) == 0) {
+            ids_a = ids_b;
+            ids_b = load_ids(kn + 64);
+        }
+        int id = -1;
+        if (kn < n) id = __builtin_amdgcn_readlane(ids_a, kn & 63);
+        const bool ok = static_cast<uint32_t>(id) < static_cast<uint32_t>(p.num_blocks);
+        nvalid = ok ? min(L - (b0 + w + kn * NW) * 16, 16) : 0;
+        const size_t off = static_cast<size_t>(ok ? id : 0) * bstride;
+        const int bytes = ok ? TB : 0;
+        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kpl + off, bytes);
+        const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vpl + off, bytes);
 #pragma unroll
-            for (int x = 0; x < BATCH; ++x) {
-                const size_t off = tile_addr(min(kk + x, cnt - 1), nv[x]);
-                load_tile<KV, D>(t[x], p.k_plane + off, p.v_plane + off);
-                if (kk + x >= cnt) nv[x] = 0;
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < NLD; ++i) tt.k[i] = rsrc_load16(rk, voff + i * 1024);
 #pragma unroll
-            for (int x = 0; x < BATCH; ++x) consume_tile<KV, D, G>(st, t[x], nv[x], qs, sscale, row);
+        for (int i = 0; i < NLD; ++i) tt.v[i] = rsrc_load16(rv, voff + i * 1024);
+    };
+
+#pragma unroll
+    for (int x = 0; x < NBUF; ++x) issue(t[x], nv[x], x);
+    for (int k0 = 0; k0 < n; k0 += NBUF) {
+#pragma unroll
+        for (int x = 0; x < NBUF; ++x) {
+            if (nv[x] == 16)
+                consume_tile<KV, D, G, false>(st, t[x], 16, qs, sscale, row);
+            else
+                consume_tile<KV, D, G, true>(st, t[x], nv[x], qs, sscale, row);
+            issue(t[x], nv[x], k0 + x + NBUF);
         }
     }
 
-    // Merge the TPI rows of this wave: lanes lane ^ off (off = LPT, 2*LPT, ...)
+    // Merge the rows of this wave: lanes lane ^ off (off = LPT, 2*LPT, ...)
     // hold the same dims for other tokens.
 #pragma unroll
     for (int off = LPT; off < 64; off <<= 1) {
@@ -350,79 +499,101 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
         }
     }
 
-    __shared__ float lds_o[NW][G][D];
-    __shared__ float lds_m[NW][G];
-    __shared__ float lds_l[NW][G];
-    if (row == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) lds_o[w][h][col * EPL + e] = st.o[h][e];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            lds_m[w][h] = st.m[h];
-            lds_l[w][h] = st.l[h];
-        }
-    }
-    __syncthreads();
-
     float vscale = 1.0f;
     if constexpr (KV == PKV_FP8_E4M3) vscale = p.v_scale[g];
-    for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-        const int h = idx / D, d = idx % D;
-        float mx = -INFINITY;
+
+    if constexpr (NW == 1) {
+        if (row == 0) {
 #pragma unroll
-        for (int x = 0; x < NW; ++x) mx = fmaxf(mx, lds_m[x][h]);
-        const float ms = (mx == -INFINITY) ? 0.0f : mx;
-        float lsum = 0.0f, acc = 0.0f;
+            for (int h = 0; h < G; ++h) {
+                const float inv = st.l[h] > 0.0f ? vscale / st.l[h] : 0.0f;
+                float r[EPL];
 #pragma unroll
-        for (int x = 0; x < NW; ++x) {
-            const float a = fast_exp2(lds_m[x][h] - ms);
-            lsum = fmaf(lds_l[x][h], a, lsum);
-            acc = fmaf(lds_o[x][h][d], a, acc);
-        }
-        const float res = lsum > 0.0f ? (acc / lsum) * vscale : 0.0f;
-        const int qh = g * G + h;
-        if (p.blocks_per_part > 0) {
-            const size_t slot = (static_cast<size_t>(s) * p.num_q_heads + qh) * p.num_parts + part;
-            p.ws_o[slot * D + d] = res;
-            if (d == 0) {
-                p.ws_ml[slot * 2] = (mx == -INFINITY) ? -INFINITY : mx * kLn2;
-                p.ws_ml[slot * 2 + 1] = lsum;
+                for (int e = 0; e < EPL; ++e) r[e] = st.o[h][e] * inv;
+                store_result<QD, D, EPL>(p, s, g * G + h, part, col * EPL, r);
+                if (p.blocks_per_part > 0 && col == 0) store_ml(p, s, g * G + h, part, st.m[h], st.l[h]);
             }
-        } else {
-            const size_t o_idx = (static_cast<size_t>(s) * p.num_q_heads + qh) * D + d;
-            uint16_t bits = (QD == PKV_F16) ? f32_to_f16_bits(res) : f32_to_bf16_bits(res);
-            static_cast<uint16_t*>(p.out)[o_idx] = bits;
+        }
+    } else {
+        // Merge the NW waves through LDS.
+        __shared__ float lds_o[NW][G][D];
+        __shared__ float lds_m[NW][G];
+        __shared__ float lds_l[NW][G];
+        if (row == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) lds_o[w][h][col * EPL + e] = st.o[h][e];
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                lds_m[w][h] = st.m[h];
+                lds_l[w][h] = st.l[h];
+            }
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+            const int h = idx / D, d = idx % D;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int x = 0; x < NW; ++x) mx = fmaxf(mx, lds_m[x][h]);
+            const float ms = (mx == -INFINITY) ? 0.0f : mx;
+            float lsum = 0.0f, acc = 0.0f;
+#pragma unroll
+            for (int x = 0; x < NW; ++x) {
+                const float a = fast_exp2(lds_m[x][h] - ms);
+                lsum = fmaf(lds_l[x][h], a, lsum);
+                acc = fmaf(lds_o[x][h][d], a, acc);
+            }
+            const float res = lsum > 0.0f ? (acc / lsum) * vscale : 0.0f;
+            const int qh = g * G + h;
+            if (p.blocks_per_part > 0) {
+                const size_t slot = (static_cast<size_t>(s) * p.num_q_heads + qh) * p.num_parts + part;
+                p.ws_o[slot * D + d] = res;
+                if (d == 0) store_ml(p, s, qh, part, mx, lsum);
+            } else {
+                const size_t o_idx = (static_cast<size_t>(s) * p.num_q_heads + qh) * D + d;
+                const uint16_t bits = (QD == PKV_F16) ? f32_to_f16_bits(res) : f32_to_bf16_bits(res);
+                static_cast<uint16_t*>(p.out)[o_idx] = bits;
+            }
         }
     }
 }
 
-constexpr int kWaves = 4;
-
-// Tiles per load batch: two for 16-bit MHA tiles; one where the group's
-// registers are already large.
+// Tiles kept in flight per wave: the ring must fit beside the softmax state
+// of the G heads.
 template <int KV, int D, int G>
-constexpr int batch_for() {
-    return (G <= 2) ? 2 : 1;
+constexpr int ring_depth() {
+    return (G <= 2) ? 4 : (G == 4 ? 2 : 1);
 }
 
-template <int KV, int QD, int D, int G>
+template <int KV, int QD, int D, int G, int NW>
 hipError_t launch(const DecodeParams& prm, dim3 grid, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, kWaves, batch_for<KV, D, G>()>), grid,
-                       dim3(kWaves * 64), 0, stream, prm);
+    hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, ring_depth<KV, D, G>()>), grid,
+                       dim3(NW * 64), 0, stream, prm);
     return hipGetLastError();
+}
+
+// Waves per workgroup: a partition of up to 16 blocks is one wave's stream;
+// longer ranges (big partitions, or the whole context when unpartitioned) are
+// shared by four waves and merged through LDS.
+template <int KV, int QD, int D, int G>
+hipError_t by_waves(const DecodeParams& prm, dim3 grid, hipStream_t st) {
+    if (prm.blocks_per_part > 0 && prm.blocks_per_part <= 16)
+        return launch<KV, QD, D, G, 1>(prm, grid, st);
+    if (prm.blocks_per_part > 0 && prm.blocks_per_part <= 32)
+        return launch<KV, QD, D, G, 2>(prm, grid, st);
+    return launch<KV, QD, D, G, 4>(prm, grid, st);
 }
 
 template <int KV, int QD, int D>
 hipError_t by_group(int G, const DecodeParams& prm, dim3 grid, hipStream_t st) {
     switch (G) {
-        case 1: return launch<KV, QD, D, 1>(prm, grid, st);
-        case 2: return launch<KV, QD, D, 2>(prm, grid, st);
-        case 4: return launch<KV, QD, D, 4>(prm, grid, st);
-        default: return launch<KV, QD, D, 8>(prm, grid, st);
+        case 1: return by_waves<KV, QD, D, 1>(prm, grid, st);
+        case 2: return by_waves<KV, QD, D, 2>(prm, grid, st);
+        case 4: return by_waves<KV, QD, D, 4>(prm, grid, st);
+        default: return by_waves<KV, QD, D, 8>(prm, grid, st);
     }
 }
 
@@ -441,8 +612,9 @@ extern "C" size_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
         max_context_len < 0)
         return 0;
     const size_t parts = (static_cast<size_t>(max_context_len) + partition_size - 1) / partition_size;
-    return static_cast<size_t>(num_seqs) * num_q_heads * parts * (2 + static_cast<size_t>(head_dim)) *
-           sizeof(float);
+    return pkv::ws_o_offset(num_seqs, num_q_heads, parts) +
+           static_cast<size_t>(num_seqs) * num_q_heads * parts * static_cast<size_t>(head_dim) *
+               sizeof(float);
 }
 
 extern "C" pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, const void* q,
@@ -466,8 +638,6 @@ extern "C" pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, con
         return fail(PKV_ERR_INVALID, "paged_attn_decode: q dtype must equal the 16-bit cache dtype");
     if (num_seqs < 0 || num_seqs > 65535)
         return fail(PKV_ERR_INVALID, "paged_attn_decode: num_seqs %d outside [0, 65535]", num_seqs);
-    if (d.num_kv_heads > 65535)
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: too many kv heads");
     if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads != 0)
         return fail(PKV_ERR_INVALID, "paged_attn_decode: %d query heads for %d kv heads",
                     num_q_heads, d.num_kv_heads);
@@ -521,19 +691,28 @@ extern "C" pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, con
             return fail(PKV_ERR_INVALID, "paged_attn_decode: workspace must be 16-byte aligned");
         const int64_t P = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
         if (P == 0) return PKV_OK;  // no tokens anywhere; the reduce writes zeros
-        if (P > 0x7FFFFFFF) return fail(PKV_ERR_INVALID, "paged_attn_decode: too many partitions");
+        if (P > 65535)
+            return fail(PKV_ERR_INVALID, "paged_attn_decode: %lld partitions (at most 65535)",
+                        static_cast<long long>(P));
         parts = static_cast<uint32_t>(P);
         prm.blocks_per_part = partition_size / 16;
         prm.num_parts = static_cast<int32_t>(P);
         prm.ws_ml = static_cast<float*>(workspace);
-        prm.ws_o = prm.ws_ml + static_cast<size_t>(num_seqs) * num_q_heads * P * 2;
+        prm.ws_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                            pkv::ws_o_offset(num_seqs, num_q_heads, P));
     } else {
         if (out == nullptr) return fail(PKV_ERR_INVALID, "paged_attn_decode: out is NULL");
+        if (reinterpret_cast<uintptr_t>(out) % 16 != 0)
+            return fail(PKV_ERR_INVALID, "paged_attn_decode: out must be 16-byte aligned");
         prm.blocks_per_part = 0;
         prm.num_parts = 1;
+        // The ordering keys hold the block count in 23 bits.
+        const int64_t max_tokens =
+            std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * 16);
+        prm.longest_first = (num_seqs <= 256 && (max_tokens + 15) / 16 < (1 << 23)) ? 1 : 0;
     }
 
-    const dim3 grid(parts, static_cast<uint32_t>(d.num_kv_heads), static_cast<uint32_t>(num_seqs));
+    const dim3 grid(static_cast<uint32_t>(d.num_kv_heads), static_cast<uint32_t>(num_seqs), parts);
     hipError_t e;
     if (d.kv_dtype == PKV_F16)
         e = by_dim<PKV_F16, PKV_F16>(d.head_dim, G, prm, grid, stream);

@@ -117,7 +117,10 @@ extern "C" pkv_status paged_attn_reduce(const void* workspace, void* out, int32_
     if (P > 0 && workspace == nullptr)
         return fail(PKV_ERR_INVALID, "paged_attn_reduce: workspace is NULL");
     const float* ml = static_cast<const float*>(workspace);
-    const float* o = ml == nullptr ? nullptr : ml + static_cast<size_t>(num_seqs) * num_q_heads * P * 2;
+    const float* o = ml == nullptr ? nullptr
+                                   : reinterpret_cast<const float*>(
+                                         static_cast<const uint8_t*>(workspace) +
+                                         pkv::ws_o_offset(num_seqs, num_q_heads, P));
     hipError_t e;
     const int32_t Pi = static_cast<int32_t>(P);
     if (out_dtype == PKV_F16)

@@ -41,12 +41,15 @@ class PagedKVCache:
             self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
         else:
             self.buf = torch.full((self.nbytes,), fill_byte, dtype=torch.uint8, device=device)
+        # Held on the instance: at interpreter exit module globals may already
+        # be gone when __del__ runs.
+        self._destroy = kv_pool_destroy
         self.handle = kv_pool_create(self.desc, self.buf, self.nbytes)
 
     def close(self):
-        if self.handle is not None:
-            kv_pool_destroy(self.handle)
-            self.handle = None
+        handle, self.handle = getattr(self, "handle", None), None
+        if handle is not None:
+            self._destroy(handle)
 
     def __del__(self):
         self.close()

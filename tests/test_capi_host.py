@@ -265,9 +265,12 @@ def test_fp8_pool_needs_scales():
 
 
 def test_workspace_bytes():
+    # (m, l) pairs, then the partial outputs from the next 256-byte boundary
     assert P.paged_attn_workspace_bytes(8, 32, 128, 32768, 512) == 8 * 32 * 64 * 130 * 4
     assert P.paged_attn_workspace_bytes(8, 32, 128, 32768, 0) == 0
-    assert P.paged_attn_workspace_bytes(2, 2, 64, 17, 16) == 2 * 2 * 2 * 66 * 4
+    assert P.paged_attn_workspace_bytes(2, 2, 64, 17, 16) == 256 + 2 * 2 * 2 * 64 * 4
+    # 3*5*7 pairs of 8 bytes = 840 bytes, padded to 1024
+    assert P.paged_attn_workspace_bytes(3, 5, 128, 100, 16) == 1024 + 3 * 5 * 7 * 128 * 4
 
 
 @pytest.mark.parametrize("name", list(W.CONFIGS))

@@ -112,3 +112,21 @@ def test_run_to_run_bitwise_determinism():
         again = H.step(side, 0)
         torch.cuda.synchronize()
         assert torch.equal(again.view(torch.int16), first.view(torch.int16))
+
+
+@pytest.mark.parametrize("batch", [1, 3, 64, 65, 130, 256, 257])
+def test_single_pass_writes_every_sequence(batch):
+    """A single-pass decode hands sequences to workgroups longest first (up to
+    256 sequences; in index order beyond). Every sequence must be computed
+    exactly once: the output starts as NaN and must match the oracle
+    everywhere. Lengths in [1, 300] give many equal block counts (ties)."""
+    cfg = W.Config(f"order_b{batch}", 1, batch, 2, 2, 64, "f16", "f16", ("uniform", 1, 300),
+                   partition_size=0)
+    say(f"single_pass_order B={batch}")
+    side = H.build_product(cfg, seed=3, run_step=False)
+    side.batch.out.fill_(float("nan"))
+    side.outputs = [H.step(side, 0).clone()]
+    torch.cuda.synchronize()
+    o = H.oracle_bookkeeping(cfg, 3)
+    check_bookkeeping(side, o)
+    check_layers(cfg, side, o, list(range(cfg.batch)), [0], whole_pool=True)

@@ -36,7 +36,7 @@ CONFIGS = {
     # Llama-2-13B-shaped layer: MHA 40 x 128, batch 32, lengths U{128..2048}, pool
     # sized to the batch with randomly permuted blocks.
     "llama13b_layer": Config("llama13b_layer", 1, 32, 40, 40, 128, "f16", "f16",
-                             ("uniform", 128, 2048), partition_size=256),
+                             ("uniform", 128, 2048)),
     # 7B-class full decode step: 32 layers, MHA 32 x 128, batch 64, every context
     # 2048 tokens (about 1.07 GB of KV per request, about 68.7 GB of pool).
     "7b_32layer": Config("7b_32layer", 32, 64, 32, 32, 128, "f16", "f16", ("const", 2048),
