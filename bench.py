@@ -74,7 +74,7 @@ class Workload:
     """One decode-step workload, product side: pool, tables, inputs, batch."""
 
     def __init__(self, cfg, seed=0, device="cuda", partition_size=None, fill_byte=None,
-                 placement_seed=None, keep_cached_inputs=True):
+                 placement_seed=None, keep_cached_inputs=True, balanced=None):
         import torch
 
         import workloads as W
@@ -104,7 +104,8 @@ class Workload:
         self.k_scale, self.v_scale = [], []
         n_cached = int(self.slots_cached.size)
         self.batch = DecodeBatch(self.cache, self.tables, lens, cfg.q_heads, qdt,
-                                 self.partition_size, device=device)
+                                 self.partition_size, device=device,
+                                 balanced=cfg.balanced if balanced is None else balanced)
         for layer in range(cfg.layers):
             kc = W.kv_tokens(cfg, seed, layer, "k", "cached", n_cached, device)
             vc = W.kv_tokens(cfg, seed, layer, "v", "cached", n_cached, device)
@@ -120,7 +121,9 @@ class Workload:
             self.v_new.append(vn)
             self.k_scale.append(ks)
             self.v_scale.append(vs)
-            if keep_cached_inputs:
+            # keep_cached_inputs: True keeps every layer's prefill rows (the
+            # tests compare them), "first" only layer 0's (the CPU baseline).
+            if keep_cached_inputs is True or (keep_cached_inputs == "first" and layer == 0):
                 self.k_cached.append(kc)
                 self.v_cached.append(vc)
             else:
@@ -314,7 +317,7 @@ def main(argv=None):
     cfg = W.CONFIGS[args.workload]
     torch.cuda.set_device(0)
     first = Workload(cfg, args.seed, "cuda", args.partition_size,
-                     keep_cached_inputs=not args.no_cpu_baseline)
+                     keep_cached_inputs=False if args.no_cpu_baseline else "first")
     pool_bytes = first.cache.nbytes
     reps = args.replicas or max(1, min(8, math.ceil(2e9 / max(pool_bytes, 1))))
     ws = [first] + [Workload(cfg, args.seed + r, "cuda", args.partition_size,
@@ -391,6 +394,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": cfg.name,
+            "single_pass": ("balanced" if first.batch.balanced else "per-sequence")
+            if first.partition_size == 0 else None,
             "layers": cfg.layers, "batch": cfg.batch, "q_heads": cfg.q_heads,
             "kv_heads": cfg.kv_heads, "head_dim": cfg.head_dim, "block_size": BS,
             "kv_dtype": cfg.kv_dtype, "q_dtype": cfg.q_dtype,

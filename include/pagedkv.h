@@ -192,11 +192,16 @@ pkv_status kv_cache_append(const pkv_pool* pool, int32_t layer, const void* k, c
                            int32_t src_dtype, const int64_t* slot_mapping, int32_t num_tokens,
                            const float* k_scale, const float* v_scale, hipStream_t stream);
 
-/* Bytes of workspace a partitioned decode needs: per (sequence, query head,
- * partition) an fp32 max, an fp32 sum and head_dim fp32 outputs, with
- * ceil(max_context_len / partition_size) partitions per sequence, laid out as
- * described below (OFF + num_seqs*num_q_heads*P*head_dim*4). 0 when
- * partition_size == 0 or an argument is out of range. */
+/* Bytes of workspace paged_attn_decode needs.
+ * partition_size > 0: per (sequence, query head, partition) an fp32 max, an
+ *   fp32 sum and head_dim fp32 outputs, with ceil(max_context_len /
+ *   partition_size) partitions per sequence, laid out as described below
+ *   (OFF + num_seqs*num_q_heads*P*head_dim*4).
+ * partition_size == 0: the balanced single pass (see paged_attn_decode): two
+ *   partial slots per wave of the launch, 8 waves per compute unit of the
+ *   current device, each min(num_q_heads, 8) x (head_dim + 4) fp32; 0 when
+ *   num_seqs > 4096 (only the per-sequence single pass exists there).
+ * 0 when an argument is out of range. */
 size_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_size);
 
@@ -226,11 +231,19 @@ size_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * num_q_heads must be num_kv_heads * G with G in {1, 2, 4, 8}.
  * k_scale, v_scale: device fp32 [num_kv_heads] for an FP8 cache (value =
  *   decode(code) * scale), ignored otherwise.
- * partition_size == 0: one pass over the whole context writes out; workspace
- *   is unused. partition_size > 0 (a multiple of 16): every partition writes
- *   its (m_p, l_p, o_p) to workspace (layout above) and out is not touched;
- *   the caller must then run paged_attn_reduce on the same stream with the
- *   same shapes. workspace_bytes must be >= paged_attn_workspace_bytes(...).
+ * partition_size == 0: a single pass writes out; no reduce call follows.
+ *   - workspace == NULL (or an FP8 cache, or num_seqs > 4096): one workgroup
+ *     per (sequence, kv head), sequences handed out longest first;
+ *   - otherwise the balanced form: the tiles of the whole batch are cut into
+ *     equal ranges, one per resident wave, so the work is even whatever the
+ *     length mix; contexts split between waves leave partials in workspace
+ *     (256-byte aligned, >= paged_attn_workspace_bytes(..., 0) bytes, no
+ *     initial contents needed) that a second kernel of the same call merges.
+ *     Calls that share a workspace must be ordered on one stream.
+ * partition_size > 0 (a multiple of 16): every partition writes its
+ *   (m_p, l_p, o_p) to workspace (layout above) and out is not touched; the
+ *   caller must then run paged_attn_reduce on the same stream with the same
+ *   shapes. workspace_bytes must be >= paged_attn_workspace_bytes(...).
  * Limits: num_seqs <= 65535; ceil(max_context_len / partition_size) <= 65535.
  * Errors: INVALID (shapes, dtypes, NULLs, alignment, workspace too small,
  *   limits), HIP. */

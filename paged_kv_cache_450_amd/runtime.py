@@ -113,12 +113,13 @@ class DecodeBatch:
     """Device-side state of one batch: tables, lengths, workspace and output.
 
     run(layer, q) issues paged_attn_decode and, when partitioned, paged_attn_reduce
-    on one stream; the output is self.out.
+    on one stream; the output is self.out. A single pass (partition_size 0) is
+    balanced across the GPU unless balanced=False.
     """
 
     def __init__(self, cache: PagedKVCache, tables: np.ndarray, lens, num_q_heads: int,
                  q_dtype, partition_size: int = 0, scale=None, k_scale=None, v_scale=None,
-                 max_context_len=None, device="cuda"):
+                 max_context_len=None, device="cuda", balanced: bool = True):
         self.cache = cache
         lens = np.asarray(lens, dtype=np.int32)
         self.num_seqs = lens.size
@@ -135,8 +136,15 @@ class DecodeBatch:
                                device=device)
         ws = paged_attn_workspace_bytes(self.num_seqs, num_q_heads, self.head_dim,
                                         self.max_context_len, partition_size)
-        self.workspace = (torch.empty(max(ws, 16) // 4, dtype=torch.float32, device=device)
-                          if partition_size > 0 else None)
+        # partition_size > 0: split-K partials for paged_attn_reduce.
+        # partition_size == 0 with a workspace: the balanced single pass (its
+        # split contexts' partials); without one: one workgroup per
+        # (sequence, kv head).
+        self.balanced = partition_size == 0 and balanced and ws > 0
+        if partition_size > 0 or self.balanced:
+            self.workspace = torch.empty(max(ws, 16) // 4, dtype=torch.float32, device=device)
+        else:
+            self.workspace = None
 
     def decode(self, layer: int, q, stream=None):
         paged_attn_decode(self.cache.handle, layer, q, None if self.partition_size else self.out,

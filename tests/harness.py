@@ -34,10 +34,11 @@ assert _BS == BS
 
 
 def build_product(cfg, seed=0, device="cuda", partition_size=None, fill_byte=POISON,
-                  run_step=True, placement_seed=None):
+                  run_step=True, placement_seed=None, balanced=None):
     """Product side: pool, bookkeeping, prefill appends, then (run_step) one
     decode step per layer whose outputs are kept in side.outputs."""
-    side = Workload(cfg, seed, device, partition_size, fill_byte, placement_seed)
+    side = Workload(cfg, seed, device, partition_size, fill_byte, placement_seed,
+                    balanced=balanced)
     if run_step:
         side.outputs = [step(side, layer).clone() for layer in range(cfg.layers)]
     return side

@@ -267,7 +267,13 @@ def test_fp8_pool_needs_scales():
 def test_workspace_bytes():
     # (m, l) pairs, then the partial outputs from the next 256-byte boundary
     assert P.paged_attn_workspace_bytes(8, 32, 128, 32768, 512) == 8 * 32 * 64 * 130 * 4
-    assert P.paged_attn_workspace_bytes(8, 32, 128, 32768, 0) == 0
+    # partition_size 0: the balanced single pass, two partial slots per wave of
+    # min(Hq, 8) heads x (D + 4) floats; 8 waves per CU, and with no GPU
+    # visible the CU count is MI355X's 256.
+    waves = 256 * 8
+    assert P.paged_attn_workspace_bytes(8, 32, 128, 32768, 0) == waves * 2 * 8 * 132 * 4
+    assert P.paged_attn_workspace_bytes(3, 5, 64, 100, 0) == waves * 2 * 5 * 68 * 4
+    assert P.paged_attn_workspace_bytes(4097, 8, 128, 100, 0) == 0  # per-sequence path only
     assert P.paged_attn_workspace_bytes(2, 2, 64, 17, 16) == 256 + 2 * 2 * 2 * 64 * 4
     # 3*5*7 pairs of 8 bytes = 840 bytes, padded to 1024
     assert P.paged_attn_workspace_bytes(3, 5, 128, 100, 16) == 1024 + 3 * 5 * 7 * 128 * 4

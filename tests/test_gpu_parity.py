@@ -103,10 +103,13 @@ def test_partition_sizes(ps):
     check_layers(cfg, side, o, list(range(cfg.batch)), [0], whole_pool=False)
 
 
-def test_run_to_run_bitwise_determinism():
+@pytest.mark.parametrize("ps", [512, 0])
+def test_run_to_run_bitwise_determinism(ps):
+    """Repeated calls give identical bits (the balanced single pass at ps 0
+    included: its merge order is fixed by the split, not by timing)."""
     cfg = W.scaled("gqa_prefix")
-    say("determinism")
-    side = H.build_product(cfg, seed=2)
+    say(f"determinism ps={ps}")
+    side = H.build_product(cfg, seed=2, partition_size=ps)
     first = side.outputs[0].clone()
     for _ in range(3):
         again = H.step(side, 0)
@@ -114,19 +117,48 @@ def test_run_to_run_bitwise_determinism():
         assert torch.equal(again.view(torch.int16), first.view(torch.int16))
 
 
+@pytest.mark.parametrize("balanced", [False, True])
 @pytest.mark.parametrize("batch", [1, 3, 64, 65, 130, 256, 257])
-def test_single_pass_writes_every_sequence(batch):
-    """A single-pass decode hands sequences to workgroups longest first (up to
-    256 sequences; in index order beyond). Every sequence must be computed
-    exactly once: the output starts as NaN and must match the oracle
-    everywhere. Lengths in [1, 300] give many equal block counts (ties)."""
+def test_single_pass_writes_every_sequence(batch, balanced):
+    """Single pass, both forms. Per sequence: workgroups take sequences longest
+    first (up to 256 sequences; in index order beyond). Balanced: the batch's
+    tiles are cut into equal ranges, one per wave (fewer ranges than waves when
+    the batch is tiny), and contexts split between waves are merged by the last
+    wave to arrive. Every sequence must be computed exactly once: the output
+    starts as NaN and must match the oracle everywhere. Lengths in [1, 300]
+    give many equal block counts and many one-block contexts."""
     cfg = W.Config(f"order_b{batch}", 1, batch, 2, 2, 64, "f16", "f16", ("uniform", 1, 300),
                    partition_size=0)
-    say(f"single_pass_order B={batch}")
-    side = H.build_product(cfg, seed=3, run_step=False)
+    say(f"single_pass B={batch} balanced={balanced}")
+    side = H.build_product(cfg, seed=3, run_step=False, balanced=balanced)
+    assert side.batch.balanced == balanced
     side.batch.out.fill_(float("nan"))
     side.outputs = [H.step(side, 0).clone()]
     torch.cuda.synchronize()
     o = H.oracle_bookkeeping(cfg, 3)
+    check_bookkeeping(side, o)
+    check_layers(cfg, side, o, list(range(cfg.batch)), [0], whole_pool=True)
+
+
+GROUPED = [  # (q heads, kv heads, head_dim, dtype): G = 2, 4, 8 on both head sizes
+    (4, 2, 64, "f16"), (8, 2, 128, "bf16"), (16, 2, 64, "bf16"), (16, 4, 128, "f16"),
+    (8, 1, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("ps", [0, 64, 512])
+@pytest.mark.parametrize("hq,hkv,dim,dt", GROUPED)
+def test_grouped_heads(hq, hkv, dim, dt, ps):
+    """Grouped query heads (matrix-core path) on both 16-bit dtypes and head
+    sizes, single pass and split-K with one, two and four waves per
+    partition; lengths in [1, 300] give partial last blocks everywhere."""
+    cfg = W.Config(f"grouped_{hq}_{hkv}_{dim}_{dt}", 1, 5, hq, hkv, dim, dt, dt,
+                   ("uniform", 1, 300), partition_size=ps)
+    say(f"grouped Hq={hq} Hkv={hkv} D={dim} {dt} ps={ps}")
+    side = H.build_product(cfg, seed=4, run_step=False)
+    side.batch.out.fill_(float("nan"))
+    side.outputs = [H.step(side, 0).clone()]
+    torch.cuda.synchronize()
+    o = H.oracle_bookkeeping(cfg, 4)
     check_bookkeeping(side, o)
     check_layers(cfg, side, o, list(range(cfg.batch)), [0], whole_pool=True)

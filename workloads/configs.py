@@ -18,6 +18,7 @@ class Config:
     pool_blocks: Optional[int] = None   # None: exactly the blocks the batch needs
     share_prefix_tokens: int = 0        # > 0: even-indexed sequences share this many tokens
     partition_size: int = 0             # default split-K partition (0: one pass)
+    balanced: bool = True               # single pass: balanced over waves (else per sequence)
 
     @property
     def group(self) -> int:
@@ -32,21 +33,20 @@ class Config:
 CONFIGS = {
     # 1 layer, batch 4, 4 query = 4 kv heads, dim 64, lengths U{1..200}, pool of
     # 64 blocks in shuffled order, one append per sequence.
-    "tiny": Config("tiny", 1, 4, 4, 4, 64, "f16", "f16", ("uniform", 1, 200), pool_blocks=64),
+    "tiny": Config("tiny", 1, 4, 4, 4, 64, "f16", "f16", ("uniform", 1, 200), pool_blocks=64,
+                   balanced=False),
     # Llama-2-13B-shaped layer: MHA 40 x 128, batch 32, lengths U{128..2048}, pool
     # sized to the batch with randomly permuted blocks.
     "llama13b_layer": Config("llama13b_layer", 1, 32, 40, 40, 128, "f16", "f16",
-                             ("uniform", 128, 2048)),
+                             ("uniform", 128, 2048), balanced=False),
     # 7B-class full decode step: 32 layers, MHA 32 x 128, batch 64, every context
     # 2048 tokens (about 1.07 GB of KV per request, about 68.7 GB of pool).
-    "7b_32layer": Config("7b_32layer", 32, 64, 32, 32, 128, "f16", "f16", ("const", 2048),
-                         partition_size=512),
+    "7b_32layer": Config("7b_32layer", 32, 64, 32, 32, 128, "f16", "f16", ("const", 2048)),
     # GQA 64 query / 8 kv heads x 128 in bf16, batch 128, lengths log-normal
     # (median 1000) clipped to [16, 8192]; half the sequences share a 512-token
     # prefix through refcounted blocks.
     "gqa_prefix": Config("gqa_prefix", 1, 128, 64, 8, 128, "bf16", "bf16",
-                         ("lognormal", 1000.0, 1.0, 16, 8192), share_prefix_tokens=512,
-                         partition_size=512),
+                         ("lognormal", 1000.0, 1.0, 16, 8192), share_prefix_tokens=512),
     # Long-context split-K: batch 8, MHA 32 x 128, lengths U{16384..32768}, KV in
     # FP8 E4M3 with per-head fp32 scales, q fp16, partitions of 512 tokens.
     "longctx_fp8": Config("longctx_fp8", 1, 8, 32, 32, 128, "e4m3", "f16",
