@@ -252,7 +252,10 @@ __device__ __forceinline__ int longest_first(const DecodeParams& p, int num_seqs
         mask |= bit;
     }
     const int s = 255 - static_cast<int>(prefix & 255u);
-    L_out = __shfl(len[s >> 6], s & 63);
+    // Uniform by construction; readfirstlane tells the compiler so (otherwise
+    // every value derived from it, down to the tile descriptors, is treated as
+    // per-lane and each buffer load becomes a loop over distinct descriptors).
+    L_out = __builtin_amdgcn_readfirstlane(__shfl(len[s >> 6], s & 63));
     return s;
 }
 
@@ -677,11 +680,17 @@ __device__ __forceinline__ f32x4_t mfma_pv(s16x4_t a, s16x4_t b, f32x4_t c) {
                                                      __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
 }
 
+// Two fp32 values rounded to nearest even into the 16-bit type, packed
+// (hardware conversions; v_cvt_pk_bf16_f32 on gfx950). Not for NaN inputs.
 template <int KV>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    const uint32_t lo = (KV == PKV_F16) ? f32_to_f16_bits(a) : f32_to_bf16_bits(a);
-    const uint32_t hi = (KV == PKV_F16) ? f32_to_f16_bits(b) : f32_to_bf16_bits(b);
-    return lo | (hi << 16);
+    if constexpr (KV == PKV_F16) {
+        return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(a))) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(b))) << 16);
+    } else {
+        return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+    }
 }
 
 template <int D>
@@ -701,9 +710,19 @@ struct MfmaTile {
     uint4 v[MfmaGeo<D>::kNv];
 };
 
-template <int KV, int D, bool kPartial>
-__device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid,
-                                             const uint4 (&qop)[MfmaGeo<D>::kNk],
+// The Q^T operand of a wave lives in its LDS (leaving the registers to a
+// deeper tile ring), chunk-major so that each per-tile read of one 32-dim
+// chunk is a contiguous, conflict-free 1 KiB.
+template <int D>
+struct QLds {
+    const uint8_t* base;  // kNk x 1 KiB
+    __device__ __forceinline__ uint4 get(int c, int lane) const {
+        return *reinterpret_cast<const uint4*>(base + c * 1024 + lane * 16);
+    }
+};
+
+template <int KV, int D, bool kPartial, class QSrc>
+__device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid, const QSrc& qsrc,
                                              f32x4_t (&o)[MfmaGeo<D>::kNd], float& m, float& lsum,
                                              float sscale, uint8_t* stage, int lane) {
     using Gm = MfmaGeo<D>;
@@ -712,7 +731,7 @@ __device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid,
     // Scores of head hl for tokens 4*kg + r.
     f32x4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int c = 0; c < Gm::kNk; ++c) sacc = mfma_qk<KV>(t.k[c], qop[c], sacc);
+    for (int c = 0; c < Gm::kNk; ++c) sacc = mfma_qk<KV>(t.k[c], qsrc.get(c, lane), sacc);
     float sc[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -722,20 +741,27 @@ __device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid,
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx);
-    const float ms = (mnew == -INFINITY) ? 0.0f : mnew;
-    const float alpha = fast_exp2(m - ms);
-    float pr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sc[r] - ms);
-    lsum = fmaf(lsum, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m = mnew;
-    if (__ballot(alpha != 1.0f)) {  // some head's running max moved
+    // m is the reference of the exponentials. It is raised, and the sums
+    // rescaled, only when a score passes it by more than kSlack (log2 units),
+    // so probabilities stay below 2^kSlack and rescaling is rare: the O^T
+    // accumulators live in AGPRs, where a rescale costs three instructions
+    // per element.
+    constexpr float kSlack = 8.0f;
+    if (__ballot(mx > m + kSlack)) {
+        const float mnew = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - mnew);  // m = -inf: 0 (o and lsum are still 0)
+        lsum *= alpha;
 #pragma unroll
         for (int j = 0; j < Gm::kNd; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) o[j][r] *= alpha;
+        m = mnew;
     }
+    const float ms = (m == -INFINITY) ? 0.0f : m;
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sc[r] - ms);
+    lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     const s16x4_t pb = __builtin_bit_cast(
         s16x4_t, make_uint2(pack2<KV>(pr[0], pr[1]), pack2<KV>(pr[2], pr[3])));
 
@@ -783,18 +809,22 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
     BlockIds<NW> ids;
     ids.init(p.block_tables + static_cast<size_t>(s) * p.max_blocks + ww.b0, n, lane);
 
-    // Q^T operand: head hl (zeros for the padding heads), dims 32c + 8*kg .. +8.
-    // Padding lanes read head G-1 (always inside q) and discard it.
-    uint4 qop[NK];
+    // Q^T operand in the wave's LDS: head hl (zeros for the padding heads),
+    // dims 32c + 8*kg .. +8. Padding lanes read head G-1 (always inside q) and
+    // discard it.
+    __shared__ __attribute__((aligned(16))) uint8_t q_all[NW][NK * 1024];
+    const QLds<D> qr{q_all[w]};
     {
         const int hq = g * G + min(hl, G - 1);
         const uint16_t* qrow =
             static_cast<const uint16_t*>(p.q) + (static_cast<size_t>(s) * p.num_q_heads + hq) * D;
+        uint4 qv[NK];
 #pragma unroll
-        for (int c = 0; c < NK; ++c) {
-            const uint4 x = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * kg);
-            qop[c] = hl < G ? x : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int c = 0; c < NK; ++c) qv[c] = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * kg);
+#pragma unroll
+        for (int c = 0; c < NK; ++c)
+            *reinterpret_cast<uint4*>(q_all[w] + c * 1024 + lane * 16) =
+                hl < G ? qv[c] : make_uint4(0u, 0u, 0u, 0u);
     }
     const float sscale = p.scale_log2;
     f32x4_t o[ND];
@@ -828,9 +858,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
 #pragma unroll
         for (int x = 0; x < NBUF; ++x) {
             if (nv[x] == 16)
-                mfma_consume<KV, D, false>(t[x], 16, qop, o, m, lsum, sscale, stage, lane);
+                mfma_consume<KV, D, false>(t[x], 16, qr, o, m, lsum, sscale, stage, lane);
             else
-                mfma_consume<KV, D, true>(t[x], nv[x], qop, o, m, lsum, sscale, stage, lane);
+                mfma_consume<KV, D, true>(t[x], nv[x], qr, o, m, lsum, sscale, stage, lane);
             issue(t[x], nv[x], k0 + x + NBUF);
         }
     }
@@ -912,10 +942,11 @@ __device__ __forceinline__ int wave_of(int64_t t, int64_t total, int W) {
     return static_cast<int>(((t + 1) * W - 1) / total);
 }
 
+// Sum over the wave, as a wave-uniform value.
 __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
+    return __builtin_amdgcn_readfirstlane(x);
 }
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
@@ -1025,6 +1056,7 @@ struct ValuMath {
                                (static_cast<size_t>(s) * p.num_q_heads + g) * D;
         load_q<KV, KV, D>(q, qrow, lane % kLpt);
     }
+    __device__ static void fetch_q_lds(const DecodeParams&, State&, int, int, int) {}
     __device__ static void issue(TileT& t, const TileRef& r, int lane) {
 #pragma unroll
         for (int i = 0; i < kNld; ++i) t.k[i] = rsrc_load16(r.k, lane * 16 + i * 1024);
@@ -1097,28 +1129,34 @@ template <int KV, int D, int G>
 struct MfmaMath {
     using Gm = MfmaGeo<D>;
     static constexpr int kG = G;
-    static constexpr bool kPrefetchQ = false;  // 16 registers per q: fetched at segment start
+    static constexpr bool kPrefetchQ = false;  // fetched into LDS at segment start
     static constexpr int kNk = Gm::kNk, kNv = Gm::kNv, kNd = Gm::kNd, kTB = Gm::kTileBytes;
+    static constexpr int kQBytes = kNk * 1024;  // Q^T operand of one wave in LDS
     using TileT = MfmaTile<D>;
-    struct QT {
-        uint4 op[Gm::kNk];
+    struct QT {  // the operand lives in LDS (QLds); nothing rides in the ring
     };
     struct State {
         f32x4_t o[Gm::kNd];
         float m, lsum;
         uint8_t* stage;
+        uint8_t* qlds;
     };
 
-    __device__ static void fetch_q(const DecodeParams& p, QT& q, int s, int g, int lane) {
+    __device__ static void fetch_q(const DecodeParams&, QT&, int, int, int) {}
+    // Q^T operand of (s, g) into the wave's LDS: head hl (zeros for the
+    // padding heads; they read head G-1, always inside q), dims 32c + 8*kg.
+    __device__ static void fetch_q_lds(const DecodeParams& p, State& x, int s, int g, int lane) {
         const int hl = lane & 15, kg = lane >> 4;
-        const int hq = g * G + min(hl, G - 1);  // padding lanes read head G-1 and discard it
+        const int hq = g * G + min(hl, G - 1);
         const uint16_t* qrow =
             static_cast<const uint16_t*>(p.q) + (static_cast<size_t>(s) * p.num_q_heads + hq) * D;
+        uint4 v[kNk];
 #pragma unroll
-        for (int c = 0; c < kNk; ++c) {
-            const uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * kg);
-            q.op[c] = hl < G ? v : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int c = 0; c < kNk; ++c) v[c] = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * kg);
+#pragma unroll
+        for (int c = 0; c < kNk; ++c)
+            *reinterpret_cast<uint4*>(x.qlds + c * 1024 + lane * 16) =
+                hl < G ? v[c] : make_uint4(0u, 0u, 0u, 0u);
     }
     __device__ static void issue(TileT& t, const TileRef& r, int lane) {
         const int koff = (lane & 15) * Gm::kRowBytes + 16 * (lane >> 4);
@@ -1134,9 +1172,10 @@ struct MfmaMath {
         x.lsum = 0.0f;
     }
     template <bool kPartial>
-    __device__ static void consume(State& x, const TileT& t, int nvalid, const QT& q, float sscale,
+    __device__ static void consume(State& x, const TileT& t, int nvalid, const QT&, float sscale,
                                    int lane) {
-        mfma_consume<KV, D, kPartial>(t, nvalid, q.op, x.o, x.m, x.lsum, sscale, x.stage, lane);
+        mfma_consume<KV, D, kPartial>(t, nvalid, QLds<D>{x.qlds}, x.o, x.m, x.lsum, sscale, x.stage,
+                                      lane);
     }
     __device__ static void finish(State& x) {
         x.lsum += __shfl_xor(x.lsum, 16);
@@ -1227,8 +1266,12 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
     walk_enter_row(p, tw, lane);
 
     __shared__ __attribute__((aligned(16))) uint8_t stage_all[4][MfmaGeo<D>::kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t q_all[4][G > 1 ? MfmaGeo<D>::kNk * 1024 : 16];
     typename M::State st;
-    if constexpr (G > 1) st.stage = stage_all[wv_in];
+    if constexpr (G > 1) {
+        st.stage = stage_all[wv_in];
+        st.qlds = q_all[wv_in];
+    }
     M::reset(st);
     typename M::QT q;
     typename M::QT qring[M::kPrefetchQ ? NBUF : 1];
@@ -1276,7 +1319,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
                 if constexpr (M::kPrefetchQ)
                     q = qring[x];
                 else
-                    M::fetch_q(p, q, cur.s, cur.g, lane);
+                    M::fetch_q_lds(p, st, cur.s, cur.g, lane);
             }
             if (cur.nvalid == 16)
                 M::template consume<false>(st, tr[x], 16, q, p.scale_log2, lane);
@@ -1372,8 +1415,8 @@ template <int KV, int QD, int D, int G, int NW>
 hipError_t launch(const DecodeParams& prm, dim3 grid, hipStream_t stream) {
     if constexpr (KV != PKV_FP8_E4M3 && G >= 2) {
         // Grouped heads on a 16-bit cache: matrix cores (q dtype = cache dtype).
-        // Ring of 3 tiles at D = 128 keeps two waves per SIMD (4 at D = 64: three).
-        hipLaunchKernelGGL((decode_mfma_kernel<KV, D, G, NW, (D == 128 ? 3 : 4)>), grid,
+        // Ring of 2 tiles at D = 128 keeps two waves per SIMD (4 at D = 64: three).
+        hipLaunchKernelGGL((decode_mfma_kernel<KV, D, G, NW, (D == 128 ? 2 : 4)>), grid,
                            dim3(NW * 64), 0, stream, prm);
     } else {
         hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, ring_depth<KV, D, G>()>), grid,
@@ -1457,10 +1500,10 @@ hipError_t launch_balanced(DecodeParams prm, int cus, hipStream_t st) {
 }
 
 // Ring depths keep two waves per SIMD (MFMA at D = 128 holds its O^T
-// accumulators and the V staging beside the ring: two tiles).
+// accumulators beside the ring, with Q^T in LDS: three tiles).
 template <int KV, int D>
 hipError_t balanced_by_group(int G, const DecodeParams& prm, int cus, hipStream_t st) {
-    constexpr int R = (D == 128) ? 2 : 4;
+    constexpr int R = (D == 128) ? 3 : 4;
     switch (G) {
         case 1: return launch_balanced<ValuMath<KV, D>, KV, D, 4>(prm, cus, st);
         case 2: return launch_balanced<MfmaMath<KV, D, 2>, KV, D, R>(prm, cus, st);
