@@ -26,6 +26,7 @@ from oracle import pool as opool
 
 BS = 16
 POISON = 0xFF  # fp16 / bf16 0xFFFF and e4m3 0xFF are NaN
+TORCH_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
 
 
 from bench import BS as _BS, OracleBookkeeping, Workload, blocks_needed, share_spec  # noqa: E402,F401

@@ -35,6 +35,7 @@ def check_bookkeeping(side, o):
 
 
 def check_layers(cfg, side, o, seqs, layers, whole_pool):
+    """Pool bytes after the appends and decode outputs against the oracle."""
     stats = []
     for layer in layers:
         p6 = H.expected_layer_pool(cfg, side, o, layer, seqs)
@@ -68,11 +69,13 @@ def test_parity_small(name):
     check_layers(cfg, side, o, list(range(cfg.batch)), range(cfg.layers), whole_pool=True)
 
 
-@pytest.mark.parametrize("name,max_seqs", [("tiny", None), ("llama13b_layer", 8),
-                                           ("gqa_prefix", 8), ("longctx_fp8", 2)])
-def test_parity_full_size(name, max_seqs):
-    """The workloads at their full sizes, in the launch configuration the
-    benchmark uses; append and output checked on sampled sequences."""
+@pytest.mark.parametrize("name,max_seqs,layers", [
+    ("tiny", None, None), ("llama13b_layer", 8, None), ("gqa_prefix", 8, None),
+    ("longctx_fp8", 2, None), ("7b_32layer", 2, (0, 31))])
+def test_parity_full_size(name, max_seqs, layers):
+    """The workloads at their full sizes (the 32-layer one with its 68.7 GB
+    pool), in the launch configuration the benchmark uses; append and output
+    checked on sampled sequences (and sampled layers)."""
     cfg = W.CONFIGS[name]
     say(f"parity_full {cfg.name} B={cfg.batch} ps={cfg.partition_size}")
     side = H.build_product(cfg, seed=0)
@@ -80,7 +83,7 @@ def test_parity_full_size(name, max_seqs):
     o = H.oracle_bookkeeping(cfg, 0)
     check_bookkeeping(side, o)
     seqs = H.sample_sequences(cfg, side, max_seqs)
-    check_layers(cfg, side, o, seqs, range(cfg.layers), whole_pool=(max_seqs is None))
+    check_layers(cfg, side, o, seqs, layers or range(cfg.layers), whole_pool=(max_seqs is None))
     # Untouched slots keep the poison byte: every block of the pool is in some
     # table, so look at the tails of the last blocks.
     per_layer = side.cache.nbytes // cfg.layers
@@ -162,3 +165,111 @@ def test_grouped_heads(hq, hkv, dim, dt, ps):
     o = H.oracle_bookkeeping(cfg, 4)
     check_bookkeeping(side, o)
     check_layers(cfg, side, o, list(range(cfg.batch)), [0], whole_pool=True)
+
+
+PLACEMENT_CASES = [  # (workload, partition size, balanced single pass)
+    ("llama13b_layer", 0, False), ("llama13b_layer", 0, True), ("llama13b_layer", 256, None),
+    ("gqa_prefix", 0, True), ("gqa_prefix", 512, None), ("longctx_fp8", 512, None),
+]
+
+
+@pytest.mark.parametrize("name,ps,balanced", PLACEMENT_CASES)
+def test_physical_placement_is_bitwise_invisible(name, ps, balanced):
+    """The same logical cache under two random physical placements gives the
+    same output bits: every decode form orders its arithmetic by logical
+    position only, never by block id."""
+    cfg = W.scaled(name)
+    say(f"placement {cfg.name} ps={ps} balanced={balanced}")
+    outs = []
+    for placement in (11, 12):
+        side = H.build_product(cfg, seed=6, partition_size=ps, placement_seed=placement,
+                               balanced=balanced)
+        torch.cuda.synchronize()
+        outs.append(side.outputs[0].clone())
+        tables = side.tables
+        del side
+    assert not np.array_equal(tables, H.oracle_bookkeeping(cfg, 6, placement_seed=11).tables)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+@pytest.mark.parametrize("ps,balanced", [(0, False), (0, True), (32, None), (64, None)])
+def test_table_narrower_than_context(ps, balanced):
+    """A block table of fewer columns than a context needs: the kernels read
+    the first max_blocks_per_seq blocks and attend over those tokens only;
+    with split-K, partitions past the table leave empty partials that the
+    reduce ignores."""
+    import paged_kv_cache_450_amd as P
+    from oracle import attention as oattn
+
+    cfg = W.Config("narrow_table", 1, 6, 4, 2, 64, "f16", "f16", ("uniform", 40, 300),
+                   partition_size=ps)
+    say(f"narrow table ps={ps} balanced={balanced}")
+    side = H.build_product(cfg, seed=7, balanced=balanced)
+    torch.cuda.synchronize()
+    o = H.oracle_bookkeeping(cfg, 7)
+    width = 5  # 80 tokens
+    narrow = side.batch.tables[:, :width].contiguous()
+    out = torch.full_like(side.batch.out, float("nan"))
+    b = side.batch
+    if ps > 0:
+        P.paged_attn_decode(side.cache.handle, 0, side.q[0], None, narrow, b.lens, b.scale,
+                            b.max_context_len, ps, b.workspace)
+        P.paged_attn_reduce(b.workspace, out, b.lens, b.max_context_len, ps)
+    else:
+        P.paged_attn_decode(side.cache.handle, 0, side.q[0], out, narrow, b.lens, b.scale,
+                            b.max_context_len, 0, b.workspace if b.balanced else None)
+    torch.cuda.synchronize()
+    seqs = list(range(cfg.batch))
+    p6 = H.expected_layer_pool(cfg, side, o, 0, seqs)
+    lens = np.minimum(side.lens, width * 16)
+    q = H.q_f64(side.q[0], cfg.q_dtype)
+    ref = oattn.paged_decode(p6, 0, q, o.tables, lens, float(np.float32(b.scale)), cfg.kv_dtype)
+    H.assert_close(H.out_f64(out, cfg.q_dtype), ref, cfg.kv_dtype, "narrow table")
+
+
+@pytest.mark.parametrize("dt,dim,hq,ps", [("f16", 128, 4, 512), ("bf16", 64, 8, 16),
+                                          ("f16", 128, 2, 64)])
+def test_reduce_merges_oracle_partials(dt, dim, hq, ps):
+    """paged_attn_reduce on its own: the workspace is filled (documented
+    layout) with the oracle's split-K partials of seeded K/V, unused
+    partitions poisoned with NaN; the merge must match the oracle's
+    unsplit attention."""
+    import paged_kv_cache_450_amd as P
+    from oracle import attention as oattn
+    from oracle import pool as opool
+
+    say(f"reduce-only {dt} D={dim} Hq={hq} ps={ps}")
+    rng = np.random.Generator(np.random.PCG64(W.seed_for("reduce_only", 0, dt, dim, hq, ps)))
+    B = 5
+    lens = rng.integers(1, 3 * ps + 7, size=B).astype(np.int32)
+    max_ctx = int(lens.max())
+    P_ = -(-max_ctx // ps)
+    ws_bytes = P.paged_attn_workspace_bytes(B, hq, dim, max_ctx, ps)
+    ml = np.full((B, hq, P_, 2), np.nan, dtype=np.float32)
+    o = np.full((B, hq, P_, dim), np.nan, dtype=np.float32)
+    ref = np.zeros((B, hq, dim))
+    scale = 1.0 / np.sqrt(dim)
+    for i in range(B):
+        L = int(lens[i])
+        seed = W.seed_for("reduce_only", 0, dt, dim, hq, ps, i)
+        q = opool.raw_to_f64(W.normal((hq, dim), dt, seed, "cpu").view(torch.int16).numpy()
+                             .view(np.uint16), dt)
+        k = opool.raw_to_f64(W.normal((L, 1, dim), dt, seed + 1, "cpu").view(torch.int16).numpy()
+                             .view(np.uint16), dt)
+        v = opool.raw_to_f64(W.normal((L, 1, dim), dt, seed + 2, "cpu").view(torch.int16).numpy()
+                             .view(np.uint16), dt)
+        m_, l_, o_ = oattn.partials(q, k, v, scale, ps)
+        n = m_.shape[0]
+        ml[i, :, :n, 0] = m_.T
+        ml[i, :, :n, 1] = l_.T
+        o[i, :, :n, :] = o_.transpose(1, 0, 2)
+        ref[i] = oattn.attend(q, k, v, scale)
+    off = (ml.nbytes + 255) // 256 * 256
+    host = np.zeros(ws_bytes, dtype=np.uint8)
+    host[:ml.nbytes] = ml.view(np.uint8).reshape(-1)
+    host[off:off + o.nbytes] = o.view(np.uint8).reshape(-1)
+    ws = torch.from_numpy(host).cuda()
+    out = torch.full((B, hq, dim), float("nan"), dtype=H.TORCH_DTYPES[dt], device="cuda")
+    P.paged_attn_reduce(ws, out, torch.from_numpy(lens).cuda(), max_ctx, ps)
+    torch.cuda.synchronize()
+    H.assert_close(H.out_f64(out, dt), ref, dt, "reduce-only")
