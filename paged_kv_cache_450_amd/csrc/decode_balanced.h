@@ -1,0 +1,477 @@
+// Balanced single pass: the streaming kernel over equal tile ranges and the
+// kernel that merges contexts split between waves.
+#pragma once
+
+#include "decode_core.h"
+#include "decode_mfma.h"
+#include "decode_valu.h"
+
+namespace {
+
+using namespace pkv::dev;
+
+// ---------------------------------------------------------------------------
+// Balanced single pass.
+//
+// Context lengths in a batch vary widely (16 to 8192 tokens in a log-normal
+// batch), so one workgroup per sequence, or per fixed-size partition, leaves
+// the GPU waiting on the longest items or paying a start-up per item. Here the
+// grid is exactly the waves the GPU holds at once, and the tiles of the whole
+// batch, ordered (sequence, kv head, block), are cut into R equal contiguous
+// ranges, one per wave. A wave streams its range through its tile ring
+// without a break: the ring runs across (sequence, head) boundaries. Each run
+// of tiles of one (sequence, kv head) inside a range is a segment. A segment
+// that covers its whole context writes the output directly; a context split
+// over several waves leaves one partial (o / l, m, l) per wave in the
+// workspace, and a second, small kernel on the same stream merges them with
+// the log-sum-exp rule (the kernel boundary makes the partials visible; a
+// merge inside the streaming kernel would need device-wide cache maintenance
+// per split, which costs more than the launch).
+
+// Issue-side walker over the tiles of the batch in (sequence, kv head, block)
+// order, holding the block ids of the current sequence's table row: blocks
+// 0..127 of the row stay in registers for the row's other heads, later blocks
+// rotate through a second pair of 64-id chunks.
+struct TileWalk {
+    int s, g, j, nblk;   // current tile: sequence, kv head, block
+    int L;               // tokens of sequence s as read here
+    int64_t a_sg;        // global index of tile (s, g, 0)
+    int chunk;           // sequences 64*chunk .. +63 have their lengths in lens
+    int lens;            // per lane: tokens of sequence 64*chunk + lane
+    int row0_a, row0_b;  // ids of blocks 0..63 and 64..127 of row s (per lane)
+    int ids_a, ids_b;    // ids of blocks base .. base+127 (per lane, two chunks)
+    int base;
+};
+
+__device__ __forceinline__ int walk_row_ids(const DecodeParams& p, const TileWalk& t, int j0,
+                                            int lane) {
+    const int jj = j0 + lane;
+    return jj < t.nblk ? p.block_tables[static_cast<size_t>(t.s) * p.max_blocks + jj] : -1;
+}
+
+__device__ __forceinline__ void walk_enter_row(const DecodeParams& p, TileWalk& t, int lane) {
+    t.row0_a = walk_row_ids(p, t, 0, lane);
+    t.row0_b = walk_row_ids(p, t, 64, lane);
+    t.base = t.j & ~63;
+    t.ids_a = t.base == 0 ? t.row0_a : walk_row_ids(p, t, t.base, lane);
+    t.ids_b = t.base == 0 ? t.row0_b : walk_row_ids(p, t, t.base + 64, lane);
+}
+
+// Block id of the current tile.
+__device__ __forceinline__ int walk_id(const DecodeParams& p, TileWalk& t, int lane) {
+    if (t.j >= t.base + 64) {  // blocks of a segment are walked in increasing order
+        t.base += 64;
+        t.ids_a = t.ids_b;
+        t.ids_b = walk_row_ids(p, t, t.base + 64, lane);
+    }
+    return __builtin_amdgcn_readlane(t.ids_a, t.j - t.base);
+}
+
+// Step to the next tile. Returns true when it starts a new segment.
+__device__ __forceinline__ void walk_advance(const DecodeParams& p, TileWalk& t, int lane) {
+    if (++t.j < t.nblk) return;
+    t.j = 0;
+    t.a_sg += t.nblk;
+    if (++t.g < p.num_kv_heads) {  // same row, next head: blocks 0..127 are at hand
+        t.base = 0;
+        t.ids_a = t.row0_a;
+        t.ids_b = t.row0_b;
+        return;
+    }
+    t.g = 0;
+    // Next sequence with tokens. A wave's range ends at or before the batch's
+    // last tile, so a later non-empty sequence exists; the bound only keeps s
+    // inside the batch should the lengths change under a running kernel.
+    do {
+        ++t.s;
+        if ((t.s >> 6) != t.chunk) {
+            t.chunk = t.s >> 6;
+            const int jj = t.chunk * 64 + lane;
+            t.lens = jj < p.num_seqs ? seq_tokens(p, jj) : 0;
+        }
+        t.L = __builtin_amdgcn_readlane(t.lens, t.s & 63);
+        t.nblk = (t.L + 15) >> 4;
+    } while (t.nblk == 0 && t.s + 1 < p.num_seqs);
+    walk_enter_row(p, t, lane);
+}
+
+// Ring-slot description of an issued tile (all wave-uniform).
+struct SlotInfo {
+    int nvalid;       // context tokens in the tile (0 past the end of the range)
+    int flags;        // bit 0: first tile of a segment, bit 1: last tile of a segment
+    int s, g, nblk;   // its segment's sequence, kv head and block count
+    int64_t a_sg;     // global index of tile (s, g, 0)
+};
+
+template <int D>
+struct SlotGeoB {
+    static constexpr int kStride = D + 4;  // floats per (wave, slot, head): o[D], m, l, pad
+};
+
+// Vector-ALU math for one query head per kv head (16-bit caches).
+template <int KV, int D>
+struct ValuMath {
+    using Gm = Geo<KV, D>;
+    static constexpr int kG = 1;
+    static constexpr bool kPrefetchQ = true;  // q is small: ride in the ring with its tile
+    static constexpr int kEpl = Gm::kEpl, kLpt = Gm::kLpt, kNld = Gm::kNld, kTB = Gm::kTileBytes;
+    using TileT = Tile<KV, D>;
+    using QT = QSlice<KV, D>;
+    struct State {
+        SoftmaxState<KV, D, 1> st;
+    };
+
+    __device__ static void fetch_q(const DecodeParams& p, QT& q, int s, int g, int lane) {
+        const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
+                               (static_cast<size_t>(s) * p.num_q_heads + g) * D;
+        load_q<KV, KV, D>(q, qrow, lane % kLpt);
+    }
+    __device__ static void fetch_q_lds(const DecodeParams&, State&, int, int, int) {}
+    __device__ static void issue(TileT& t, const TileRef& r, int lane) {
+#pragma unroll
+        for (int i = 0; i < kNld; ++i) t.k[i] = rsrc_load16(r.k, lane * 16 + i * 1024);
+#pragma unroll
+        for (int i = 0; i < kNld; ++i) t.v[i] = rsrc_load16(r.v, lane * 16 + i * 1024);
+    }
+    __device__ static void reset(State& x) {
+        x.st.m[0] = -INFINITY;
+        x.st.l[0] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kEpl; ++e) x.st.o[0][e] = 0.0f;
+    }
+    template <bool kPartial>
+    __device__ static void consume(State& x, const TileT& t, int nvalid, const QT& q, float sscale,
+                                   int lane) {
+        const QT qs[1] = {q};
+        consume_tile<KV, D, 1, kPartial>(x.st, t, nvalid, qs, sscale, lane / kLpt);
+    }
+    // Merge the rows of the wave; afterwards lanes of row 0 hold dims
+    // col*EPL .. +EPL, and every lane holds m and l.
+    __device__ static void finish(State& x) {
+#pragma unroll
+        for (int off = kLpt; off < 64; off <<= 1) {
+            const float m2 = __shfl_xor(x.st.m[0], off);
+            const float l2 = __shfl_xor(x.st.l[0], off);
+            const float mx = fmaxf(x.st.m[0], m2);
+            const float ms = (mx == -INFINITY) ? 0.0f : mx;
+            const float a = fast_exp2(x.st.m[0] - ms), b = fast_exp2(m2 - ms);
+            x.st.l[0] = x.st.l[0] * a + l2 * b;
+#pragma unroll
+            for (int e = 0; e < kEpl; ++e) {
+                const float o2 = __shfl_xor(x.st.o[0][e], off);
+                x.st.o[0][e] = x.st.o[0][e] * a + o2 * b;
+            }
+            x.st.m[0] = mx;
+        }
+    }
+    __device__ static void store_out(const DecodeParams& p, const State& x, int s, int g, int lane) {
+        if (lane >= kLpt) return;
+        const float inv = x.st.l[0] > 0.0f ? 1.0f / x.st.l[0] : 0.0f;
+        uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) +
+                                              (static_cast<size_t>(s) * p.num_q_heads + g) * D +
+                                              lane * kEpl);
+#pragma unroll
+        for (int e = 0; e < kEpl / 8; ++e) {
+            uint32_t wv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                wv[i] = pack2<KV>(x.st.o[0][8 * e + 2 * i] * inv, x.st.o[0][8 * e + 2 * i + 1] * inv);
+            dst[e] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+    }
+    __device__ static void store_partial(float* slot, const State& x, int lane) {
+        if (lane >= kLpt) return;
+        const float inv = x.st.l[0] > 0.0f ? 1.0f / x.st.l[0] : 0.0f;
+        float4* dst = reinterpret_cast<float4*>(slot + lane * kEpl);
+#pragma unroll
+        for (int e = 0; e < kEpl / 4; ++e)
+            dst[e] = make_float4(x.st.o[0][4 * e] * inv, x.st.o[0][4 * e + 1] * inv,
+                                 x.st.o[0][4 * e + 2] * inv, x.st.o[0][4 * e + 3] * inv);
+        if (lane == 0) {
+            slot[D] = x.st.m[0];
+            slot[D + 1] = x.st.l[0];
+        }
+    }
+};
+
+// Matrix-core math for G grouped query heads (16-bit caches).
+template <int KV, int D, int G>
+struct MfmaMath {
+    using Gm = MfmaGeo<D>;
+    static constexpr int kG = G;
+    static constexpr bool kPrefetchQ = false;  // fetched into LDS at segment start
+    static constexpr int kNk = Gm::kNk, kNv = Gm::kNv, kNd = Gm::kNd, kTB = Gm::kTileBytes;
+    static constexpr int kQBytes = kNk * 1024;  // Q^T operand of one wave in LDS
+    using TileT = MfmaTile<D>;
+    struct QT {  // the operand lives in LDS (QLds); nothing rides in the ring
+    };
+    struct State {
+        f32x4_t o[Gm::kNd];
+        float m, lsum;
+        uint8_t* stage;
+        uint8_t* qlds;
+    };
+
+    __device__ static void fetch_q(const DecodeParams&, QT&, int, int, int) {}
+    // Q^T operand of (s, g) into the wave's LDS: head hl (zeros for the
+    // padding heads; they read head G-1, always inside q), dims 32c + 8*kg.
+    __device__ static void fetch_q_lds(const DecodeParams& p, State& x, int s, int g, int lane) {
+        const int hl = lane & 15, kg = lane >> 4;
+        const int hq = g * G + min(hl, G - 1);
+        const uint16_t* qrow =
+            static_cast<const uint16_t*>(p.q) + (static_cast<size_t>(s) * p.num_q_heads + hq) * D;
+        uint4 v[kNk];
+#pragma unroll
+        for (int c = 0; c < kNk; ++c) v[c] = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * kg);
+#pragma unroll
+        for (int c = 0; c < kNk; ++c)
+            *reinterpret_cast<uint4*>(x.qlds + c * 1024 + lane * 16) =
+                hl < G ? v[c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    __device__ static void issue(TileT& t, const TileRef& r, int lane) {
+        const int koff = (lane & 15) * Gm::kRowBytes + 16 * (lane >> 4);
+#pragma unroll
+        for (int c = 0; c < kNk; ++c) t.k[c] = rsrc_load16(r.k, koff + 64 * c);
+#pragma unroll
+        for (int i = 0; i < kNv; ++i) t.v[i] = rsrc_load16(r.v, lane * 16 + 1024 * i);
+    }
+    __device__ static void reset(State& x) {
+#pragma unroll
+        for (int j = 0; j < kNd; ++j) x.o[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        x.m = -INFINITY;
+        x.lsum = 0.0f;
+    }
+    template <bool kPartial>
+    __device__ static void consume(State& x, const TileT& t, int nvalid, const QT&, float sscale,
+                                   int lane) {
+        mfma_consume<KV, D, kPartial>(t, nvalid, QLds<D>{x.qlds}, x.o, x.m, x.lsum, sscale, x.stage,
+                                      lane);
+    }
+    __device__ static void finish(State& x) {
+        x.lsum += __shfl_xor(x.lsum, 16);
+        x.lsum += __shfl_xor(x.lsum, 32);
+    }
+    __device__ static void store_out(const DecodeParams& p, const State& x, int s, int g, int lane) {
+        const int hl = lane & 15, kg = lane >> 4;
+        if (hl >= G) return;
+        const float inv = x.lsum > 0.0f ? 1.0f / x.lsum : 0.0f;
+        uint16_t* dst = static_cast<uint16_t*>(p.out) +
+                        (static_cast<size_t>(s) * p.num_q_heads + g * G + hl) * D + 4 * kg;
+#pragma unroll
+        for (int j = 0; j < kNd; ++j)
+            *reinterpret_cast<uint2*>(dst + 16 * j) =
+                make_uint2(pack2<KV>(x.o[j][0] * inv, x.o[j][1] * inv),
+                           pack2<KV>(x.o[j][2] * inv, x.o[j][3] * inv));
+    }
+    __device__ static void store_partial(float* slot, const State& x, int lane) {
+        const int hl = lane & 15, kg = lane >> 4;
+        if (hl >= G) return;
+        float* hs = slot + hl * SlotGeoB<D>::kStride;
+        const float inv = x.lsum > 0.0f ? 1.0f / x.lsum : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kNd; ++j)
+            *reinterpret_cast<float4*>(hs + 16 * j + 4 * kg) =
+                make_float4(x.o[j][0] * inv, x.o[j][1] * inv, x.o[j][2] * inv, x.o[j][3] * inv);
+        if (kg == 0) {
+            hs[D] = x.m;
+            hs[D + 1] = x.lsum;
+        }
+    }
+};
+
+template <class M, int KV, int D, int NBUF>
+__global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams p) {
+    constexpr int G = M::kG;
+    constexpr int SS = SlotGeoB<D>::kStride;
+    const int lane = threadIdx.x & 63;
+    const int wv_in = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int w = blockIdx.x * 4 + wv_in;
+    const int W = p.num_waves;
+
+    // Total tiles of the batch, then this wave's range [t0, t1).
+    int64_t total = 0;
+    for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
+        const int jj = c0 + lane;
+        total += wave_sum(jj < p.num_seqs ? (seq_tokens(p, jj) + 15) >> 4 : 0);
+    }
+    total *= p.num_kv_heads;
+    // R non-empty ranges: with fewer tiles than waves the surplus waves idle,
+    // so every wave of a split context really holds a piece of it.
+    const int R = static_cast<int>(total < W ? total : W);
+    if (w >= R) return;
+    const int64_t t0 = range_start(total, w, R);
+    const int64_t t1 = range_start(total, w + 1, R);
+    const int n = static_cast<int>(t1 - t0);
+
+    // Locate tile t0: the sequence holding it, then its head and block.
+    TileWalk tw;
+    bool found = false;
+    {
+        int64_t carry = 0;
+        for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {  // t0 < total: some chunk holds it
+            const int jj = c0 + lane;
+            const int len = jj < p.num_seqs ? seq_tokens(p, jj) : 0;
+            const int tiles = ((len + 15) >> 4) * p.num_kv_heads;
+            const int incl = wave_incl_scan(tiles, lane);
+            const uint64_t hit = __ballot(jj < p.num_seqs && carry + incl > t0);
+            if (hit) {
+                const int ln = __builtin_ffsll(static_cast<long long>(hit)) - 1;
+                tw.s = c0 + ln;
+                tw.chunk = c0 >> 6;
+                tw.lens = len;
+                tw.L = __builtin_amdgcn_readlane(len, ln);
+                tw.nblk = (tw.L + 15) >> 4;
+                const int64_t a_s = carry + __builtin_amdgcn_readlane(incl - tiles, ln);
+                const int64_t off = t0 - a_s;
+                tw.g = static_cast<int>(off / tw.nblk);
+                tw.j = static_cast<int>(off % tw.nblk);
+                tw.a_sg = a_s + static_cast<int64_t>(tw.g) * tw.nblk;
+                found = true;
+                break;
+            }
+            carry += __builtin_amdgcn_readlane(incl, 63);
+        }
+    }
+    if (!found) return;  // lengths changed between the two passes
+    walk_enter_row(p, tw, lane);
+
+    __shared__ __attribute__((aligned(16))) uint8_t stage_all[4][MfmaGeo<D>::kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t q_all[4][G > 1 ? MfmaGeo<D>::kNk * 1024 : 16];
+    typename M::State st;
+    if constexpr (G > 1) {
+        st.stage = stage_all[wv_in];
+        st.qlds = q_all[wv_in];
+    }
+    M::reset(st);
+    typename M::QT q;
+    typename M::QT qring[M::kPrefetchQ ? NBUF : 1];
+
+    const size_t bstride = static_cast<size_t>(p.num_kv_heads) * M::kTB;
+    typename M::TileT tr[NBUF];
+    SlotInfo si[NBUF];
+
+    // Issue tile kn of the range into a ring slot (and the q of a segment
+    // that starts there).
+    auto issue = [&](typename M::TileT& tt, SlotInfo& info, typename M::QT& qq, int kn) {
+        if (kn >= n) {
+            info.nvalid = 0;
+            info.flags = 0;
+            const TileRef r = tile_ref(p, p.k_plane, p.v_plane, bstride, M::kTB, -1, 0, 0);
+            M::issue(tt, r, lane);
+            return;
+        }
+        if (kn > 0) walk_advance(p, tw, lane);
+        const bool first = kn == 0 || tw.j == 0;
+        const bool last = kn == n - 1 || tw.j == tw.nblk - 1;
+        info.flags = (first ? 1 : 0) | (last ? 2 : 0);
+        info.s = tw.s;
+        info.g = tw.g;
+        info.nblk = tw.nblk;
+        info.a_sg = tw.a_sg;
+        if constexpr (M::kPrefetchQ) {
+            if (first) M::fetch_q(p, qq, tw.s, tw.g, lane);
+        }
+        const uint8_t* kpl = p.k_plane + static_cast<size_t>(tw.g) * M::kTB;
+        const uint8_t* vpl = p.v_plane + static_cast<size_t>(tw.g) * M::kTB;
+        const TileRef r =
+            tile_ref(p, kpl, vpl, bstride, M::kTB, walk_id(p, tw, lane), tw.j * 16, tw.L);
+        info.nvalid = r.nvalid;
+        M::issue(tt, r, lane);
+    };
+
+#pragma unroll
+    for (int x = 0; x < NBUF; ++x) issue(tr[x], si[x], qring[M::kPrefetchQ ? x : 0], x);
+    for (int k0 = 0; k0 < n; k0 += NBUF) {
+#pragma unroll
+        for (int x = 0; x < NBUF; ++x) {
+            const SlotInfo cur = si[x];
+            if (cur.flags & 1) {
+                if constexpr (M::kPrefetchQ)
+                    q = qring[x];
+                else
+                    M::fetch_q_lds(p, st, cur.s, cur.g, lane);
+            }
+            if (cur.nvalid == 16)
+                M::template consume<false>(st, tr[x], 16, q, p.scale_log2, lane);
+            else if (cur.nvalid > 0)
+                M::template consume<true>(st, tr[x], cur.nvalid, q, p.scale_log2, lane);
+            if (cur.flags & 2) {
+                // End of a segment: write the output, or the partial of a split context.
+                M::finish(st);
+                if (cur.a_sg >= t0 && cur.a_sg + cur.nblk <= t1) {
+                    M::store_out(p, st, cur.s, cur.g, lane);
+                } else {  // split context: slot 0 if it began before this range, else 1
+                    const int slot = (cur.a_sg <= t0) ? 0 : 1;
+                    M::store_partial(p.slots + static_cast<size_t>(w * 2 + slot) * G * SS, st, lane);
+                }
+                M::reset(st);
+            }
+            issue(tr[x], si[x], qring[M::kPrefetchQ ? x : 0], k0 + x + NBUF);
+        }
+    }
+}
+
+// Second kernel of the balanced single pass: one workgroup per (kv head,
+// sequence). It recomputes the split of the batch into R ranges, and for a
+// context that was split merges the partials its waves left in their slots;
+// it also writes the zeros of an empty context. Contexts held by one wave
+// were written by the streaming kernel and are left alone. A thread owns 4
+// dims of one head; a long context is split over tens of waves, so both
+// passes over the partials (their maximum, then the weighted sum) keep
+// several independent loads in flight.
+template <int KV, int D, int G>
+__global__ __launch_bounds__(256) void balanced_merge_kernel(const DecodeParams p) {
+    constexpr int SS = SlotGeoB<D>::kStride;
+    const int g = blockIdx.x, s = blockIdx.y, lane = threadIdx.x & 63;
+    int64_t total = 0, before = 0;  // blocks of the batch, and of sequences < s
+    for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
+        const int jj = c0 + lane;
+        const int nb = jj < p.num_seqs ? (seq_tokens(p, jj) + 15) >> 4 : 0;
+        total += wave_sum(nb);
+        before += wave_sum(jj < s ? nb : 0);
+    }
+    const int nblk = (seq_tokens(p, s) + 15) >> 4;
+    uint16_t* out = static_cast<uint16_t*>(p.out) +
+                    (static_cast<size_t>(s) * p.num_q_heads + g * G) * D;
+    const int t = threadIdx.x;
+    if (nblk == 0) {
+        for (int idx = t; idx < G * D; idx += 256) out[idx] = 0;
+        return;
+    }
+    total *= p.num_kv_heads;
+    const int R = static_cast<int>(total < p.num_waves ? total : p.num_waves);
+    const int64_t a_sg = before * p.num_kv_heads + static_cast<int64_t>(g) * nblk;
+    const int wa = wave_of(a_sg, total, R);
+    const int wb = wave_of(a_sg + nblk - 1, total, R);
+    if (wa == wb) return;  // written whole by its wave
+    // Wave wa's piece began before its range: slot 1; waves after it: slot 0.
+    const int slot_a = (a_sg <= range_start(total, wa, R)) ? 0 : 1;
+    for (int idx = t; idx < G * D / 4; idx += 256) {
+        const int h = idx / (D / 4), d = (idx % (D / 4)) * 4;
+        const float* base = p.slots + static_cast<size_t>(h) * SS;
+        auto part = [&](int v) -> const float* {
+            const int slot = v == wa ? slot_a : 0;
+            return base + static_cast<size_t>(v * 2 + slot) * G * SS;
+        };
+        float mx = -INFINITY;
+#pragma unroll 8
+        for (int v = wa; v <= wb; ++v) mx = fmaxf(mx, part(v)[D]);
+        const float ms = (mx == -INFINITY) ? 0.0f : mx;
+        float wsum = 0.0f;
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 4
+        for (int v = wa; v <= wb; ++v) {
+            const float* hs = part(v);
+            const float4 ov = *reinterpret_cast<const float4*>(hs + d);
+            const float wv = hs[D + 1] * fast_exp2(hs[D] - ms);
+            wsum += wv;
+            acc = make_float4(fmaf(wv, ov.x, acc.x), fmaf(wv, ov.y, acc.y), fmaf(wv, ov.z, acc.z),
+                              fmaf(wv, ov.w, acc.w));
+        }
+        const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+        *reinterpret_cast<uint2*>(out + h * D + d) =
+            make_uint2(pack2<KV>(acc.x * inv, acc.y * inv), pack2<KV>(acc.z * inv, acc.w * inv));
+    }
+}
+
+}  // namespace
