@@ -88,7 +88,7 @@ class Workload:
     """One decode-step workload, product side: pool, tables, inputs, batch."""
 
     def __init__(self, cfg, seed=0, device="cuda", partition_size=None, fill_byte=None,
-                 placement_seed=None, keep_cached_inputs=True, balanced=None):
+                 placement_seed=None, keep_cached_inputs=True, balanced=None, fused=True):
         import torch
 
         import workloads as W
@@ -96,6 +96,9 @@ class Workload:
 
         self.cfg = cfg
         self.seed = seed
+        # fused: a step stores the new tokens inside the decode call
+        # (paged_attn_decode_append); else kv_cache_append, then paged_attn_decode.
+        self.fused = fused
         lens = W.context_lengths(cfg, seed)
         self.lens = lens
         self.cached = lens - 1
@@ -173,11 +176,19 @@ class Workload:
     def reduce(self, stream=None):
         self.batch.reduce(stream)
 
+    def decode_append(self, layer, stream=None):
+        self.batch.k_scale, self.batch.v_scale = self.k_scale[layer], self.v_scale[layer]
+        self.batch.decode_append(layer, self.q[layer], self.k_new[layer], self.v_new[layer],
+                                 stream)
+
     def step(self, layer=None, stream=None):
         layers = range(self.cfg.layers) if layer is None else [layer]
         for l in layers:
-            self.append(l, stream)
-            self.decode(l, stream)
+            if self.fused:
+                self.decode_append(l, stream)
+            else:
+                self.append(l, stream)
+                self.decode(l, stream)
             self.reduce(stream)
         return self.batch.out
 
@@ -327,6 +338,9 @@ def main(argv=None):
     ap.add_argument("--replicas", type=int, default=None,
                     help="independent copies rotated over (default: enough for >= 2 GB)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--unfused", action="store_true",
+                    help="run a step as kv_cache_append + paged_attn_decode instead of the "
+                         "fused paged_attn_decode_append")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -350,12 +364,13 @@ def main(argv=None):
         return 1
     cfg = W.CONFIGS[args.workload]
     torch.cuda.set_device(0)
+    fused = not args.unfused
     first = Workload(cfg, args.seed, "cuda", args.partition_size,
-                     keep_cached_inputs=False if args.no_cpu_baseline else "first")
+                     keep_cached_inputs=False if args.no_cpu_baseline else "first", fused=fused)
     pool_bytes = first.cache.nbytes
     reps = args.replicas or max(1, min(8, math.ceil(2e9 / max(pool_bytes, 1))))
     ws = [first] + [Workload(cfg, args.seed + r, "cuda", args.partition_size,
-                             keep_cached_inputs=False) for r in range(1, reps)]
+                             keep_cached_inputs=False, fused=fused) for r in range(1, reps)]
     kv_bytes = [w.kv_bytes() for w in ws]
     kv_unique = [w.kv_unique_bytes() for w in ws]
     stream = torch.cuda.current_stream()
@@ -407,7 +422,12 @@ def main(argv=None):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / (args.steps * nl) * 1e3
 
-    decode_us = per_launch_us(lambda w, l: w.decode(l, stream))
+    # The decode call as the step makes it (fused: it also stores the new
+    # tokens), and the separate append kernel for reference.
+    if fused:
+        decode_us = per_launch_us(lambda w, l: w.decode_append(l, stream))
+    else:
+        decode_us = per_launch_us(lambda w, l: w.decode(l, stream))
     append_us = per_launch_us(lambda w, l: w.append(l, stream))
     reduce_us = (per_launch_us(lambda w, l: w.reduce(stream))
                  if first.partition_size > 0 else 0.0)
@@ -438,6 +458,7 @@ def main(argv=None):
             "kv_dtype": cfg.kv_dtype, "q_dtype": cfg.q_dtype,
             "context_lens": list(cfg.lengths),
             "partition_size": first.partition_size,
+            "append": "fused into decode" if fused else "separate kernel",
             "replicas": reps, "pool_bytes_per_replica": pool_bytes,
             "kv_bytes_per_step": int(sum(kv_bytes) / reps),
             "kv_unique_bytes_per_step": int(sum(kv_unique) / reps),
@@ -446,7 +467,7 @@ def main(argv=None):
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(cfg.batch / (ms_per_step * 1e-3), 1),
         "gpu_ms_per_step": round(gpu_ms_per_step, 5),
-        "kernel_us": {"append": round(append_us, 3), "decode": round(decode_us, 3),
+        "kernel_us": {"decode": round(decode_us, 3), "append_separate": round(append_us, 3),
                       "reduce": round(reduce_us, 3)},
         "roofline": {
             "bound": "hbm",

@@ -254,6 +254,40 @@ pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, const void* q,
                              int32_t max_context_len, int32_t partition_size, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
+/* One decode step of one layer in one call: kv_cache_append of each
+ * sequence's new token, then paged_attn_decode ([P2] "PagedAttention：...":
+ * the step appends the token produced last and attends over the whole
+ * context, the new token included). On a 16-bit cache with one query head
+ * per kv head, the per-sequence and split-K forms store the new tokens from
+ * inside the decode kernel (the wave that reads a token's tile takes it from
+ * new_k / new_v and writes its slot), which saves the append launch; every
+ * other form (balanced single pass, grouped heads, FP8) runs the append as a
+ * kernel of its own first, on the same stream.
+ * new_k, new_v: device [num_seqs][num_kv_heads][head_dim] of src_dtype, which
+ *   must equal q_dtype (for a 16-bit cache, also the cache dtype); 16-byte
+ *   aligned.
+ * Sequence i's new token is its last position p = L_i - 1 (L_i =
+ *   context_lens[i]): it is stored to slot block_tables[i][p / 16] * 16 +
+ *   p % 16 exactly as kv_cache_append would store it (same bytes; E4M3
+ *   encoding for an FP8 cache), and the attention uses those bytes. No write
+ *   for a sequence with L_i <= 0, with L_i above min(max_context_len,
+ *   max_blocks_per_seq * 16) (its last position is outside the call), or
+ *   whose block id there is outside the pool.
+ * Precondition: the block holding each written slot belongs to its sequence
+ *   alone (refcount 1, as kv_seq_extend guarantees for blocks it writes into);
+ *   its other tokens are read in the same call.
+ * Every other argument, the output, the workspace and the errors are those of
+ * paged_attn_decode; additional errors: INVALID (NULL or misaligned new_k /
+ * new_v, src_dtype != q_dtype). */
+pkv_status paged_attn_decode_append(const pkv_pool* pool, int32_t layer, const void* new_k,
+                                    const void* new_v, int32_t src_dtype, const void* q,
+                                    int32_t q_dtype, void* out, const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, float scale,
+                                    const float* k_scale, const float* v_scale,
+                                    int32_t max_context_len, int32_t partition_size,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Merge the partitions a partitioned paged_attn_decode left in workspace
  * into out (device [num_seqs][num_q_heads][head_dim] of out_dtype F16 or BF16):
  *   M = max_p m_p, w_p = l_p exp(m_p - M), out = sum_p w_p o_p / sum_p w_p

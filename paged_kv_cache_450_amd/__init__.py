@@ -78,6 +78,8 @@ def _load():
         "paged_attn_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "paged_attn_decode": (i32, [vp, i32, vp, i32, vp, vp, i32, vp, i32, i32, f32, vp, vp,
                                     i32, i32, vp, sz, vp]),
+        "paged_attn_decode_append": (i32, [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, i32,
+                                           i32, f32, vp, vp, i32, i32, vp, sz, vp]),
         "paged_attn_reduce": (i32, [vp, vp, i32, vp, i32, i32, i32, i32, i32, vp]),
         "pkv_last_error": (ctypes.c_char_p, []),
     }
@@ -263,6 +265,31 @@ def paged_attn_decode(pool, layer: int, q, out, block_tables, context_lens, scal
                                  q.shape[0], q.shape[1], float(scale), _ptr(k_scale),
                                  _ptr(v_scale), max_context_len, partition_size, _ptr(workspace),
                                  ws_bytes, _stream(stream)))
+
+
+def paged_attn_decode_append(pool, layer: int, new_k, new_v, q, out, block_tables, context_lens,
+                             scale: float, max_context_len: int, partition_size: int = 0,
+                             workspace=None, k_scale=None, v_scale=None, stream=None) -> None:
+    """The fused decode step: new_k, new_v [B, Hkv, D] (q's dtype) are stored at
+    each sequence's last position, then paged_attn_decode runs over them."""
+    torch = _torch()
+    _dev(new_k, "new_k"); _dev(new_v, "new_v")
+    _dev(q, "q"); _dev(out, "out"); _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32); _dev(workspace, "workspace")
+    _dev(k_scale, "k_scale", torch.float32); _dev(v_scale, "v_scale", torch.float32)
+    if q.dim() != 3 or block_tables.dim() != 2:
+        raise ValueError("q must be [B, Hq, D] and block_tables [B, W]")
+    if new_k.shape != new_v.shape or new_k.dtype != new_v.dtype or new_k.dim() != 3 or \
+            new_k.shape[0] != q.shape[0] or new_k.shape[2] != q.shape[2]:
+        raise ValueError("new_k and new_v must be [B, Hkv, D] like q")
+    if out is not None and (out.shape != q.shape or out.dtype != q.dtype):
+        raise ValueError("out must match q")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.paged_attn_decode_append(
+        pool, layer, _ptr(new_k), _ptr(new_v), _dtype_code(new_k), _ptr(q), _dtype_code(q),
+        _ptr(out), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), q.shape[0],
+        q.shape[1], float(scale), _ptr(k_scale), _ptr(v_scale), max_context_len, partition_size,
+        _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def paged_attn_reduce(workspace, out, context_lens, max_context_len: int, partition_size: int,

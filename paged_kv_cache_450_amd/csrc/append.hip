@@ -20,9 +20,30 @@ namespace {
 
 using namespace pkv::dev;
 
+// Where token t goes: slots[t] (kv_cache_append), or, for the fused decode
+// step, the last position L - 1 of sequence t's context through its table row
+// (no slot when L is outside [1, reach] or the id is outside the pool).
+struct SlotSource {
+    const int64_t* slots;
+    const int32_t* tables;  // set: positions from the tables
+    const int32_t* lens;
+    int32_t max_blocks;
+    int32_t reach;
+};
+
+__device__ __forceinline__ int64_t token_slot(const SlotSource& src, int64_t t, int64_t num_slots) {
+    if (src.tables == nullptr) return src.slots[t];
+    const int L = src.lens[t];
+    if (L < 1 || L > src.reach) return -1;
+    const int pos = L - 1;
+    const int id = src.tables[t * src.max_blocks + pos / 16];
+    if (id < 0 || static_cast<int64_t>(id) * 16 >= num_slots) return -1;
+    return static_cast<int64_t>(id) * 16 + pos % 16;
+}
+
 template <int KV, int SRC, int D>
 __global__ __launch_bounds__(256) void append_kernel(
-    const uint4* __restrict__ k, const uint4* __restrict__ v, const int64_t* __restrict__ slots,
+    const uint4* __restrict__ k, const uint4* __restrict__ v, const SlotSource src,
     int32_t num_tokens, int32_t num_kv_heads, uint8_t* __restrict__ k_plane,
     uint8_t* __restrict__ v_plane, int64_t num_slots, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale) {
@@ -34,7 +55,7 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int chunk = static_cast<int>(gid % kChunks);
     const int64_t t = row / num_kv_heads;
     const int h = static_cast<int>(row % num_kv_heads);
-    const int64_t slot = slots[t];
+    const int64_t slot = token_slot(src, t, num_slots);
     if (slot < 0 || slot >= num_slots) return;
     const int64_t block = slot >> 4, off = slot & 15;
     const int64_t dst_row = (block * num_kv_heads + h) * 16 + off;  // in rows of D elements
@@ -45,26 +66,13 @@ __global__ __launch_bounds__(256) void append_kernel(
         reinterpret_cast<uint4*>(v_plane)[dst_row * kChunks + chunk] = vx;
     } else {
         const float ks = k_scale[h], vs = v_scale[h];
-        auto quant8 = [](const uint4& x, float s) -> uint2 {
-            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-            uint32_t out[2] = {0u, 0u};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float a = (SRC == PKV_F16) ? f16_lo(w[i]) : bf16_lo(w[i]);
-                const float b = (SRC == PKV_F16) ? f16_hi(w[i]) : bf16_hi(w[i]);
-                const uint32_t ca = f32_to_e4m3(a / s);
-                const uint32_t cb = f32_to_e4m3(b / s);
-                out[i >> 1] |= (ca | (cb << 8)) << ((i & 1) * 16);
-            }
-            return make_uint2(out[0], out[1]);
-        };
-        reinterpret_cast<uint2*>(k_plane)[dst_row * kChunks + chunk] = quant8(kx, ks);
-        reinterpret_cast<uint2*>(v_plane)[dst_row * kChunks + chunk] = quant8(vx, vs);
+        reinterpret_cast<uint2*>(k_plane)[dst_row * kChunks + chunk] = quant_e4m3x8<SRC>(kx, ks);
+        reinterpret_cast<uint2*>(v_plane)[dst_row * kChunks + chunk] = quant_e4m3x8<SRC>(vx, vs);
     }
 }
 
 template <int KV, int SRC, int D>
-hipError_t launch_append(const void* k, const void* v, const int64_t* slots, int32_t num_tokens,
+hipError_t launch_append(const void* k, const void* v, const SlotSource& slots, int32_t num_tokens,
                          int32_t num_kv_heads, uint8_t* k_plane, uint8_t* v_plane,
                          int64_t num_slots, const float* ks, const float* vs,
                          hipStream_t stream) {
@@ -79,11 +87,29 @@ hipError_t launch_append(const void* k, const void* v, const int64_t* slots, int
 }
 
 template <int KV, int SRC>
-hipError_t dispatch_dim(int D, const void* k, const void* v, const int64_t* slots, int32_t T,
+hipError_t dispatch_dim(int D, const void* k, const void* v, const SlotSource& slots, int32_t T,
                         int32_t H, uint8_t* kp, uint8_t* vp, int64_t ns, const float* ks,
                         const float* vs, hipStream_t st) {
     if (D == 64) return launch_append<KV, SRC, 64>(k, v, slots, T, H, kp, vp, ns, ks, vs, st);
     return launch_append<KV, SRC, 128>(k, v, slots, T, H, kp, vp, ns, ks, vs, st);
+}
+
+hipError_t dispatch_dtype(const pkv_pool_desc& d, uint8_t* kp, uint8_t* vp, const void* k,
+                          const void* v, int32_t src_dtype, const SlotSource& src, int32_t T,
+                          const float* ks, const float* vs, hipStream_t st) {
+    const int64_t num_slots = static_cast<int64_t>(d.num_blocks) * d.block_size;
+    const int H = d.num_kv_heads;
+    if (d.kv_dtype == PKV_F16)
+        return dispatch_dim<PKV_F16, PKV_F16>(d.head_dim, k, v, src, T, H, kp, vp, num_slots, ks,
+                                             vs, st);
+    if (d.kv_dtype == PKV_BF16)
+        return dispatch_dim<PKV_BF16, PKV_BF16>(d.head_dim, k, v, src, T, H, kp, vp, num_slots,
+                                               ks, vs, st);
+    if (src_dtype == PKV_F16)
+        return dispatch_dim<PKV_FP8_E4M3, PKV_F16>(d.head_dim, k, v, src, T, H, kp, vp, num_slots,
+                                                  ks, vs, st);
+    return dispatch_dim<PKV_FP8_E4M3, PKV_BF16>(d.head_dim, k, v, src, T, H, kp, vp, num_slots, ks,
+                                               vs, st);
 }
 
 }  // namespace
@@ -119,25 +145,21 @@ extern "C" pkv_status kv_cache_append(const pkv_pool* pool, int32_t layer, const
     uint8_t* base = static_cast<uint8_t*>(pool->base);
     uint8_t* kp = base + pkv::layer_plane_offset(d, layer, 0);
     uint8_t* vp = base + pkv::layer_plane_offset(d, layer, 1);
-    const int64_t num_slots = static_cast<int64_t>(d.num_blocks) * d.block_size;
-    hipError_t e;
-    if (d.kv_dtype == PKV_F16)
-        e = dispatch_dim<PKV_F16, PKV_F16>(d.head_dim, k, v, slot_mapping, num_tokens,
-                                           d.num_kv_heads, kp, vp, num_slots, k_scale, v_scale,
-                                           stream);
-    else if (d.kv_dtype == PKV_BF16)
-        e = dispatch_dim<PKV_BF16, PKV_BF16>(d.head_dim, k, v, slot_mapping, num_tokens,
-                                             d.num_kv_heads, kp, vp, num_slots, k_scale, v_scale,
-                                             stream);
-    else if (src_dtype == PKV_F16)
-        e = dispatch_dim<PKV_FP8_E4M3, PKV_F16>(d.head_dim, k, v, slot_mapping, num_tokens,
-                                                d.num_kv_heads, kp, vp, num_slots, k_scale,
-                                                v_scale, stream);
-    else
-        e = dispatch_dim<PKV_FP8_E4M3, PKV_BF16>(d.head_dim, k, v, slot_mapping, num_tokens,
-                                                 d.num_kv_heads, kp, vp, num_slots, k_scale,
-                                                 v_scale, stream);
+    const SlotSource src{slot_mapping, nullptr, nullptr, 0, 0};
+    const hipError_t e =
+        dispatch_dtype(d, kp, vp, k, v, src_dtype, src, num_tokens, k_scale, v_scale, stream);
     if (e != hipSuccess)
         return fail(PKV_ERR_HIP, "kv_cache_append: launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
+}
+
+hipError_t pkv::launch_append_last(const pkv_pool_desc& d, uint8_t* k_plane, uint8_t* v_plane,
+                                   const void* k, const void* v, int32_t src_dtype,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t num_seqs, int32_t reach,
+                                   const float* k_scale, const float* v_scale,
+                                   hipStream_t stream) {
+    const SlotSource src{nullptr, block_tables, context_lens, max_blocks_per_seq, reach};
+    return dispatch_dtype(d, k_plane, v_plane, k, v, src_dtype, src, num_seqs, k_scale, v_scale,
+                          stream);
 }

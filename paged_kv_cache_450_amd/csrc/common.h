@@ -49,4 +49,15 @@ inline size_t ws_o_offset(size_t num_seqs, size_t num_q_heads, size_t parts) {
     return (ml + 255) & ~static_cast<size_t>(255);
 }
 
+// The fused decode step's append, as its own kernel (append.hip), for decode
+// forms that do not store the new tokens themselves: token i of k, v
+// ([num_seqs][Hkv][D] of src_dtype) goes to the last position L - 1 of
+// sequence i (context_lens[i] = L) through its table row, when 1 <= L <= reach
+// and the id there is inside the pool; the same bytes as kv_cache_append.
+hipError_t launch_append_last(const pkv_pool_desc& d, uint8_t* k_plane, uint8_t* v_plane,
+                              const void* k, const void* v, int32_t src_dtype,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t reach,
+                              const float* k_scale, const float* v_scale, hipStream_t stream);
+
 }  // namespace pkv

@@ -67,11 +67,38 @@ hipError_t launch(const DecodeParams& prm, dim3 grid, hipStream_t stream) {
         // Ring of 2 tiles at D = 128 keeps two waves per SIMD (4 at D = 64: three).
         hipLaunchKernelGGL((decode_mfma_kernel<KV, D, G, NW, (D == 128 ? 2 : 4)>), grid,
                            dim3(NW * 64), 0, stream, prm);
+    } else if constexpr (KV != PKV_FP8_E4M3 && G == 1) {
+        if (prm.new_k != nullptr)  // the new tokens stored from inside the kernel
+            hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, ring_depth<KV, D, G>(), true>),
+                               grid, dim3(NW * 64), 0, stream, prm);
+        else
+            hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, ring_depth<KV, D, G>()>), grid,
+                               dim3(NW * 64), 0, stream, prm);
     } else {
         hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, ring_depth<KV, D, G>()>), grid,
                            dim3(NW * 64), 0, stream, prm);
     }
     return hipGetLastError();
+}
+
+// The fused step's append as a kernel of its own (ahead of the decode, same
+// stream), for the forms that do not store the new tokens themselves.
+pkv_status append_first(const char* fn, const pkv_pool* pool, int32_t layer, const void* new_k,
+                        const void* new_v, int32_t src_dtype, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                        int32_t max_context_len, const float* k_scale, const float* v_scale,
+                        hipStream_t stream) {
+    const pkv_pool_desc& d = pool->desc;
+    const int64_t reach =
+        std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * 16);
+    uint8_t* base = static_cast<uint8_t*>(pool->base);
+    const hipError_t e = pkv::launch_append_last(
+        d, base + pkv::layer_plane_offset(d, layer, 0), base + pkv::layer_plane_offset(d, layer, 1),
+        new_k, new_v, src_dtype, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+        static_cast<int32_t>(reach), k_scale, v_scale, stream);
+    if (e != hipSuccess)
+        return pkv::fail(PKV_ERR_HIP, "%s: append launch failed: %s", fn, hipGetErrorString(e));
+    return PKV_OK;
 }
 
 // Waves per workgroup: a partition of up to 16 blocks is one wave's stream;
@@ -187,51 +214,54 @@ extern "C" size_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
                sizeof(float);
 }
 
-extern "C" pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, const void* q,
-                                        int32_t q_dtype, void* out, const int32_t* block_tables,
-                                        int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                        int32_t num_seqs, int32_t num_q_heads, float scale,
-                                        const float* k_scale, const float* v_scale,
-                                        int32_t max_context_len, int32_t partition_size,
-                                        void* workspace, size_t workspace_bytes,
-                                        hipStream_t stream) {
+namespace {
+
+// Shared by paged_attn_decode and paged_attn_decode_append (new_k, new_v:
+// the fused append's source rows, or NULL).
+pkv_status decode_impl(const char* fn, const pkv_pool* pool, int32_t layer, const void* q,
+                       int32_t q_dtype, void* out, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t num_q_heads, float scale, const float* k_scale,
+                       const float* v_scale, int32_t max_context_len, int32_t partition_size,
+                       void* workspace, size_t workspace_bytes, const void* new_k,
+                       const void* new_v, hipStream_t stream) {
     using pkv::fail;
-    if (pool == nullptr) return fail(PKV_ERR_INVALID, "paged_attn_decode: pool is NULL");
+    if (pool == nullptr) return fail(PKV_ERR_INVALID, "%s: pool is NULL", fn);
     const pkv_pool_desc& d = pool->desc;
     if (pool->base == nullptr)
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: pool has no device memory");
+        return fail(PKV_ERR_INVALID, "%s: pool has no device memory", fn);
     if (layer < 0 || layer >= d.num_layers)
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: layer %d out of range", layer);
+        return fail(PKV_ERR_INVALID, "%s: layer %d out of range", fn, layer);
     if (!pkv::is_16bit(q_dtype))
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: q dtype must be F16 or BF16");
+        return fail(PKV_ERR_INVALID, "%s: q dtype must be F16 or BF16", fn);
     if (pkv::is_16bit(d.kv_dtype) && q_dtype != d.kv_dtype)
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: q dtype must equal the 16-bit cache dtype");
+        return fail(PKV_ERR_INVALID, "%s: q dtype must equal the 16-bit cache dtype", fn);
     if (num_seqs < 0 || num_seqs > 65535)
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: num_seqs %d outside [0, 65535]", num_seqs);
+        return fail(PKV_ERR_INVALID, "%s: num_seqs %d outside [0, 65535]", fn, num_seqs);
     if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads != 0)
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: %d query heads for %d kv heads",
+        return fail(PKV_ERR_INVALID, "%s: %d query heads for %d kv heads", fn,
                     num_q_heads, d.num_kv_heads);
     const int G = num_q_heads / d.num_kv_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8)
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: group size %d not in {1,2,4,8}", G);
+        return fail(PKV_ERR_INVALID, "%s: group size %d not in {1,2,4,8}", fn, G);
     if (max_blocks_per_seq < 0 || max_context_len < 0)
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: negative table width or context");
+        return fail(PKV_ERR_INVALID, "%s: negative table width or context", fn);
     if (partition_size < 0 || partition_size % 16 != 0)
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: partition_size %d not a multiple of 16",
+        return fail(PKV_ERR_INVALID, "%s: partition_size %d not a multiple of 16", fn,
                     partition_size);
     if (!std::isfinite(scale))
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: scale is not finite");
+        return fail(PKV_ERR_INVALID, "%s: scale is not finite", fn);
     if (max_blocks_per_seq > (1 << 26))
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: max_blocks_per_seq too large");
+        return fail(PKV_ERR_INVALID, "%s: max_blocks_per_seq too large", fn);
     if (num_seqs == 0) return PKV_OK;
     if (d.num_blocks == 0)
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: the pool has no blocks");
+        return fail(PKV_ERR_INVALID, "%s: the pool has no blocks", fn);
     if (q == nullptr || block_tables == nullptr || context_lens == nullptr)
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: NULL q, block_tables or context_lens");
+        return fail(PKV_ERR_INVALID, "%s: NULL q, block_tables or context_lens", fn);
     if (reinterpret_cast<uintptr_t>(q) % 16 != 0)
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: q must be 16-byte aligned");
+        return fail(PKV_ERR_INVALID, "%s: q must be 16-byte aligned", fn);
     if (d.kv_dtype == PKV_FP8_E4M3 && (k_scale == nullptr || v_scale == nullptr))
-        return fail(PKV_ERR_INVALID, "paged_attn_decode: an FP8 cache needs k_scale and v_scale");
+        return fail(PKV_ERR_INVALID, "%s: an FP8 cache needs k_scale and v_scale", fn);
 
     DecodeParams prm{};
     const uint8_t* base = static_cast<const uint8_t*>(pool->base);
@@ -249,20 +279,22 @@ extern "C" pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, con
     prm.num_q_heads = num_q_heads;
     prm.max_ctx = max_context_len;
     prm.scale_log2 = scale * pkv::dev::kLog2e;
+    prm.new_k = static_cast<const uint8_t*>(new_k);
+    prm.new_v = static_cast<const uint8_t*>(new_v);
 
     uint32_t parts = 1;
     if (partition_size > 0) {
         const size_t need = paged_attn_workspace_bytes(num_seqs, num_q_heads, d.head_dim,
                                                        max_context_len, partition_size);
         if (workspace == nullptr || workspace_bytes < need)
-            return fail(PKV_ERR_INVALID, "paged_attn_decode: workspace of %zu bytes, %zu needed",
+            return fail(PKV_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn,
                         workspace_bytes, need);
         if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
-            return fail(PKV_ERR_INVALID, "paged_attn_decode: workspace must be 16-byte aligned");
+            return fail(PKV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
         const int64_t P = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
         if (P == 0) return PKV_OK;  // no tokens anywhere; the reduce writes zeros
         if (P > 65535)
-            return fail(PKV_ERR_INVALID, "paged_attn_decode: %lld partitions (at most 65535)",
+            return fail(PKV_ERR_INVALID, "%s: %lld partitions (at most 65535)", fn,
                         static_cast<long long>(P));
         parts = static_cast<uint32_t>(P);
         prm.blocks_per_part = partition_size / 16;
@@ -271,9 +303,9 @@ extern "C" pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, con
         prm.ws_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
                                             pkv::ws_o_offset(num_seqs, num_q_heads, P));
     } else {
-        if (out == nullptr) return fail(PKV_ERR_INVALID, "paged_attn_decode: out is NULL");
+        if (out == nullptr) return fail(PKV_ERR_INVALID, "%s: out is NULL", fn);
         if (reinterpret_cast<uintptr_t>(out) % 16 != 0)
-            return fail(PKV_ERR_INVALID, "paged_attn_decode: out must be 16-byte aligned");
+            return fail(PKV_ERR_INVALID, "%s: out must be 16-byte aligned", fn);
         prm.blocks_per_part = 0;
         prm.num_parts = 1;
         if (workspace != nullptr && pkv::is_16bit(d.kv_dtype) && num_seqs <= kBalancedMaxSeqs) {
@@ -282,17 +314,24 @@ extern "C" pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, con
             const int waves = cus * kBalancedWavesPerCu;
             const size_t need = balanced_bytes(G, d.head_dim, waves);
             if (workspace_bytes < need)
-                return fail(PKV_ERR_INVALID, "paged_attn_decode: workspace of %zu bytes, %zu needed",
+                return fail(PKV_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn,
                             workspace_bytes, need);
             if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-                return fail(PKV_ERR_INVALID, "paged_attn_decode: workspace must be 256-byte aligned");
+                return fail(PKV_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
             prm.slots = static_cast<float*>(workspace);
             prm.num_seqs = num_seqs;
+            if (new_k != nullptr) {
+                const pkv_status sa = append_first(
+                    fn, pool, layer, new_k, new_v, q_dtype, block_tables, max_blocks_per_seq,
+                    context_lens, num_seqs, max_context_len, k_scale, v_scale, stream);
+                if (sa != PKV_OK) return sa;
+                prm.new_k = prm.new_v = nullptr;
+            }
             const hipError_t eb = (d.kv_dtype == PKV_F16)
                                       ? balanced_by_dim<PKV_F16>(d.head_dim, G, prm, cus, stream)
                                       : balanced_by_dim<PKV_BF16>(d.head_dim, G, prm, cus, stream);
             if (eb != hipSuccess)
-                return fail(PKV_ERR_HIP, "paged_attn_decode: launch failed: %s", hipGetErrorString(eb));
+                return fail(PKV_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(eb));
             return PKV_OK;
         }
         // The ordering keys hold the block count in 23 bits.
@@ -301,6 +340,17 @@ extern "C" pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, con
         prm.longest_first = (num_seqs <= 256 && (max_tokens + 15) / 16 < (1 << 23)) ? 1 : 0;
     }
 
+    // The fused step's new tokens: stored from inside the vector-ALU kernel
+    // on 16-bit caches with one query head per kv head; elsewhere (FP8, the
+    // matrix-core kernel), that code would cost the kernel more than the
+    // separate append launch does.
+    if (new_k != nullptr && !(pkv::is_16bit(d.kv_dtype) && G == 1)) {
+        const pkv_status sa = append_first(fn, pool, layer, new_k, new_v, q_dtype, block_tables,
+                                           max_blocks_per_seq, context_lens, num_seqs,
+                                           max_context_len, k_scale, v_scale, stream);
+        if (sa != PKV_OK) return sa;
+        prm.new_k = prm.new_v = nullptr;
+    }
     const dim3 grid(static_cast<uint32_t>(d.num_kv_heads), static_cast<uint32_t>(num_seqs), parts);
     hipError_t e;
     if (d.kv_dtype == PKV_F16)
@@ -312,6 +362,43 @@ extern "C" pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, con
     else
         e = by_dim<PKV_FP8_E4M3, PKV_BF16>(d.head_dim, G, prm, grid, stream);
     if (e != hipSuccess)
-        return fail(PKV_ERR_HIP, "paged_attn_decode: launch failed: %s", hipGetErrorString(e));
+        return fail(PKV_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, const void* q,
+                                        int32_t q_dtype, void* out, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                        int32_t num_seqs, int32_t num_q_heads, float scale,
+                                        const float* k_scale, const float* v_scale,
+                                        int32_t max_context_len, int32_t partition_size,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+    return decode_impl("paged_attn_decode", pool, layer, q, q_dtype, out, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale, k_scale,
+                       v_scale, max_context_len, partition_size, workspace, workspace_bytes,
+                       nullptr, nullptr, stream);
+}
+
+extern "C" pkv_status paged_attn_decode_append(
+    const pkv_pool* pool, int32_t layer, const void* new_k, const void* new_v, int32_t src_dtype,
+    const void* q, int32_t q_dtype, void* out, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, float scale, const float* k_scale, const float* v_scale,
+    int32_t max_context_len, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+    using pkv::fail;
+    const char* fn = "paged_attn_decode_append";
+    if (src_dtype != q_dtype)
+        return fail(PKV_ERR_INVALID, "%s: the new tokens' dtype must equal the q dtype", fn);
+    if (num_seqs > 0 && (new_k == nullptr || new_v == nullptr))
+        return fail(PKV_ERR_INVALID, "%s: NULL new_k or new_v", fn);
+    if ((reinterpret_cast<uintptr_t>(new_k) | reinterpret_cast<uintptr_t>(new_v)) % 16 != 0)
+        return fail(PKV_ERR_INVALID, "%s: new_k and new_v must be 16-byte aligned", fn);
+    return decode_impl(fn, pool, layer, q, q_dtype, out, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, k_scale, v_scale,
+                       max_context_len, partition_size, workspace, workspace_bytes, new_k, new_v,
+                       stream);
 }

@@ -40,6 +40,10 @@ struct DecodeParams {
     float* slots;             // [waves][2][G][D + 4] partials of split contexts
     int32_t num_waves;        // waves of the balanced launch
     int32_t num_seqs;
+    // Fused append (NULL: none): the new token of every sequence, K and V rows
+    // [B][Hkv][D] of the 16-bit source dtype (the q dtype).
+    const uint8_t* new_k;
+    const uint8_t* new_v;
 };
 
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
@@ -155,9 +159,11 @@ __device__ __forceinline__ void combine_waves(const DecodeParams& p, int s, int 
 
 // The work of one wave: sequence s, its length L as this kernel reads it, and
 // its tiles, the logical blocks b0 + w + k*NW for k < n (the partition's
-// blocks dealt round robin to the NW waves of the workgroup).
+// blocks dealt round robin to the NW waves of the workgroup). newk: the index
+// of the tile holding the token a fused append writes (position L - 1), when
+// this wave reads it; else -1.
 struct WaveWork {
-    int s, L, b0, n;
+    int s, L, b0, n, newk;
 };
 
 // Grid (kv head, sequence, partition), kv head fastest. Workgroups are dealt
@@ -166,7 +172,7 @@ struct WaveWork {
 // partitions do not (short sequences have no late partitions).
 // Returns false when the workgroup has no tokens; every wave of the
 // workgroup takes the same branch.
-template <int G, int D, int NW>
+template <int G, int D, int NW, bool kFused = false>
 __device__ __forceinline__ bool locate_work(const DecodeParams& p, int g, int part, int w,
                                             WaveWork& ww) {
     // Lr: the context as the reduce sees it (clamped to max_ctx); L: the
@@ -206,6 +212,13 @@ __device__ __forceinline__ bool locate_work(const DecodeParams& p, int g, int pa
     ww.L = L;
     ww.b0 = b0 + w;
     ww.n = span > w ? (span - w + NW - 1) / NW : 0;
+    // The fused append writes position L - 1 only when the context is whole
+    // here (not clamped): otherwise its last token lies outside this call.
+    ww.newk = -1;
+    if constexpr (kFused) {
+        if (ww.n > 0 && ww.b0 + (ww.n - 1) * NW == nblk - 1 && p.context_lens[s] == L)
+            ww.newk = ww.n - 1;
+    }
     return true;
 }
 
@@ -272,9 +285,13 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
     }
 }
 
-// Tokens of sequence j as this kernel reads them (clamped like the other paths).
+// Tokens of a context of raw length `raw` as this kernel reads it (clamped
+// like the other paths).
+__device__ __forceinline__ int clamp_tokens(const DecodeParams& p, int raw) {
+    return min(max(raw, 0), min(p.max_ctx, p.max_blocks * 16));
+}
 __device__ __forceinline__ int seq_tokens(const DecodeParams& p, int j) {
-    return min(max(p.context_lens[j], 0), min(p.max_ctx, p.max_blocks * 16));
+    return clamp_tokens(p, p.context_lens[j]);
 }
 
 __device__ __forceinline__ int64_t range_start(int64_t total, int w, int W) {
@@ -291,6 +308,67 @@ __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
     return __builtin_amdgcn_readfirstlane(x);
+}
+
+// ---------------------------------------------------------------------------
+// Fused append (16-bit caches, vector-ALU decode). The new token of a sequence
+// is the last position L - 1 of its context; the one wave that reads the tile
+// holding it takes the token's K and V from the source rows instead of the
+// pool (the pool bytes it loaded for that row are discarded), and writes them
+// to the token's slot. No other wave reads that slot: it lies in the
+// sequence's own last block, which is never shared while tokens are written
+// into it.
+//
+// The wave fetches the source rows before its tile ring fills (one 16-byte
+// chunk per lane: lanes 0..15 K, lanes 16..31 V, chunk = lane mod the row's
+// chunk count) and parks them in 512 bytes of its LDS once they land, so no
+// register is held across the ring for them.
+template <int D>
+struct NewSrc {
+    static constexpr int kChunks = D * 2 / 16;  // 16-byte chunks of a 16-bit row
+    uint4 x;
+
+    __device__ __forceinline__ void fetch(const DecodeParams& p, int s, int g, int lane) {
+        const uint8_t* row = ((lane & 16) ? p.new_v : p.new_k) +
+                             (static_cast<size_t>(s) * p.num_kv_heads + g) * (D * 2);
+        x = *reinterpret_cast<const uint4*>(row + (lane & (kChunks - 1)) * 16);
+    }
+    // Copy the rows to 512 bytes of LDS: K chunk c at 16c, V chunk c at 256 + 16c.
+    __device__ __forceinline__ void stash(uint8_t* lds, int lane) const {
+        if (lane < 32)
+            *reinterpret_cast<uint4*>(lds + (lane & 16) * 16 + (lane & (kChunks - 1)) * 16) = x;
+    }
+};
+
+// Source chunk c of the new token's K (kv = 0) or V (kv = 1) row, from LDS.
+__device__ __forceinline__ uint4 new_chunk(const uint8_t* lds, int kv, int c) {
+    return *reinterpret_cast<const uint4*>(lds + kv * 256 + c * 16);
+}
+
+// Replace the new token's row in the loads of a tile read in natural layout
+// (lane l of load i holds bytes (l % LPR) * 16 of token i * (64 / LPR) +
+// l / LPR). val holds, on every lane, the bytes for its column.
+template <int LPR, int N>
+__device__ __forceinline__ void patch_natural(uint4 (&r)[N], const uint4& val, int off, int lane) {
+    constexpr int kTpi = 64 / LPR;
+    const bool row = lane / LPR == off % kTpi;
+    const int i0 = off / kTpi;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        if (i == i0 && row) r[i] = val;
+}
+
+// Write the new token's cache row (LPR lanes of 16 bytes: lane c stores
+// column c of kval and vval) to offset off of block id, kv head g.
+template <int LPR>
+__device__ __forceinline__ void store_new_row(const DecodeParams& p, int g, int id, int off,
+                                              int tile_bytes, const uint4& kval,
+                                              const uint4& vval, int lane) {
+    if (lane >= LPR) return;
+    const size_t at = (static_cast<size_t>(id) * p.num_kv_heads + g) * tile_bytes +
+                      static_cast<size_t>(off) * (LPR * 16) + lane * 16;
+    *reinterpret_cast<uint4*>(const_cast<uint8_t*>(p.k_plane) + at) = kval;
+    *reinterpret_cast<uint4*>(const_cast<uint8_t*>(p.v_plane) + at) = vval;
 }
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {

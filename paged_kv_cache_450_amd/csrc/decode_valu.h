@@ -222,8 +222,11 @@ __device__ __forceinline__ void store_result(const DecodeParams& p, int s, int q
 // refilled with the tile NBUF positions ahead, so every wave keeps NBUF tiles
 // of loads in flight from its first tile to its last. Used for FP8 caches and
 // for one query head per kv head.
-template <int KV, int QD, int D, int G, int NW, int NBUF>
+// kFused (16-bit caches): the call also stores each sequence's new token
+// (see NewSrc).
+template <int KV, int QD, int D, int G, int NW, int NBUF, bool kFused = false>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
+    static_assert(!kFused || KV != PKV_FP8_E4M3, "fused append: 16-bit caches");
     using Gm = Geo<KV, D>;
     constexpr int EPL = Gm::kEpl, LPT = Gm::kLpt, NLD = Gm::kNld, TB = Gm::kTileBytes;
 
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
     const int col = lane % LPT;
 
     WaveWork ww;
-    if (!locate_work<G, D, NW>(p, g, part, w, ww)) return;
+    if (!locate_work<G, D, NW, kFused>(p, g, part, w, ww)) return;
     const int s = ww.s, L = ww.L, n = ww.n;
     BlockIds<NW> ids;
     ids.init(p.block_tables + static_cast<size_t>(s) * p.max_blocks + ww.b0, n, lane);
@@ -267,10 +270,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
 
     Tile<KV, D> t[NBUF];
     int nv[NBUF];
+    // Fused append: the wave that reads the new token's tile fetches its
+    // source rows first and parks them in LDS once they land (by then the
+    // ring's first tiles are in flight behind them).
+    __shared__ __attribute__((aligned(16))) uint8_t new_rows[kFused ? NW : 1][kFused ? 512 : 16];
+    NewSrc<D> ns;
+    if (kFused && ww.newk >= 0) ns.fetch(p, s, g, lane);
+    int new_id = -1;
     // Issue the loads of tile kn into a ring slot.
     auto issue = [&](Tile<KV, D>& tt, int& nvalid, int kn) {
-        const TileRef r = tile_ref(p, kpl, vpl, bstride, TB, ids.next(kn), (ww.b0 + kn * NW) * 16, L);
+        const int id = ids.next(kn);
+        const TileRef r = tile_ref(p, kpl, vpl, bstride, TB, id, (ww.b0 + kn * NW) * 16, L);
         nvalid = r.nvalid;
+        if (kFused && kn == ww.newk) new_id = id;
 #pragma unroll
         for (int i = 0; i < NLD; ++i) tt.k[i] = rsrc_load16(r.k, voff + i * 1024);
 #pragma unroll
@@ -279,9 +291,20 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
 
 #pragma unroll
     for (int x = 0; x < NBUF; ++x) issue(t[x], nv[x], x);
+    if (kFused && ww.newk >= 0) ns.stash(new_rows[w], lane);
     for (int k0 = 0; k0 < n; k0 += NBUF) {
 #pragma unroll
         for (int x = 0; x < NBUF; ++x) {
+            if (kFused && k0 + x == ww.newk && nv[x] > 0) {
+                // The new token (the last of the context): from the source
+                // rows into the tile and into its slot.
+                const int off = nv[x] - 1;
+                const uint4 kc = new_chunk(new_rows[w], 0, col);
+                const uint4 vc = new_chunk(new_rows[w], 1, col);
+                patch_natural<LPT>(t[x].k, kc, off, lane);
+                patch_natural<LPT>(t[x].v, vc, off, lane);
+                store_new_row<LPT>(p, g, new_id, off, TB, kc, vc, lane);
+            }
             if (nv[x] == 16)
                 consume_tile<KV, D, G, false>(st, t[x], 16, qs, sscale, row);
             else

@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "pagedkv.h"
+
 namespace pkv {
 namespace dev {
 
@@ -93,6 +95,24 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
         code = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));  // exact scaling, RNE
     }
     return sign | code;
+}
+
+// Eight 16-bit source elements (one 16-byte chunk, element e in bytes 2e,
+// 2e+1) to eight E4M3 codes (byte e): code = e4m3(fp32(x) / scale), the
+// quotient correctly rounded. SRC is PKV_F16 or PKV_BF16.
+template <int SRC>
+__device__ __forceinline__ uint2 quant_e4m3x8(const uint4& x, float scale) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = (SRC == PKV_F16) ? f16_lo(w[i]) : bf16_lo(w[i]);
+        const float b = (SRC == PKV_F16) ? f16_hi(w[i]) : bf16_hi(w[i]);
+        const uint32_t ca = f32_to_e4m3(a / scale);
+        const uint32_t cb = f32_to_e4m3(b / scale);
+        out[i >> 1] |= (ca | (cb << 8)) << ((i & 1) * 16);
+    }
+    return make_uint2(out[0], out[1]);
 }
 
 }  // namespace dev

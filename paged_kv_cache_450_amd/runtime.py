@@ -19,7 +19,8 @@ import torch
 from . import (BLOCK_SIZE, PKV_BF16, PKV_F16, PKV_FP8_E4M3, PoolDesc, block_alloc, block_free,
                kv_cache_append, kv_pool_bytes, kv_pool_create, kv_pool_destroy,
                kv_pool_free_list, kv_pool_num_free, kv_seq_extend, kv_seq_fork,
-               paged_attn_decode, paged_attn_reduce, paged_attn_workspace_bytes)
+               paged_attn_decode, paged_attn_decode_append, paged_attn_reduce,
+               paged_attn_workspace_bytes)
 
 DTYPE_CODES = {"f16": PKV_F16, "bf16": PKV_BF16, "e4m3": PKV_FP8_E4M3}
 
@@ -113,7 +114,8 @@ class DecodeBatch:
     """Device-side state of one batch: tables, lengths, workspace and output.
 
     run(layer, q) issues paged_attn_decode and, when partitioned, paged_attn_reduce
-    on one stream; the output is self.out. A single pass (partition_size 0) is
+    on one stream; the output is self.out. decode_append(layer, q, k, v) is the
+    fused form that also stores each sequence's new token. A single pass (partition_size 0) is
     balanced across the GPU unless balanced=False.
     """
 
@@ -150,6 +152,18 @@ class DecodeBatch:
         paged_attn_decode(self.cache.handle, layer, q, None if self.partition_size else self.out,
                           self.tables, self.lens, self.scale, self.max_context_len,
                           self.partition_size, self.workspace, self.k_scale, self.v_scale, stream)
+
+    def decode_append(self, layer: int, q, new_k, new_v, stream=None):
+        """The fused step: store each sequence's new token at its last position,
+        then decode (paged_attn_decode_append)."""
+        want = (self.num_seqs, self.cache.desc.num_kv_heads, self.head_dim)
+        if tuple(new_k.shape) != want or tuple(new_v.shape) != want:
+            raise ValueError(f"new_k and new_v must be {want}")
+        paged_attn_decode_append(self.cache.handle, layer, new_k, new_v, q,
+                                 None if self.partition_size else self.out, self.tables,
+                                 self.lens, self.scale, self.max_context_len,
+                                 self.partition_size, self.workspace, self.k_scale, self.v_scale,
+                                 stream)
 
     def reduce(self, stream=None):
         if self.partition_size > 0:

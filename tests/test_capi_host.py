@@ -29,7 +29,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     out = subprocess.run(["nm", "-D", "--defined-only", P.library_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -241,6 +241,22 @@ def test_kernel_entry_points_validate_before_touching_the_gpu():
                                       None, 64, 0, None, 0, None),                           # out NULL
         lambda: lib.paged_attn_decode(pool, 0, 16, P.PKV_F16, 16, 16, 4, 16, 1, 2,
                                       float("nan"), None, None, 64, 0, None, 0, None),       # scale
+        # fused step: its own checks, then every check of paged_attn_decode
+        lambda: lib.paged_attn_decode_append(pool, 0, 16, 16, P.PKV_BF16, 16, P.PKV_F16, 16, 16,
+                                             4, 16, 1, 2, 1.0, None, None, 64, 0, None, 0,
+                                             None),                                  # src dtype
+        lambda: lib.paged_attn_decode_append(pool, 0, None, 16, P.PKV_F16, 16, P.PKV_F16, 16,
+                                             16, 4, 16, 1, 2, 1.0, None, None, 64, 0, None, 0,
+                                             None),                                  # new_k NULL
+        lambda: lib.paged_attn_decode_append(pool, 0, 16, 8, P.PKV_F16, 16, P.PKV_F16, 16, 16,
+                                             4, 16, 1, 2, 1.0, None, None, 64, 0, None, 0,
+                                             None),                                  # align
+        lambda: lib.paged_attn_decode_append(pool, 0, 16, 16, P.PKV_F16, 16, P.PKV_F16, 16, 16,
+                                             4, 16, 1, 3, 1.0, None, None, 64, 0, None, 0,
+                                             None),                                  # heads
+        lambda: lib.paged_attn_decode_append(pool, 2, 16, 16, P.PKV_F16, 16, P.PKV_F16, 16, 16,
+                                             4, 16, 1, 2, 1.0, None, None, 64, 0, None, 0,
+                                             None),                                  # layer
         lambda: lib.paged_attn_reduce(16, 16, P.PKV_F16, 16, 1, 2, 96, 64, 32, None),        # dim
         lambda: lib.paged_attn_reduce(16, 16, P.PKV_F16, 16, 1, 2, 64, 64, 0, None),         # PS
         lambda: lib.paged_attn_reduce(16, None, P.PKV_F16, 16, 1, 2, 64, 64, 32, None),      # out
@@ -252,6 +268,9 @@ def test_kernel_entry_points_validate_before_touching_the_gpu():
     assert lib.paged_attn_decode(pool, 0, 16, P.PKV_F16, 16, 16, 4, 16, 0, 2, 1.0, None, None, 64,
                                  0, None, 0, None) == P.PKV_OK
     assert lib.kv_cache_append(pool, 0, 16, 16, P.PKV_F16, 16, 0, None, None, None) == P.PKV_OK
+    assert lib.paged_attn_decode_append(pool, 0, None, None, P.PKV_F16, 16, P.PKV_F16, 16, 16, 4,
+                                        16, 0, 2, 1.0, None, None, 64, 0, None, 0,
+                                        None) == P.PKV_OK
     P.kv_pool_destroy(pool)
 
 
@@ -261,6 +280,13 @@ def test_fp8_pool_needs_scales():
     assert P.lib.kv_cache_append(pool, 0, 16, 16, P.PKV_F16, 16, 1, None, None, None) == P.PKV_ERR_INVALID
     assert P.lib.paged_attn_decode(pool, 0, 16, P.PKV_F16, 16, 16, 4, 16, 1, 1, 1.0, None, None,
                                    64, 0, None, 0, None) == P.PKV_ERR_INVALID
+    assert P.lib.paged_attn_decode_append(pool, 0, 16, 16, P.PKV_F16, 16, P.PKV_F16, 16, 16, 4,
+                                          16, 1, 1, 1.0, None, None, 64, 0, None, 0,
+                                          None) == P.PKV_ERR_INVALID
+    # an FP8 cache takes new tokens of the q dtype only
+    assert P.lib.paged_attn_decode_append(pool, 0, 16, 16, P.PKV_BF16, 16, P.PKV_F16, 16, 16, 4,
+                                          16, 1, 1, 1.0, 16, 16, 64, 0, None, 0,
+                                          None) == P.PKV_ERR_INVALID
     P.kv_pool_destroy(pool)
 
 

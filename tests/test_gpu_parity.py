@@ -55,30 +55,33 @@ def check_layers(cfg, side, o, seqs, layers, whole_pool):
     return stats
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("name", list(W.CONFIGS))
-def test_parity_small(name):
+def test_parity_small(name, fused):
     """Scaled versions of the five workloads: whole pool bytewise after the
-    appends (stray writes included) and every output of every layer."""
+    appends (stray writes included) and every output of every layer, with the
+    step as separate append and decode calls and as the fused call."""
     cfg = W.scaled(name)
     say(f"parity_small {cfg.name} B={cfg.batch} Hq={cfg.q_heads} Hkv={cfg.kv_heads} "
-        f"D={cfg.head_dim} kv={cfg.kv_dtype} ps={cfg.partition_size}")
-    side = H.build_product(cfg, seed=0)
+        f"D={cfg.head_dim} kv={cfg.kv_dtype} ps={cfg.partition_size} fused={fused}")
+    side = H.build_product(cfg, seed=0, fused=fused)
     torch.cuda.synchronize()
     o = H.oracle_bookkeeping(cfg, 0)
     check_bookkeeping(side, o)
     check_layers(cfg, side, o, list(range(cfg.batch)), range(cfg.layers), whole_pool=True)
 
 
-@pytest.mark.parametrize("name,max_seqs,layers", [
-    ("tiny", None, None), ("llama13b_layer", 8, None), ("gqa_prefix", 8, None),
-    ("longctx_fp8", 2, None), ("7b_32layer", 2, (0, 31))])
-def test_parity_full_size(name, max_seqs, layers):
+@pytest.mark.parametrize("name,max_seqs,layers,fused", [
+    ("tiny", None, None, True), ("llama13b_layer", 8, None, True),
+    ("llama13b_layer", 8, None, False), ("gqa_prefix", 8, None, True),
+    ("longctx_fp8", 2, None, True), ("7b_32layer", 2, (0, 31), True)])
+def test_parity_full_size(name, max_seqs, layers, fused):
     """The workloads at their full sizes (the 32-layer one with its 68.7 GB
-    pool), in the launch configuration the benchmark uses; append and output
-    checked on sampled sequences (and sampled layers)."""
+    pool), in the launch configuration the benchmark uses (the fused step);
+    append and output checked on sampled sequences (and sampled layers)."""
     cfg = W.CONFIGS[name]
-    say(f"parity_full {cfg.name} B={cfg.batch} ps={cfg.partition_size}")
-    side = H.build_product(cfg, seed=0)
+    say(f"parity_full {cfg.name} B={cfg.batch} ps={cfg.partition_size} fused={fused}")
+    side = H.build_product(cfg, seed=0, fused=fused)
     torch.cuda.synchronize()
     o = H.oracle_bookkeeping(cfg, 0)
     check_bookkeeping(side, o)
@@ -225,6 +228,62 @@ def test_table_narrower_than_context(ps, balanced):
     q = H.q_f64(side.q[0], cfg.q_dtype)
     ref = oattn.paged_decode(p6, 0, q, o.tables, lens, float(np.float32(b.scale)), cfg.kv_dtype)
     H.assert_close(H.out_f64(out, cfg.q_dtype), ref, cfg.kv_dtype, "narrow table")
+
+
+@pytest.mark.parametrize("clamp", ["table", "max_context_len"])
+@pytest.mark.parametrize("ps,balanced", [(0, False), (0, True), (32, None)])
+@pytest.mark.parametrize("hq", [2, 4])
+def test_fused_append_writes_only_inside_the_call(hq, ps, balanced, clamp):
+    """paged_attn_decode_append stores a sequence's new token only when its
+    last position is inside what the call reads: not for a zero-length
+    context, nor for one clamped by a narrow table or by max_context_len;
+    those slots keep their poison byte. Outputs match the oracle over the
+    clamped contexts. One query head per kv head (hq 2) stores the tokens
+    from inside the vector kernel, two (hq 4) through the separate append
+    kernel; the balanced pass always through the latter."""
+    import paged_kv_cache_450_amd as P
+    from oracle import attention as oattn
+
+    cfg = W.Config("fused_clamp", 1, 7, hq, 2, 64, "f16", "f16", ("uniform", 40, 300),
+                   partition_size=ps)
+    say(f"fused clamp={clamp} hq={hq} ps={ps} balanced={balanced}")
+    side = H.build_product(cfg, seed=8, balanced=balanced, run_step=False)
+    b = side.batch
+    o = H.oracle_bookkeeping(cfg, 8)
+    lens = side.lens.copy()
+    lens[1] = 0
+    if clamp == "table":
+        width, max_ctx = 5, b.max_context_len  # 80 tokens of table
+        tables = b.tables[:, :width].contiguous()
+        reach = width * 16
+    else:
+        width, max_ctx = b.tables.shape[1], 120
+        tables = b.tables
+        reach = max_ctx
+    lens_dev = torch.from_numpy(lens).cuda()
+    out = torch.full_like(b.out, float("nan"))
+    P.paged_attn_decode_append(side.cache.handle, 0, side.k_new[0], side.v_new[0], side.q[0],
+                               None if ps else out, tables, lens_dev, b.scale, max_ctx, ps,
+                               b.workspace)
+    if ps:
+        P.paged_attn_reduce(b.workspace, out, lens_dev, max_ctx, ps)
+    torch.cuda.synchronize()
+    seqs = list(range(cfg.batch))
+    p6 = H.expected_layer_pool(cfg, side, o, 0, seqs)
+    written = [i for i in seqs if 1 <= lens[i] <= reach]
+    assert 0 < len(written) < cfg.batch - 1
+    for i in seqs:
+        slot = int(o.slots_new[i])
+        blk, off = slot // 16, slot % 16
+        got = H.gpu_layer_blocks(cfg, side, 0, np.array([blk]))[:, 0, :, off, :]
+        if i in written:
+            assert np.array_equal(got, p6[0][:, blk, :, off, :]), i
+        else:
+            assert np.all(got.view(np.uint8) == H.POISON), i
+    q = H.q_f64(side.q[0], cfg.q_dtype)
+    ref = oattn.paged_decode(p6, 0, q, o.tables, np.minimum(lens, reach),
+                             float(np.float32(b.scale)), cfg.kv_dtype)
+    H.assert_close(H.out_f64(out, cfg.q_dtype), ref, cfg.kv_dtype, "fused clamp")
 
 
 @pytest.mark.parametrize("dt,dim,hq,ps", [("f16", 128, 4, 512), ("bf16", 64, 8, 16),
