@@ -51,17 +51,17 @@ KERNEL_SOURCES = {
                                            "common.h")),
 }
 MEASURED_TRAFFIC = {  # workload -> counters of its decode kernel
-    "llama13b_layer": {  # FETCH 366,973.2 KiB x 1.99988 + WRITE 320.0 KiB
-        "kernel": "valu", "bytes": 751_842_065,
-        "sources_sha256": "f4ad09cba7c3be13e923e298bb81ced247467a78c866ded9fc434b918d513437",
+    "llama13b_layer": {  # FETCH 367,313.7 KiB x 1.99988 + WRITE 960.0 KiB
+        "kernel": "valu", "bytes": 753_195_730,
+        "sources_sha256": "aade371398348d39c3c1eda88f024714e41064af8896a021aa4b0ea186847666",
         "summary": "profiles/decode_kernel_llama13b_layer.md"},
-    "longctx_fp8": {  # FETCH 715,682.8 KiB x 1.99998 + WRITE 5,755.1 KiB
-        "kernel": "valu", "bytes": 1_471_593_425,
-        "sources_sha256": "f4ad09cba7c3be13e923e298bb81ced247467a78c866ded9fc434b918d513437",
+    "longctx_fp8": {  # FETCH 715,690.3 KiB x 1.99998 + WRITE 5,754.9 KiB
+        "kernel": "valu", "bytes": 1_471_608_580,
+        "sources_sha256": "aade371398348d39c3c1eda88f024714e41064af8896a021aa4b0ea186847666",
         "summary": "profiles/decode_kernel_longctx_fp8.md"},
-    "gqa_prefix": {  # streaming kernel: FETCH 409,170.2 KiB x 1.99995 + WRITE 12,219.2 KiB
-        "kernel": "balanced", "bytes": 850_470_015,
-        "sources_sha256": "46a7d52a0ebb40b4fa12984c5f5bfeecba7c67ebcdf896500a88a62a71c1e47e",
+    "gqa_prefix": {  # streaming kernel: FETCH 408,802.7 KiB x 1.99994 + WRITE 12,218.5 KiB
+        "kernel": "balanced", "bytes": 849_715_881,
+        "sources_sha256": "bfbec6de60d3ef665a3b3db0b473e33a0f095acc01299f0a12f897e39f7b3872",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
 }
 
