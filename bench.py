@@ -327,6 +327,38 @@ def cpu_baseline(w: Workload, budget_s: float):
     }
 
 
+def block_copy_rate(cfg, pairs: int, iters: int, stream) -> dict:
+    """kv_block_copy of `pairs` blocks (every layer, K and V) into fresh blocks
+    of a pool of the workload's geometry, timed over `iters` calls back to back
+    with one event pair; bytes = read + written."""
+    import torch
+
+    import paged_kv_cache_450_amd as P
+    from paged_kv_cache_450_amd.runtime import PagedKVCache
+
+    cache = PagedKVCache(cfg.layers, 2 * pairs, cfg.kv_heads, cfg.head_dim, cfg.kv_dtype, "cuda",
+                         fill_byte=1)
+    rng = np.random.default_rng(0)
+    src = rng.permutation(pairs).astype(np.int32)
+    dst = (pairs + rng.permutation(pairs)).astype(np.int32)
+    P.kv_block_copy(cache.handle, src, dst, stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(iters):
+        P.kv_block_copy(cache.handle, src, dst, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / iters * 1e3
+    esz = 1 if cfg.kv_dtype == "e4m3" else 2
+    block_bytes = cfg.layers * 2 * cfg.kv_heads * BS * cfg.head_dim * esz
+    moved = 2 * pairs * block_bytes
+    cache.close()
+    return {"pairs": pairs, "bytes_per_block": block_bytes, "us": round(us, 3),
+            "GBs": round(moved / (us * 1e-6) / 1e9, 1),
+            "frac_hbm": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 # ------------------------------------------------------------------ main ----
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
@@ -338,6 +370,9 @@ def main(argv=None):
     ap.add_argument("--replicas", type=int, default=None,
                     help="independent copies rotated over (default: enough for >= 2 GB)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--block-copy", type=int, default=0, metavar="N",
+                    help="also time kv_block_copy of N block pairs (copy on write) on a pool of "
+                         "the workload's geometry")
     ap.add_argument("--unfused", action="store_true",
                     help="run a step as kv_cache_append + paged_attn_decode instead of the "
                          "fused paged_attn_decode_append")
@@ -480,6 +515,8 @@ def main(argv=None):
             "algorithmic_bytes": int(per_layer_unique),
         },
     }
+    if args.block_copy > 0:
+        result["block_copy"] = block_copy_rate(cfg, args.block_copy, args.steps, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
     print(json.dumps(result), flush=True)

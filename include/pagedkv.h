@@ -175,6 +175,40 @@ pkv_status kv_seq_extend(pkv_pool* pool, int32_t num_seqs, int32_t* block_tables
                          int32_t max_blocks_per_seq, const int32_t* cur_lens,
                          const int32_t* new_lens, int64_t* slot_mapping_out);
 
+/* kv_seq_extend with copy on write ([P2] "PagedAttention：...": several
+ * logical blocks may map to one physical block, as for beam search or a
+ * shared prompt; a sequence about to write into a block it shares takes a
+ * private copy first).
+ * Sequences are served in index order. When sequence i's first new token
+ * lands in a partially filled block whose refcount is above 1 at that moment,
+ * a fresh block is popped (as by block_alloc), block_tables[i][cur_lens[i]/16]
+ * is set to it, one reference on the shared block is released, and the pair
+ * (shared, fresh) is written to copy_src_out[c], copy_dst_out[c] (host int32
+ * arrays of at least num_seqs entries). A block shared by k rows is thus
+ * copied by the first k - 1 writers and kept by the last. *num_copies_out
+ * receives the number of pairs. Everything else is kv_seq_extend.
+ * Before any token is written into a fresh block, run kv_block_copy on the
+ * pairs (same stream as the appends).
+ * Errors: those of kv_seq_extend (OOM counts the copies' blocks; STATE only
+ * for a free block), INVALID (NULL num_copies_out, or NULL copy arrays when a
+ * copy is needed). On error nothing changes. */
+pkv_status kv_seq_extend_cow(pkv_pool* pool, int32_t num_seqs, int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* cur_lens,
+                             const int32_t* new_lens, int64_t* slot_mapping_out,
+                             int32_t* copy_src_out, int32_t* copy_dst_out,
+                             int32_t* num_copies_out);
+
+/* Copy whole blocks on the GPU: for every layer, K and V, all kv heads,
+ * block dst_ids[i] := block src_ids[i] ([P2] "PagedAttention：...": the copy
+ * of copy on write). src_ids, dst_ids: host int32 arrays of n ids in
+ * [0, num_blocks); destinations distinct and none of them a source of the
+ * same call (sources may repeat). Enqueued on stream; nothing is allocated
+ * (the ids travel as kernel arguments, 128 pairs per launch).
+ * Errors: INVALID (NULL pool, base or arrays, negative n, ids out of range,
+ *   a repeated destination, a destination that is also a source), HIP. */
+pkv_status kv_block_copy(const pkv_pool* pool, const int32_t* src_ids, const int32_t* dst_ids,
+                         int32_t n, hipStream_t stream);
+
 /* Write each token's K and V into its slot of one layer ([P2]
  * "PagedAttention：...": the cache grows by slots as tokens are produced;
  * third pitfall: FP8 KV cache).

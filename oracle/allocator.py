@@ -24,7 +24,13 @@ What the pages leave open, and the reading taken (this library's policy):
 * every call validates all of its arguments before it changes anything, and
   fails as a whole: INVALID (bad argument), OOM (too few free blocks), STATE
   (freeing a free block, sharing a free block, appending into a block that is
-  shared - there is no copy-on-write);
+  shared - unless the call is the copy-on-write form);
+* copy on write (``extend_cow``): a sequence whose next token lands in a
+  partially filled block that other rows still hold first takes a fresh
+  block, which must receive a copy of the shared one before the token is
+  written; it releases its reference on the shared block. Sequences are
+  served in index order, so of k rows sharing a block the first k - 1 writers
+  copy and the last one keeps the original;
 * a sequence grows one token at a time: the token at position pos goes to slot
   table[pos // BS] * BS + pos % BS, and a new block is taken from the stack
   when pos % BS == 0; sequences of one call are served in index order.
@@ -114,10 +120,21 @@ class AllocatorModel:
         Returns the slots of the new tokens, sequence by sequence, in position
         order. Fails as a whole (INVALID, STATE or OOM) with nothing changed.
         """
+        return self._extend(tables, cur_lens, new_lens, cow=False)[0]
+
+    def extend_cow(self, tables, cur_lens, new_lens):
+        """extend with copy on write. Returns (slots, copies): copies lists the
+        (shared block, fresh block) pairs in the order they were taken."""
+        return self._extend(tables, cur_lens, new_lens, cow=True)
+
+    def _extend(self, tables, cur_lens, new_lens, cow):
         bs = self.block_size
         num_seqs = len(tables)
         if len(cur_lens) != num_seqs or len(new_lens) != num_seqs:
             raise AllocError(INVALID, "length arrays do not match")
+        # Validation walks the sequences in order on a scratch copy of the
+        # counts, so that it sees the copies taken by earlier sequences.
+        ref = list(self.ref)
         needed = 0
         for i in range(num_seqs):
             cur, new = int(cur_lens[i]), int(new_lens[i])
@@ -128,18 +145,29 @@ class AllocatorModel:
                 b = int(tables[i][cur // bs])
                 if not 0 <= b < self.num_blocks:
                     raise AllocError(INVALID, "block id out of range")
-                if self.ref[b] != 1:
+                if ref[b] < 1 or (ref[b] > 1 and not cow):
                     raise AllocError(STATE, "appending into a free or shared block")
+                if ref[b] > 1:
+                    ref[b] -= 1
+                    needed += 1
             needed += -(-new // bs) - (-(-cur // bs))
         if needed > len(self.free_stack):
             raise AllocError(OOM, "not enough free blocks")
-        slots = []
+        slots, copies = [], []
         for i in range(num_seqs):
             row = tables[i]
-            for pos in range(int(cur_lens[i]), int(new_lens[i])):
+            cur, new = int(cur_lens[i]), int(new_lens[i])
+            if cow and new > cur and cur % bs != 0 and self.ref[int(row[cur // bs])] > 1:
+                shared = int(row[cur // bs])
+                fresh = self.free_stack.pop()
+                self.ref[fresh] = 1
+                self.ref[shared] -= 1
+                row[cur // bs] = fresh
+                copies.append((shared, fresh))
+            for pos in range(cur, new):
                 if pos % bs == 0:
                     b = self.free_stack.pop()
                     self.ref[b] = 1
                     row[pos // bs] = b
                 slots.append(int(row[pos // bs]) * bs + pos % bs)
-        return slots
+        return slots, copies

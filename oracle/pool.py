@@ -101,3 +101,13 @@ def append(pool6: np.ndarray, layer: int, k_raw: np.ndarray, v_raw: np.ndarray,
     # pool6[layer, c, block[t], :, offset[t], :] = codes[t] for every kept t
     pool6[layer, 0, block, :, offset, :] = k_codes[keep]
     pool6[layer, 1, block, :, offset, :] = v_codes[keep]
+
+
+def copy_blocks(pool6: np.ndarray, src_ids, dst_ids) -> None:
+    """Copy on write's copy (in place): every layer's K and V of block
+    dst_ids[i] become those of block src_ids[i]. Destinations are distinct
+    and none is a source, so the pairs do not depend on one another."""
+    src = np.asarray(src_ids, dtype=np.int64)
+    dst = np.asarray(dst_ids, dtype=np.int64)
+    if src.size:
+        pool6[:, :, dst] = pool6[:, :, src]

@@ -74,6 +74,9 @@ def _load():
         "block_refcount": (i32, [vp, i32]),
         "kv_seq_fork": (i32, [vp, p_i32, p_i32, i32]),
         "kv_seq_extend": (i32, [vp, i32, p_i32, i32, p_i32, p_i32, p_i64]),
+        "kv_seq_extend_cow": (i32, [vp, i32, p_i32, i32, p_i32, p_i32, p_i64, p_i32, p_i32,
+                                    p_i32]),
+        "kv_block_copy": (i32, [vp, p_i32, p_i32, i32, vp]),
         "kv_cache_append": (i32, [vp, i32, vp, vp, i32, vp, i32, vp, vp, vp]),
         "paged_attn_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "paged_attn_decode": (i32, [vp, i32, vp, i32, vp, vp, i32, vp, i32, i32, f32, vp, vp,
@@ -187,6 +190,28 @@ def kv_seq_extend(pool, block_tables: np.ndarray, cur_lens, new_lens) -> np.ndar
     return slots
 
 
+def kv_seq_extend_cow(pool, block_tables: np.ndarray, cur_lens, new_lens):
+    """kv_seq_extend with copy on write. Returns (slots, copy_src, copy_dst): the
+    block pairs to copy with kv_block_copy before the new tokens are written."""
+    bt = _host_i32(block_tables, writable=True)
+    if bt.ndim != 2:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]")
+    cur = _host_i32(cur_lens).reshape(-1)
+    new = _host_i32(new_lens).reshape(-1)
+    if cur.size != bt.shape[0] or new.size != bt.shape[0]:
+        raise ValueError("length arrays do not match block_tables")
+    total = int(new.astype(np.int64).sum() - cur.astype(np.int64).sum())
+    slots = np.empty(max(total, 0), dtype=np.int64)
+    src = np.empty(max(bt.shape[0], 1), dtype=np.int32)
+    dst = np.empty(max(bt.shape[0], 1), dtype=np.int32)
+    n = ctypes.c_int32(0)
+    _check(lib.kv_seq_extend_cow(pool, bt.shape[0], _i32_ptr(bt), bt.shape[1], _i32_ptr(cur),
+                                 _i32_ptr(new),
+                                 slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                 _i32_ptr(src), _i32_ptr(dst), ctypes.byref(n)))
+    return slots, src[:n.value].copy(), dst[:n.value].copy()
+
+
 # -------------------------------------------------------------- kernels ----
 def _torch():
     import torch
@@ -239,6 +264,15 @@ def kv_cache_append(pool, layer: int, k, v, slot_mapping, k_scale=None, v_scale=
         raise ValueError("one slot per token")
     _check(lib.kv_cache_append(pool, layer, _ptr(k), _ptr(v), _dtype_code(k), _ptr(slot_mapping),
                                k.shape[0], _ptr(k_scale), _ptr(v_scale), _stream(stream)))
+
+
+def kv_block_copy(pool, src_ids, dst_ids, stream=None) -> None:
+    """Copy whole blocks (every layer, K and V) src_ids[i] -> dst_ids[i] (host ids)."""
+    src = _host_i32(src_ids).reshape(-1)
+    dst = _host_i32(dst_ids).reshape(-1)
+    if src.size != dst.size:
+        raise ValueError("one destination per source")
+    _check(lib.kv_block_copy(pool, _i32_ptr(src), _i32_ptr(dst), src.size, _stream(stream)))
 
 
 def paged_attn_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,

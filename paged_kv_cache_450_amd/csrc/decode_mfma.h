@@ -28,8 +28,8 @@ using namespace pkv::dev;
 // ds_read_tr16_b64 returns the transposed 4 x 16-bit groups (one read per 16
 // dims). Row pitches 2D + 48 (D = 128) and 2D + 16 (D = 64) bytes keep both
 // the row writes and the transposed reads free of bank conflicts.
-// P is rounded to the cache dtype for the PV product; both products
-// accumulate in fp32.
+// P enters the PV product in the cache dtype (bf16: as the sum of two bf16
+// terms, see mfma_consume); both products accumulate in fp32.
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -126,6 +126,19 @@ __device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid, c
     lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     const s16x4_t pb = __builtin_bit_cast(
         s16x4_t, make_uint2(pack2<KV>(pr[0], pr[1]), pack2<KV>(pr[2], pr[3])));
+    // bf16 keeps 8 bits of a probability, which can leave a product with one
+    // dominant token 2^-9 of |v| off; the rounding residual goes through a
+    // second product, so P enters exact to about 2^-17. (f16 keeps 11 bits.)
+    s16x4_t pb_lo = {0, 0, 0, 0};
+    if constexpr (KV == PKV_BF16) {
+        float rl[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            rl[r] = pr[r] - __builtin_bit_cast(float, static_cast<uint32_t>(
+                                                          static_cast<uint16_t>(pb[r])) << 16);
+        pb_lo = __builtin_bit_cast(s16x4_t,
+                                   make_uint2(pack2<KV>(rl[0], rl[1]), pack2<KV>(rl[2], rl[3])));
+    }
 
     // Stage V in LDS (natural layout, padded rows); tokens past nvalid become
     // zeros so that stale or NaN bytes never meet a zero probability.
@@ -149,6 +162,7 @@ __device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid, c
         const v4i16 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) v4i16*)(rd + 32 * jd));
         o[jd] = mfma_pv<KV>(__builtin_bit_cast(s16x4_t, va), pb, o[jd]);
+        if constexpr (KV == PKV_BF16) o[jd] = mfma_pv<KV>(__builtin_bit_cast(s16x4_t, va), pb_lo, o[jd]);
     }
 }
 

@@ -173,48 +173,82 @@ pkv_status kv_seq_fork(pkv_pool* pool, const int32_t* src_row, int32_t* dst_row,
     return PKV_OK;
 }
 
-pkv_status kv_seq_extend(pkv_pool* pool, int32_t num_seqs, int32_t* block_tables,
-                         int32_t max_blocks_per_seq, const int32_t* cur_lens,
-                         const int32_t* new_lens, int64_t* slot_mapping_out) {
-    if (pool == nullptr) return fail(PKV_ERR_INVALID, "kv_seq_extend: pool is NULL");
+// kv_seq_extend and kv_seq_extend_cow. cow == false: a token landing in a
+// shared block is an error. cow == true: the sequence first takes a private
+// copy of that block (the pair goes to copy_src / copy_dst). Sequences are
+// served in index order, so a block shared by k rows is copied by the first
+// k - 1 of them that write into it and kept by the last.
+static pkv_status extend_impl(const char* who, pkv_pool* pool, int32_t num_seqs,
+                              int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* cur_lens, const int32_t* new_lens,
+                              int64_t* slot_mapping_out, bool cow, int32_t* copy_src,
+                              int32_t* copy_dst, int32_t* num_copies) {
+    if (pool == nullptr) return fail(PKV_ERR_INVALID, "%s: pool is NULL", who);
     if (num_seqs < 0 || max_blocks_per_seq < 0)
-        return fail(PKV_ERR_INVALID, "kv_seq_extend: negative size");
+        return fail(PKV_ERR_INVALID, "%s: negative size", who);
+    if (cow && num_copies == nullptr) return fail(PKV_ERR_INVALID, "%s: num_copies_out is NULL", who);
+    if (cow) *num_copies = 0;
     if (num_seqs == 0) return PKV_OK;
     if (block_tables == nullptr || cur_lens == nullptr || new_lens == nullptr)
-        return fail(PKV_ERR_INVALID, "kv_seq_extend: NULL array");
+        return fail(PKV_ERR_INVALID, "%s: NULL array", who);
     const int32_t bs = pool->desc.block_size;
-    int64_t needed = 0, tokens = 0;
+    int64_t needed = 0, tokens = 0, copies = 0;
+    // Reference drops of earlier copies in this call, so a later writer into
+    // the same block sees the count it will find.
+    std::unordered_map<int32_t, int32_t> dropped;
     for (int32_t i = 0; i < num_seqs; ++i) {
         const int64_t cur = cur_lens[i], nw = new_lens[i];
         if (cur < 0 || nw < cur)
-            return fail(PKV_ERR_INVALID, "kv_seq_extend: seq %d: lengths %lld -> %lld", i,
+            return fail(PKV_ERR_INVALID, "%s: seq %d: lengths %lld -> %lld", who, i,
                         static_cast<long long>(cur), static_cast<long long>(nw));
         const int64_t nb_new = (nw + bs - 1) / bs, nb_cur = (cur + bs - 1) / bs;
         if (nb_new > max_blocks_per_seq)
-            return fail(PKV_ERR_INVALID, "kv_seq_extend: seq %d needs %lld blocks, row holds %d",
-                        i, static_cast<long long>(nb_new), max_blocks_per_seq);
+            return fail(PKV_ERR_INVALID, "%s: seq %d needs %lld blocks, row holds %d", who, i,
+                        static_cast<long long>(nb_new), max_blocks_per_seq);
         if (nw > cur && cur % bs != 0) {
             const int32_t b = block_tables[static_cast<int64_t>(i) * max_blocks_per_seq + cur / bs];
             if (b < 0 || b >= pool->desc.num_blocks)
-                return fail(PKV_ERR_INVALID, "kv_seq_extend: seq %d: block id %d out of range", i,
-                            b);
-            if (pool->ref[b] != 1)
-                return fail(PKV_ERR_STATE,
-                            "kv_seq_extend: seq %d: block %d has refcount %d (free or shared)", i,
-                            b, pool->ref[b]);
+                return fail(PKV_ERR_INVALID, "%s: seq %d: block id %d out of range", who, i, b);
+            const auto it = dropped.find(b);
+            const int32_t ref = pool->ref[b] - (it == dropped.end() ? 0 : it->second);
+            if (ref < 1 || (ref > 1 && !cow))
+                return fail(PKV_ERR_STATE, "%s: seq %d: block %d has refcount %d (free or shared)",
+                            who, i, b, ref);
+            if (ref > 1) {
+                dropped[b] += 1;
+                needed += 1;
+                copies += 1;
+            }
         }
         needed += nb_new - nb_cur;
         tokens += nw - cur;
     }
     if (tokens > 0 && slot_mapping_out == nullptr)
-        return fail(PKV_ERR_INVALID, "kv_seq_extend: slot_mapping_out is NULL");
+        return fail(PKV_ERR_INVALID, "%s: slot_mapping_out is NULL", who);
+    if (copies > 0 && (copy_src == nullptr || copy_dst == nullptr))
+        return fail(PKV_ERR_INVALID, "%s: copy_src_out or copy_dst_out is NULL", who);
     if (needed > static_cast<int64_t>(pool->free_stack.size()))
-        return fail(PKV_ERR_OOM, "kv_seq_extend: %lld blocks needed, %zu free",
+        return fail(PKV_ERR_OOM, "%s: %lld blocks needed, %zu free", who,
                     static_cast<long long>(needed), pool->free_stack.size());
     int64_t k = 0;
+    int32_t c = 0;
     for (int32_t i = 0; i < num_seqs; ++i) {
         int32_t* row = block_tables + static_cast<int64_t>(i) * max_blocks_per_seq;
-        for (int32_t pos = cur_lens[i]; pos < new_lens[i]; ++pos) {
+        const int32_t cur = cur_lens[i];
+        if (cow && new_lens[i] > cur && cur % bs != 0) {
+            const int32_t b = row[cur / bs];
+            if (pool->ref[b] > 1) {  // copy on write: a private block for this row
+                const int32_t nb = pool->free_stack.back();
+                pool->free_stack.pop_back();
+                pool->ref[nb] = 1;
+                pool->ref[b] -= 1;
+                row[cur / bs] = nb;
+                copy_src[c] = b;
+                copy_dst[c] = nb;
+                ++c;
+            }
+        }
+        for (int32_t pos = cur; pos < new_lens[i]; ++pos) {
             if (pos % bs == 0) {
                 const int32_t b = pool->free_stack.back();
                 pool->free_stack.pop_back();
@@ -224,7 +258,25 @@ pkv_status kv_seq_extend(pkv_pool* pool, int32_t num_seqs, int32_t* block_tables
             slot_mapping_out[k++] = static_cast<int64_t>(row[pos / bs]) * bs + pos % bs;
         }
     }
+    if (cow) *num_copies = c;
     return PKV_OK;
+}
+
+pkv_status kv_seq_extend(pkv_pool* pool, int32_t num_seqs, int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* cur_lens,
+                         const int32_t* new_lens, int64_t* slot_mapping_out) {
+    return extend_impl("kv_seq_extend", pool, num_seqs, block_tables, max_blocks_per_seq,
+                       cur_lens, new_lens, slot_mapping_out, false, nullptr, nullptr, nullptr);
+}
+
+pkv_status kv_seq_extend_cow(pkv_pool* pool, int32_t num_seqs, int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* cur_lens,
+                             const int32_t* new_lens, int64_t* slot_mapping_out,
+                             int32_t* copy_src_out, int32_t* copy_dst_out,
+                             int32_t* num_copies_out) {
+    return extend_impl("kv_seq_extend_cow", pool, num_seqs, block_tables, max_blocks_per_seq,
+                       cur_lens, new_lens, slot_mapping_out, true, copy_src_out, copy_dst_out,
+                       num_copies_out);
 }
 
 }  // extern "C"

@@ -29,7 +29,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     out = subprocess.run(["nm", "-D", "--defined-only", P.library_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -107,6 +107,19 @@ class Both:
         slots = self.model.extend(t, cur, new)
         return np.array(t, dtype=np.int32), np.array(slots, dtype=np.int64)
 
+    def c_extend_cow(self, rows, cur, new):
+        t = np.array(rows, dtype=np.int32)
+        slots, src, dst = P.kv_seq_extend_cow(self.pool, t, cur, new)
+        return t, slots, src, dst
+
+    def m_extend_cow(self, rows, cur, new):
+        t = [list(r) for r in rows]
+        slots, copies = self.model.extend_cow(t, cur, new)
+        src = [a for a, _ in copies]
+        dst = [b for _, b in copies]
+        return (np.array(t, dtype=np.int32), np.array(slots, dtype=np.int64),
+                np.array(src, dtype=np.int32), np.array(dst, dtype=np.int32))
+
     def c_fork(self, src, n):
         dst = np.full(len(src), -1, dtype=np.int32)
         P.kv_seq_fork(self.pool, np.array(src, dtype=np.int32), dst, n)
@@ -177,6 +190,50 @@ def test_cpp_block_manager_matches_model_on_random_traces(seed):
                 b.call("extend", [[-1] * 2], [0], [40])   # row too short
             else:
                 b.call("alloc", -1)
+    P.kv_pool_destroy(b.pool)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_cpp_copy_on_write_matches_model_on_random_traces(seed):
+    """kv_seq_extend_cow against the model: forks share the partially filled
+    last block too, so growing sequences take copies; tables, slots, copy
+    pairs, the free stack and every refcount agree after every call."""
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(4, 60))
+    b = Both(n)
+    tables = {}   # rid -> (row, length)
+    nid = 0
+    copies = 0
+    for _ in range(400):
+        op = rng.choice(["admit", "grow", "grow", "finish", "fork"])
+        if op == "admit":
+            length = int(rng.integers(1, 50))
+            exc, res = b.call("extend_cow", [[-1] * 6], [0], [length])
+            if exc is None:
+                tables[nid] = (list(res[0][0]), length)
+                nid += 1
+        elif op == "grow" and tables:
+            rids = [r for r in sorted(tables) if rng.random() < 0.7] or sorted(tables)[:1]
+            rows = [tables[r][0] for r in rids]
+            cur = [tables[r][1] for r in rids]
+            new = [min(c + int(rng.integers(0, 4)), 96) for c in cur]
+            exc, res = b.call("extend_cow", rows, cur, new)
+            if exc is None:
+                copies += len(res[2])
+                for k, r in enumerate(rids):
+                    tables[r] = (list(res[0][k]), new[k])
+        elif op == "finish" and tables:
+            r = list(tables)[int(rng.integers(0, len(tables)))]
+            row, length = tables.pop(r)
+            b.call("free", row[: -(-length // 16)])
+        elif op == "fork" and tables:
+            r = list(tables)[int(rng.integers(0, len(tables)))]
+            row, length = tables[r]
+            exc, dst = b.call("fork", row, -(-length // 16))
+            if exc is None:
+                tables[nid] = (list(dst), length)
+                nid += 1
+    assert copies > 0
     P.kv_pool_destroy(b.pool)
 
 

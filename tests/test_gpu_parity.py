@@ -332,3 +332,46 @@ def test_reduce_merges_oracle_partials(dt, dim, hq, ps):
     P.paged_attn_reduce(ws, out, torch.from_numpy(lens).cuda(), max_ctx, ps)
     torch.cuda.synchronize()
     H.assert_close(H.out_f64(out, dt), ref, dt, "reduce-only")
+
+
+@pytest.mark.parametrize("balanced", [False, True])
+@pytest.mark.parametrize("dt,hq,hkv,dim", [("bf16", 16, 2, 128), ("f16", 16, 2, 128),
+                                           ("bf16", 8, 2, 64), ("bf16", 2, 2, 128)])
+def test_peaked_softmax_precision(dt, hq, hkv, dim, balanced):
+    """A sharply peaked softmax (q scaled by 3) over large values (V scaled by
+    6) on short contexts: one token carries nearly all the weight, so the
+    error of the probabilities as they enter the PV product shows up almost
+    undiluted. The tolerance still holds."""
+    import paged_kv_cache_450_amd as P
+    from oracle import attention as oattn
+    from oracle import pool as opool
+    from paged_kv_cache_450_amd.runtime import PagedKVCache
+
+    say(f"peaked softmax {dt} Hq={hq} Hkv={hkv} D={dim} balanced={balanced}")
+    name = f"peaked_{dt}_{hq}_{hkv}_{dim}"
+    B, width = 24, 4
+    lens = np.random.default_rng(W.seed_for(name, 0, "lens")).integers(1, 49, size=B).astype(np.int32)
+    nb = int(sum(-(-int(n) // 16) for n in lens))
+    cache = PagedKVCache(1, nb, hkv, dim, dt, "cuda", fill_byte=H.POISON)
+    tables = np.full((B, width), -1, dtype=np.int32)
+    slots = P.kv_seq_extend(cache.handle, tables, np.zeros(B, np.int32), lens)
+    T = int(lens.sum())
+    k = W.normal((T, hkv, dim), dt, W.seed_for(name, 0, "k"), "cuda")
+    v = (W.normal((T, hkv, dim), dt, W.seed_for(name, 0, "v"), "cuda").float() * 6).to(k.dtype)
+    q = (W.normal((B, hq, dim), dt, W.seed_for(name, 0, "q"), "cuda").float() * 3).to(k.dtype)
+    P.kv_cache_append(cache.handle, 0, k, v, torch.from_numpy(slots).cuda())
+    scale = float(np.float32(1.0 / np.sqrt(dim)))
+    out = torch.full((B, hq, dim), float("nan"), dtype=k.dtype, device="cuda")
+    ws = None
+    if balanced:
+        wsb = P.paged_attn_workspace_bytes(B, hq, dim, int(lens.max()), 0)
+        ws = torch.empty(wsb // 4, dtype=torch.float32, device="cuda")
+    P.paged_attn_decode(cache.handle, 0, q, out, torch.from_numpy(tables).cuda(),
+                        torch.from_numpy(lens).cuda(), scale, int(lens.max()), 0, ws)
+    torch.cuda.synchronize()
+    host = np.full(opool.pool_bytes(1, nb, 16, hkv, dim, dt), H.POISON, dtype=np.uint8)
+    p6 = opool.view_pool(host, 1, nb, 16, hkv, dim, dt)
+    opool.append(p6, 0, H.raw16(k), H.raw16(v), dt, dt, slots)
+    ref = oattn.paged_decode(p6, 0, H.q_f64(q, dt), tables, lens, scale, dt)
+    H.assert_close(H.out_f64(out, dt), ref, dt, name)
+    cache.close()
