@@ -12,13 +12,17 @@ manager calls followed by one decode step), "vLLM 也不是银弹：真实部署
 """
 
 import math
+from collections import deque
+from dataclasses import dataclass, field
 
 import numpy as np
 import torch
 
-from . import (BLOCK_SIZE, PKV_BF16, PKV_F16, PKV_FP8_E4M3, PoolDesc, block_alloc, block_free,
-               kv_cache_append, kv_pool_bytes, kv_pool_create, kv_pool_destroy,
-               kv_pool_free_list, kv_pool_num_free, kv_seq_extend, kv_seq_fork,
+from . import (BLOCK_SIZE, PKV_BF16, PKV_ERR_OOM, PKV_F16, PKV_FP8_E4M3, PkvError, PoolDesc,
+               block_alloc, block_free,
+               kv_block_copy, kv_cache_append, kv_pool_bytes, kv_pool_create, kv_pool_destroy,
+               kv_pool_free_list, kv_pool_num_free, kv_seq_extend, kv_seq_extend_cow,
+               kv_seq_fork,
                paged_attn_decode, paged_attn_decode_append, paged_attn_reduce,
                paged_attn_workspace_bytes)
 
@@ -174,3 +178,168 @@ class DecodeBatch:
         self.decode(layer, q, stream)
         self.reduce(stream)
         return self.out
+
+
+# ------------------------------------------------------- continuous batching ----
+@dataclass
+class Sequence:
+    """One running sequence: a sample of a request, its table row and length."""
+    rid: int
+    sample: int
+    row: np.ndarray        # int32 [max_blocks_per_seq], -1 past its blocks
+    length: int
+    gen_len: int
+    generated: int = 0
+
+    @property
+    def num_blocks(self) -> int:
+        return -(-self.length // BLOCK_SIZE)
+
+
+@dataclass
+class IterationPlan:
+    """The bookkeeping of one iteration, before any GPU work."""
+    finished: list = field(default_factory=list)   # (rid, sample) that left
+    admitted: list = field(default_factory=list)   # (spec, prompt slots int64)
+    preempted: list = field(default_factory=list)  # rids sent back to the queue
+    batch: list = field(default_factory=list)      # the running Sequences, in order
+    tables: np.ndarray = None                      # int32 [B, W] after the step's growth
+    lens: np.ndarray = None                        # int32 [B], the new token included
+    slots: np.ndarray = None                       # int64 [B], the new tokens' slots
+    copy_src: np.ndarray = None                    # copy-on-write pairs
+    copy_dst: np.ndarray = None
+
+
+class ContinuousBatcher:
+    """The per-iteration loop of continuous batching over one pool.
+
+    [P2] "连续批处理：别再等最慢的那个请求了": after every decode iteration the
+    finished requests leave the batch and free their blocks, the free blocks
+    are counted, waiting requests are admitted while they can be allocated,
+    and one decode step runs over everything that is running.
+
+    Readings where that sketch is open:
+      * a request that cannot be allocated stays at the head of the queue and
+        admission stops (first come, first served);
+      * the reserve kept free (MIN_BLOCKS) is one block per running sequence:
+        one decode step takes at most one block per sequence (a new block, or
+        a copy on write), so a step never runs out of blocks;
+      * a request with several samples is admitted as one sequence holding
+        the prompt plus forks sharing every prompt block, the partially
+        filled last one too ("PagedAttention：..."); copy on write separates
+        them at their first step;
+      * admission writes the prompt's K and V into the cache (prefill); the
+        attention over the prompt is not part of this path;
+      * when the step's growth does not fit ("vLLM 也不是银弹：...": a full
+        cache forces preemption), the most recently admitted request gives
+        back every block of all its samples and returns to the head of the
+        queue, to be prefilled again (recomputation); this repeats until the
+        step fits.
+
+    plan() does the bookkeeping of an iteration on the host (block manager
+    calls only); execute() then issues its GPU work on one stream: the prompt
+    appends, the block copies, and one fused decode step per layer.
+    """
+
+    def __init__(self, cache: PagedKVCache, max_blocks_per_seq: int):
+        self.cache = cache
+        self.width = max_blocks_per_seq
+        self.waiting = deque()
+        self.running = []
+        self.iteration = 0
+        self._specs = {}
+
+    def submit(self, spec) -> None:
+        self.waiting.append(spec)
+
+    def plan(self) -> IterationPlan:
+        h = self.cache.handle
+        p = IterationPlan()
+        # 1. finished requests leave and free their blocks
+        keep = []
+        for s in self.running:
+            if s.generated >= s.gen_len:
+                block_free(h, s.row[:s.num_blocks])
+                p.finished.append((s.rid, s.sample))
+            else:
+                keep.append(s)
+        self.running = keep
+        # 2-3. admit while the prompt fits above the reserve
+        while self.waiting:
+            spec = self.waiting[0]
+            need = -(-spec.prompt_len // BLOCK_SIZE)
+            if kv_pool_num_free(h) - need < len(self.running) + spec.samples:
+                break
+            self.waiting.popleft()
+            row = np.full(self.width, -1, dtype=np.int32)
+            slots = kv_seq_extend(h, row[None, :], [0], [spec.prompt_len])
+            seqs = [Sequence(spec.rid, 0, row, spec.prompt_len, spec.gen_len)]
+            for k in range(1, spec.samples):
+                r = np.full(self.width, -1, dtype=np.int32)
+                kv_seq_fork(h, row, r, need)
+                seqs.append(Sequence(spec.rid, k, r, spec.prompt_len, spec.gen_len))
+            self.running.extend(seqs)
+            self._specs[spec.rid] = spec
+            p.admitted.append((spec, slots))
+        # 4. the decode step's growth: one token per running sequence
+        while self.running:
+            tables = np.stack([s.row for s in self.running])
+            cur = np.array([s.length for s in self.running], dtype=np.int32)
+            try:
+                slots, src, dst = kv_seq_extend_cow(h, tables, cur, cur + 1)
+                break
+            except PkvError as e:
+                if e.status != PKV_ERR_OOM:
+                    raise
+                self._preempt_last(p)
+        p.batch = list(self.running)
+        if p.batch:
+            for k, s in enumerate(p.batch):
+                s.row[:] = tables[k]
+                s.length += 1
+                s.generated += 1
+            p.tables, p.lens, p.slots = tables, cur + 1, slots
+            p.copy_src, p.copy_dst = src, dst
+        self.iteration += 1
+        return p
+
+    def _preempt_last(self, p: IterationPlan) -> None:
+        rid = self.running[-1].rid
+        spec = self._specs[rid]
+        for s in [s for s in self.running if s.rid == rid]:
+            block_free(self.cache.handle, s.row[:s.num_blocks])
+        self.running = [s for s in self.running if s.rid != rid]
+        # admitted this iteration: its prompt appends are dropped with it
+        p.admitted = [(a, sl) for a, sl in p.admitted if a.rid != rid]
+        p.preempted.append(rid)
+        self.waiting.appendleft(spec)
+
+    def execute(self, plan: IterationPlan, prompt_kv, step_inputs, num_q_heads: int,
+                scale=None, k_scale=None, v_scale=None, workspace=None, stream=None):
+        """The iteration's GPU work. prompt_kv(spec, layer) -> (k, v) rows of a
+        prompt; step_inputs(layer, batch_size) -> (q, k_new, v_new). Returns the
+        decode outputs, one [B, Hq, D] tensor per layer."""
+        h = self.cache.handle
+        desc = self.cache.desc
+        for spec, slots in plan.admitted:
+            dev_slots = torch.from_numpy(slots).to(self.cache.buf.device)
+            for layer in range(desc.num_layers):
+                k, v = prompt_kv(spec, layer)
+                kv_cache_append(h, layer, k, v, dev_slots, k_scale, v_scale, stream)
+        outs = []
+        if not plan.batch:
+            return outs
+        kv_block_copy(h, plan.copy_src, plan.copy_dst, stream)
+        dev = self.cache.buf.device
+        tables = torch.from_numpy(plan.tables).to(dev)
+        lens = torch.from_numpy(plan.lens).to(dev)
+        sc = (1.0 / math.sqrt(desc.head_dim)) if scale is None else scale
+        max_ctx = int(plan.lens.max())
+        for layer in range(desc.num_layers):
+            q, kn, vn = step_inputs(layer, len(plan.batch))
+            out = torch.empty((len(plan.batch), num_q_heads, desc.head_dim), dtype=q.dtype,
+                              device=dev)
+            paged_attn_decode_append(h, layer, kn, vn, q, out, tables, lens, sc, max_ctx, 0,
+                                     workspace, k_scale, v_scale, stream)
+            outs.append(out)
+        return outs

@@ -1,0 +1,56 @@
+"""The continuous-batching loop's bookkeeping (host only, no GPU): the
+library's ContinuousBatcher over the C block manager against the oracle's
+loop over its allocator model, iteration by iteration on seeded request
+traces with parallel samples (forks sharing a partially filled block)."""
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_450_amd as P
+import workloads as W
+from paged_kv_cache_450_amd.runtime import ContinuousBatcher, PagedKVCache
+from tests.oracle_loop import OracleBatcher
+
+
+# 18 blocks: the largest request (4 prompt blocks, 3 samples each growing by
+# 3 blocks plus a copy) fits alone, so preemption always makes progress.
+@pytest.mark.parametrize("seed,num_blocks", [(0, 40), (1, 64), (2, 24), (3, 200), (4, 18)])
+def test_loop_bookkeeping_matches_oracle(seed, num_blocks):
+    trace = W.request_trace("batching_host", seed, 60, max_prompt=60, max_gen=40)
+    width = -(-(60 + 40) // 16)
+    cache = PagedKVCache(1, num_blocks, 2, 64, "f16", device=None)  # bookkeeping only
+    prod, orc = ContinuousBatcher(cache, width), OracleBatcher(num_blocks, width)
+    pending = list(trace)
+    copies = admitted = finished = preempted = 0
+    for it in range(3000):
+        while pending and pending[0].arrival <= it:
+            prod.submit(pending[0])
+            orc.submit(pending.pop(0))
+        p = prod.plan()
+        fin, adm, batch, slots, cps, pre = orc.plan()
+        assert p.finished == fin and p.preempted == pre
+        preempted += len(pre)
+        assert [s.rid for s, _ in p.admitted] == [s.rid for s, _ in adm]
+        for (_, a), (_, b) in zip(p.admitted, adm):
+            assert np.array_equal(a, np.array(b, dtype=np.int64))
+        assert [(s.rid, s.sample, s.length) for s in p.batch] == \
+            [(s.rid, s.sample, s.length) for s in batch]
+        if batch:
+            assert np.array_equal(p.tables, np.array([s.row for s in batch], dtype=np.int32))
+            assert np.array_equal(p.slots, np.array(slots, dtype=np.int64))
+            assert list(zip(p.copy_src.tolist(), p.copy_dst.tolist())) == cps
+        assert list(P.kv_pool_free_list(cache.handle)) == orc.model.free_stack
+        copies += len(cps)
+        admitted += len(adm)
+        for s in p.batch:  # a sequence never outgrows its row: it reaches prompt + gen
+            assert s.length <= 100
+        finished += len(fin)
+        if not pending and not prod.running and not prod.waiting:
+            break
+    # every request ran to the end; preempted ones were admitted again
+    assert admitted == len(trace) + preempted and not prod.running
+    assert copies > 0 and finished > 0
+    if num_blocks == 18:
+        assert preempted > 0  # this pool does run out
+    assert P.kv_pool_num_free(cache.handle) == num_blocks  # every block came back
+    cache.close()

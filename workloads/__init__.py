@@ -16,6 +16,7 @@ used here.
 """
 
 from .configs import CONFIGS, Config, scaled  # noqa: F401
+from .requests import RequestSpec, prompt_rows, request_trace, step_rows  # noqa: F401
 from .gen import (  # noqa: F401
     context_lengths,
     fp8_scales,
