@@ -359,6 +359,84 @@ def block_copy_rate(cfg, pairs: int, iters: int, stream) -> dict:
             "frac_hbm": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def serving_rate(cfg, iters: int, stream) -> dict:
+    """The continuous-batching loop (ContinuousBatcher) over a seeded request
+    stream shaped like the workload: prompts drawn from its context lengths,
+    8 to 128 generated tokens, a third of the requests with 2-3 samples, and
+    a pool of the workload's size (so requests queue and, at times, are
+    preempted). Inputs are drawn before the timed region; the region holds
+    the bookkeeping (host) and the GPU work of every iteration."""
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_450_amd.runtime import ContinuousBatcher, PagedKVCache
+
+    lens = W.context_lengths(cfg, 0)
+    max_prompt, max_gen = int(lens.max()), 128
+    nb = cfg.pool_blocks or blocks_needed(cfg, lens)
+    width = -(-(max_prompt + max_gen) // BS)
+    trace = W.request_trace(cfg.name + "_serve", 0, 4 * iters, max_prompt, max_gen,
+                            mean_gap=0.25)
+    rng = np.random.default_rng(0)
+    lo = int(lens.min())
+    trace = [W.RequestSpec(r.rid, r.arrival, int(rng.integers(lo, max_prompt + 1)),
+                           max(8, r.gen_len), r.samples) for r in trace]
+    cache = PagedKVCache(cfg.layers, nb, cfg.kv_heads, cfg.head_dim, cfg.kv_dtype, "cuda")
+    loop = ContinuousBatcher(cache, width)
+    dt = cfg.src_dtype
+    kp = W.normal((max_prompt, cfg.kv_heads, cfg.head_dim), dt, 1, "cuda")
+    vp = W.normal((max_prompt, cfg.kv_heads, cfg.head_dim), dt, 2, "cuda")
+    cap = 4096
+    qs = W.normal((cap, cfg.q_heads, cfg.head_dim), cfg.q_dtype, 3, "cuda")
+    ks = W.normal((cap, cfg.kv_heads, cfg.head_dim), dt, 4, "cuda")
+    vs = W.normal((cap, cfg.kv_heads, cfg.head_dim), dt, 5, "cuda")
+    k_scale = v_scale = None
+    if cfg.kv_dtype == "e4m3":
+        k_scale, v_scale = W.fp8_scales([kp, ks]), W.fp8_scales([vp, vs])
+    # the workload's single-pass form: balanced (with a workspace) or per sequence
+    wsb = P_workspace_bytes(cfg) if cfg.balanced else 0
+    workspace = torch.empty(wsb // 4, dtype=torch.float32, device="cuda") if wsb else None
+
+    def prompt_kv(spec, layer):
+        return kp[:spec.prompt_len], vp[:spec.prompt_len]
+
+    def step_inputs(layer, n):
+        return qs[:n], ks[:n], vs[:n]
+
+    pending = list(trace)
+    host_s = 0.0
+    tokens = copies = preempted = 0
+    batches = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for it in range(iters):
+        while pending and pending[0].arrival <= it:
+            loop.submit(pending.pop(0))
+        h0 = time.perf_counter()
+        plan = loop.plan()
+        host_s += time.perf_counter() - h0
+        loop.execute(plan, prompt_kv, step_inputs, cfg.q_heads, k_scale=k_scale,
+                     v_scale=v_scale, workspace=workspace, stream=stream)
+        tokens += len(plan.batch)
+        batches.append(len(plan.batch))
+        copies += len(plan.copy_src) if plan.copy_src is not None else 0
+        preempted += len(plan.preempted)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cache.close()
+    return {"iterations": iters, "decode_tokens": tokens, "tokens_per_s": round(tokens / wall, 1),
+            "ms_per_iteration": round(wall / iters * 1e3, 4),
+            "host_plan_us_per_iteration": round(host_s / iters * 1e6, 1),
+            "mean_batch": round(float(np.mean(batches)), 2), "max_batch": int(max(batches)),
+            "copies": copies, "preemptions": preempted, "pool_blocks": nb,
+            "requests_admitted": 4 * iters - len(pending) - len(loop.waiting)}
+
+
+def P_workspace_bytes(cfg) -> int:
+    import paged_kv_cache_450_amd as P
+    return P.paged_attn_workspace_bytes(1, cfg.q_heads, cfg.head_dim, 1, 0)
+
+
 # ------------------------------------------------------------------ main ----
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
@@ -373,6 +451,9 @@ def main(argv=None):
     ap.add_argument("--block-copy", type=int, default=0, metavar="N",
                     help="also time kv_block_copy of N block pairs (copy on write) on a pool of "
                          "the workload's geometry")
+    ap.add_argument("--serve", type=int, default=0, metavar="ITERS",
+                    help="also run the continuous-batching loop for ITERS iterations on a "
+                         "request stream of the workload's shape and report its rates")
     ap.add_argument("--unfused", action="store_true",
                     help="run a step as kv_cache_append + paged_attn_decode instead of the "
                          "fused paged_attn_decode_append")
@@ -515,6 +596,8 @@ def main(argv=None):
             "algorithmic_bytes": int(per_layer_unique),
         },
     }
+    if args.serve > 0:
+        result["serving"] = serving_rate(cfg, args.serve, stream)
     if args.block_copy > 0:
         result["block_copy"] = block_copy_rate(cfg, args.block_copy, args.steps, stream)
     if not args.no_cpu_baseline:
