@@ -117,7 +117,9 @@ void kv_pool_destroy(pkv_pool* pool);
 
 /* Number of free blocks ([P2] "连续批处理": get_num_free_blocks; a request
  * for n blocks can be served exactly when this is >= n, since blocks are
- * interchangeable). Returns -1 for a NULL pool. Cache usage = 1 - free/total. */
+ * interchangeable). With prefix caching, cached blocks count as free (they are
+ * evicted on demand). Returns -1 for a NULL pool. Cache usage = 1 -
+ * free/total. */
 int32_t kv_pool_num_free(const pkv_pool* pool);
 
 /* Copy the free-block stack, bottom first, into out[0 .. min(n, cap)) and
@@ -208,6 +210,42 @@ pkv_status kv_seq_extend_cow(pkv_pool* pool, int32_t num_seqs, int32_t* block_ta
  *   a repeated destination, a destination that is also a source), HIP. */
 pkv_status kv_block_copy(const pkv_pool* pool, const int32_t* src_ids, const int32_t* dst_ids,
                          int32_t n, hipStream_t stream);
+
+/* Prefix caching ([P2] "PagedAttention：...": requests with the same prompt
+ * prefix share its physical blocks; "从零开始：vLLM 部署的实战建议", third step:
+ * prefix caching). The caller names the contents of a full block with a
+ * 64-bit key (for example a hash of every token up to the block's end); the
+ * library keeps the map key -> block. A keyed block whose last reference is
+ * released keeps its contents and waits on the cached list instead of the
+ * free stack; kv_prefix_acquire can revive it. Allocation (block_alloc,
+ * kv_seq_extend, kv_seq_extend_cow) takes the free stack first and then evicts
+ * cached blocks, the longest cached first, dropping their keys.
+ * kv_pool_num_free counts free and cached blocks; kv_pool_free_list lists the
+ * free stack only. */
+
+/* Register ids[i] (live blocks whose 16 slots are written) under keys[i]
+ * (host arrays). A block keeps the first key it is given and a key the first
+ * block; other pairs are skipped. *num_registered_out (may be NULL) receives
+ * the number of pairs taken.
+ * Errors: INVALID (NULL arrays, ids out of range), STATE (a free block). On
+ * error nothing changes. */
+pkv_status kv_prefix_register(pkv_pool* pool, const uint64_t* keys, const int32_t* ids,
+                              int32_t n, int32_t* num_registered_out);
+
+/* The longest leading run keys[0..m) of registered keys: writes their blocks
+ * to ids_out[0..m) (host), takes one reference on each (a cached block
+ * becomes live again) and writes m to *matched_out. The caller then owns the
+ * references, to release with block_free.
+ * Errors: INVALID (NULL pool, arrays or matched_out, negative n). */
+pkv_status kv_prefix_acquire(pkv_pool* pool, const uint64_t* keys, int32_t n, int32_t* ids_out,
+                             int32_t* matched_out);
+
+/* Number of cached blocks, or -1 for NULL. */
+int32_t kv_pool_num_cached(const pkv_pool* pool);
+
+/* Copies up to cap cached block ids, longest cached first, into out; returns
+ * the number of cached blocks (or -1 for NULL / bad arguments). */
+int32_t kv_pool_cached_list(const pkv_pool* pool, int32_t* out, int32_t cap);
 
 /* Write each token's K and V into its slot of one layer ([P2]
  * "PagedAttention：...": the cache grows by slots as tokens are produced;

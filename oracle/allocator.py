@@ -34,6 +34,17 @@ What the pages leave open, and the reading taken (this library's policy):
 * a sequence grows one token at a time: the token at position pos goes to slot
   table[pos // BS] * BS + pos % BS, and a new block is taken from the stack
   when pos % BS == 0; sequences of one call are served in index order.
+
+Prefix caching ("PagedAttention：...": requests sharing a prompt prefix share
+its blocks; "从零开始：..." step three), with the reading taken:
+
+* the caller names a full block's contents with a key; a block keeps the
+  first key it gets, a key the first block;
+* a keyed block whose count reaches 0 keeps its contents and joins the back
+  of a cached list instead of the free stack; looking its key up revives it;
+* allocation takes the free stack first, then the front of the cached list
+  (the longest cached block), whose key is dropped; cached blocks count as
+  free.
 """
 
 OK, INVALID, OOM, STATE = 0, -1, -2, -3
@@ -53,10 +64,30 @@ class AllocatorModel:
         self.block_size = block_size
         self.free_stack = list(range(num_blocks - 1, -1, -1))
         self.ref = [0] * num_blocks
+        self.key_of = {}      # block -> key
+        self.block_of = {}    # key -> block
+        self.cached = []      # keyed blocks with no reference, oldest first
 
     # -- block manager -------------------------------------------------------
     def num_free(self) -> int:
-        return len(self.free_stack)
+        return len(self.free_stack) + len(self.cached)
+
+    def _take(self) -> int:
+        if self.free_stack:
+            b = self.free_stack.pop()
+        else:
+            b = self.cached.pop(0)
+            del self.block_of[self.key_of.pop(b)]
+        self.ref[b] = 1
+        return b
+
+    def _release(self, b) -> None:
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            if b in self.key_of:
+                self.cached.append(b)
+            else:
+                self.free_stack.append(b)
 
     def refcount(self, block_id: int) -> int:
         if 0 <= block_id < self.num_blocks:
@@ -66,14 +97,9 @@ class AllocatorModel:
     def alloc(self, n: int) -> list:
         if n < 0:
             raise AllocError(INVALID, "negative count")
-        if n > len(self.free_stack):
+        if n > self.num_free():
             raise AllocError(OOM, "not enough free blocks")
-        ids = []
-        for _ in range(n):
-            b = self.free_stack.pop()
-            self.ref[b] = 1
-            ids.append(b)
-        return ids
+        return [self._take() for _ in range(n)]
 
     def _check_ids(self, ids):
         for b in ids:
@@ -90,9 +116,7 @@ class AllocatorModel:
             if self.ref[b] < c:
                 raise AllocError(STATE, "freeing a block more times than it is held")
         for b in ids:
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                self.free_stack.append(b)
+            self._release(b)
 
     def incref(self, ids) -> None:
         ids = [int(b) for b in ids]
@@ -151,7 +175,7 @@ class AllocatorModel:
                     ref[b] -= 1
                     needed += 1
             needed += -(-new // bs) - (-(-cur // bs))
-        if needed > len(self.free_stack):
+        if needed > self.num_free():
             raise AllocError(OOM, "not enough free blocks")
         slots, copies = [], []
         for i in range(num_seqs):
@@ -159,15 +183,45 @@ class AllocatorModel:
             cur, new = int(cur_lens[i]), int(new_lens[i])
             if cow and new > cur and cur % bs != 0 and self.ref[int(row[cur // bs])] > 1:
                 shared = int(row[cur // bs])
-                fresh = self.free_stack.pop()
-                self.ref[fresh] = 1
+                fresh = self._take()
                 self.ref[shared] -= 1
                 row[cur // bs] = fresh
                 copies.append((shared, fresh))
             for pos in range(cur, new):
                 if pos % bs == 0:
-                    b = self.free_stack.pop()
-                    self.ref[b] = 1
-                    row[pos // bs] = b
+                    row[pos // bs] = self._take()
                 slots.append(int(row[pos // bs]) * bs + pos % bs)
         return slots, copies
+
+    # -- prefix caching ----------------------------------------------------------
+    def register(self, keys, ids) -> int:
+        """Name live blocks by content keys; returns how many pairs were taken."""
+        ids = [int(b) for b in ids]
+        keys = [int(k) for k in keys]
+        if len(keys) != len(ids):
+            raise AllocError(INVALID, "one key per block")
+        self._check_ids(ids)
+        for b in ids:
+            if self.ref[b] == 0:
+                raise AllocError(STATE, "registering a free block")
+        taken = 0
+        for k, b in zip(keys, ids):
+            if b in self.key_of or k in self.block_of:
+                continue
+            self.key_of[b] = k
+            self.block_of[k] = b
+            taken += 1
+        return taken
+
+    def acquire(self, keys) -> list:
+        """Blocks of the longest leading run of known keys, one reference each."""
+        out = []
+        for k in keys:
+            b = self.block_of.get(int(k))
+            if b is None:
+                break
+            if self.ref[b] == 0:
+                self.cached.remove(b)
+            self.ref[b] += 1
+            out.append(b)
+        return out

@@ -77,6 +77,10 @@ def _load():
         "kv_seq_extend_cow": (i32, [vp, i32, p_i32, i32, p_i32, p_i32, p_i64, p_i32, p_i32,
                                     p_i32]),
         "kv_block_copy": (i32, [vp, p_i32, p_i32, i32, vp]),
+        "kv_prefix_register": (i32, [vp, ctypes.POINTER(ctypes.c_uint64), p_i32, i32, p_i32]),
+        "kv_prefix_acquire": (i32, [vp, ctypes.POINTER(ctypes.c_uint64), i32, p_i32, p_i32]),
+        "kv_pool_num_cached": (i32, [vp]),
+        "kv_pool_cached_list": (i32, [vp, p_i32, i32]),
         "kv_cache_append": (i32, [vp, i32, vp, vp, i32, vp, i32, vp, vp, vp]),
         "paged_attn_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "paged_attn_decode": (i32, [vp, i32, vp, i32, vp, vp, i32, vp, i32, i32, f32, vp, vp,
@@ -146,6 +150,44 @@ def kv_pool_free_list(pool) -> np.ndarray:
     out = np.empty(n, dtype=np.int32)
     lib.kv_pool_free_list(pool, _i32_ptr(out), n)
     return out
+
+
+def kv_pool_num_cached(pool) -> int:
+    return int(lib.kv_pool_num_cached(pool))
+
+
+def kv_pool_cached_list(pool) -> np.ndarray:
+    """Cached blocks (prefix caching), longest cached first."""
+    n = lib.kv_pool_cached_list(pool, None, 0)
+    if n < 0:
+        raise PkvError(PKV_ERR_INVALID, "kv_pool_cached_list failed")
+    out = np.empty(n, dtype=np.int32)
+    lib.kv_pool_cached_list(pool, _i32_ptr(out), n)
+    return out
+
+
+def _u64_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
+
+
+def kv_prefix_register(pool, keys, ids) -> int:
+    """Register full blocks under content keys; returns how many pairs were taken."""
+    k = np.ascontiguousarray(np.asarray(keys, dtype=np.uint64).reshape(-1))
+    b = _host_i32(ids).reshape(-1)
+    if k.size != b.size:
+        raise ValueError("one key per block")
+    n = ctypes.c_int32(0)
+    _check(lib.kv_prefix_register(pool, _u64_ptr(k), _i32_ptr(b), b.size, ctypes.byref(n)))
+    return n.value
+
+
+def kv_prefix_acquire(pool, keys) -> np.ndarray:
+    """Blocks of the longest leading run of registered keys, one reference taken on each."""
+    k = np.ascontiguousarray(np.asarray(keys, dtype=np.uint64).reshape(-1))
+    out = np.empty(max(k.size, 1), dtype=np.int32)
+    m = ctypes.c_int32(0)
+    _check(lib.kv_prefix_acquire(pool, _u64_ptr(k), k.size, _i32_ptr(out), ctypes.byref(m)))
+    return out[:m.value].copy()
 
 
 def block_alloc(pool, n: int) -> np.ndarray:

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstddef>
 #include <cstdint>
+#include <unordered_map>
 #include <vector>
 
 #include "pagedkv.h"
@@ -14,6 +15,16 @@ struct pkv_pool {
     size_t bytes;
     std::vector<int32_t> free_stack;  // top = back()
     std::vector<int32_t> ref;         // per-block reference count
+    // Prefix caching. A block may hold a content key. A keyed block whose last
+    // reference is released keeps its contents on the cached list (a doubly
+    // linked list by id, oldest release at the head) instead of going back to
+    // the free stack; allocation evicts from the head, dropping the key, only
+    // once the free stack is empty.
+    std::unordered_map<uint64_t, int32_t> key_block;
+    std::vector<uint64_t> block_key;
+    std::vector<uint8_t> keyed;
+    std::vector<int32_t> cprev, cnext;
+    int32_t chead = -1, ctail = -1, ncached = 0;
 };
 
 namespace pkv {

@@ -81,6 +81,10 @@ pkv_status kv_pool_create(const pkv_pool_desc* desc, void* device_base, size_t b
         for (int32_t i = 0; i < desc->num_blocks; ++i)
             p->free_stack[i] = desc->num_blocks - 1 - i;  // top = 0
         p->ref.assign(desc->num_blocks, 0);
+        p->block_key.assign(desc->num_blocks, 0);
+        p->keyed.assign(desc->num_blocks, 0);
+        p->cprev.assign(desc->num_blocks, -1);
+        p->cnext.assign(desc->num_blocks, -1);
     } catch (...) {
         delete p;
         return fail(PKV_ERR_OOM, "kv_pool_create: host allocation failed");
@@ -93,7 +97,7 @@ void kv_pool_destroy(pkv_pool* pool) { delete pool; }
 
 int32_t kv_pool_num_free(const pkv_pool* pool) {
     if (pool == nullptr) return -1;
-    return static_cast<int32_t>(pool->free_stack.size());
+    return static_cast<int32_t>(pool->free_stack.size()) + pool->ncached;
 }
 
 int32_t kv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap) {
@@ -104,19 +108,63 @@ int32_t kv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap) {
     return n;
 }
 
+// ---- cached list (prefix caching) ------------------------------------------
+static void cached_unlink(pkv_pool* p, int32_t b) {
+    const int32_t pv = p->cprev[b], nx = p->cnext[b];
+    (pv >= 0 ? p->cnext[pv] : p->chead) = nx;
+    (nx >= 0 ? p->cprev[nx] : p->ctail) = pv;
+    p->cprev[b] = p->cnext[b] = -1;
+    p->ncached -= 1;
+}
+
+static void cached_push(pkv_pool* p, int32_t b) {
+    p->cprev[b] = p->ctail;
+    p->cnext[b] = -1;
+    (p->ctail >= 0 ? p->cnext[p->ctail] : p->chead) = b;
+    p->ctail = b;
+    p->ncached += 1;
+}
+
+static size_t available(const pkv_pool* p) {
+    return p->free_stack.size() + static_cast<size_t>(p->ncached);
+}
+
+// A block for a new owner (the caller checked that one is available): the top
+// of the free stack, else the longest-cached block, whose key is dropped.
+static int32_t take_block(pkv_pool* p) {
+    int32_t b;
+    if (!p->free_stack.empty()) {
+        b = p->free_stack.back();
+        p->free_stack.pop_back();
+    } else {
+        b = p->chead;
+        cached_unlink(p, b);
+        p->key_block.erase(p->block_key[b]);
+        p->keyed[b] = 0;
+    }
+    p->ref[b] = 1;
+    return b;
+}
+
+// One reference released; a block left with none goes to the free stack, or
+// to the cached list if it holds a key.
+static void release(pkv_pool* p, int32_t b) {
+    if (--p->ref[b] == 0) {
+        if (p->keyed[b])
+            cached_push(p, b);
+        else
+            p->free_stack.push_back(b);
+    }
+}
+
 pkv_status block_alloc(pkv_pool* pool, int32_t n, int32_t* out_ids) {
     if (pool == nullptr) return fail(PKV_ERR_INVALID, "block_alloc: pool is NULL");
     if (n < 0) return fail(PKV_ERR_INVALID, "block_alloc: negative count %d", n);
     if (n > 0 && out_ids == nullptr) return fail(PKV_ERR_INVALID, "block_alloc: out_ids is NULL");
-    if (static_cast<size_t>(n) > pool->free_stack.size())
+    if (static_cast<size_t>(n) > available(pool))
         return fail(PKV_ERR_OOM, "block_alloc: %d blocks requested, %zu free", n,
-                    pool->free_stack.size());
-    for (int32_t i = 0; i < n; ++i) {
-        const int32_t b = pool->free_stack.back();
-        pool->free_stack.pop_back();
-        pool->ref[b] = 1;
-        out_ids[i] = b;
-    }
+                    available(pool));
+    for (int32_t i = 0; i < n; ++i) out_ids[i] = take_block(pool);
     return PKV_OK;
 }
 
@@ -141,10 +189,7 @@ pkv_status block_free(pkv_pool* pool, int32_t n, const int32_t* ids) {
         if (pool->ref[kv.first] < kv.second)
             return fail(PKV_ERR_STATE, "block_free: block %d holds %d references, %d released",
                         kv.first, pool->ref[kv.first], kv.second);
-    for (int32_t i = 0; i < n; ++i) {
-        const int32_t b = ids[i];
-        if (--pool->ref[b] == 0) pool->free_stack.push_back(b);
-    }
+    for (int32_t i = 0; i < n; ++i) release(pool, ids[i]);
     return PKV_OK;
 }
 
@@ -227,9 +272,9 @@ static pkv_status extend_impl(const char* who, pkv_pool* pool, int32_t num_seqs,
         return fail(PKV_ERR_INVALID, "%s: slot_mapping_out is NULL", who);
     if (copies > 0 && (copy_src == nullptr || copy_dst == nullptr))
         return fail(PKV_ERR_INVALID, "%s: copy_src_out or copy_dst_out is NULL", who);
-    if (needed > static_cast<int64_t>(pool->free_stack.size()))
+    if (needed > static_cast<int64_t>(available(pool)))
         return fail(PKV_ERR_OOM, "%s: %lld blocks needed, %zu free", who,
-                    static_cast<long long>(needed), pool->free_stack.size());
+                    static_cast<long long>(needed), available(pool));
     int64_t k = 0;
     int32_t c = 0;
     for (int32_t i = 0; i < num_seqs; ++i) {
@@ -238,9 +283,7 @@ static pkv_status extend_impl(const char* who, pkv_pool* pool, int32_t num_seqs,
         if (cow && new_lens[i] > cur && cur % bs != 0) {
             const int32_t b = row[cur / bs];
             if (pool->ref[b] > 1) {  // copy on write: a private block for this row
-                const int32_t nb = pool->free_stack.back();
-                pool->free_stack.pop_back();
-                pool->ref[nb] = 1;
+                const int32_t nb = take_block(pool);
                 pool->ref[b] -= 1;
                 row[cur / bs] = nb;
                 copy_src[c] = b;
@@ -249,12 +292,7 @@ static pkv_status extend_impl(const char* who, pkv_pool* pool, int32_t num_seqs,
             }
         }
         for (int32_t pos = cur; pos < new_lens[i]; ++pos) {
-            if (pos % bs == 0) {
-                const int32_t b = pool->free_stack.back();
-                pool->free_stack.pop_back();
-                pool->ref[b] = 1;
-                row[pos / bs] = b;
-            }
+            if (pos % bs == 0) row[pos / bs] = take_block(pool);
             slot_mapping_out[k++] = static_cast<int64_t>(row[pos / bs]) * bs + pos % bs;
         }
     }
@@ -277,6 +315,60 @@ pkv_status kv_seq_extend_cow(pkv_pool* pool, int32_t num_seqs, int32_t* block_ta
     return extend_impl("kv_seq_extend_cow", pool, num_seqs, block_tables, max_blocks_per_seq,
                        cur_lens, new_lens, slot_mapping_out, true, copy_src_out, copy_dst_out,
                        num_copies_out);
+}
+
+int32_t kv_pool_num_cached(const pkv_pool* pool) {
+    if (pool == nullptr) return -1;
+    return pool->ncached;
+}
+
+int32_t kv_pool_cached_list(const pkv_pool* pool, int32_t* out, int32_t cap) {
+    if (pool == nullptr || cap < 0 || (cap > 0 && out == nullptr)) return -1;
+    int32_t k = 0;
+    for (int32_t b = pool->chead; b >= 0 && k < cap; b = pool->cnext[b]) out[k++] = b;
+    return pool->ncached;
+}
+
+pkv_status kv_prefix_register(pkv_pool* pool, const uint64_t* keys, const int32_t* ids,
+                              int32_t n, int32_t* num_registered_out) {
+    pkv_status st = check_ids(pool, n, ids, "kv_prefix_register");
+    if (st != PKV_OK) return st;
+    if (n > 0 && keys == nullptr) return fail(PKV_ERR_INVALID, "kv_prefix_register: keys is NULL");
+    for (int32_t i = 0; i < n; ++i)
+        if (pool->ref[ids[i]] == 0)
+            return fail(PKV_ERR_STATE, "kv_prefix_register: block %d is free", ids[i]);
+    int32_t added = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t b = ids[i];
+        if (pool->keyed[b] || pool->key_block.count(keys[i])) continue;  // first key wins
+        pool->key_block.emplace(keys[i], b);
+        pool->block_key[b] = keys[i];
+        pool->keyed[b] = 1;
+        ++added;
+    }
+    if (num_registered_out != nullptr) *num_registered_out = added;
+    return PKV_OK;
+}
+
+pkv_status kv_prefix_acquire(pkv_pool* pool, const uint64_t* keys, int32_t n, int32_t* ids_out,
+                             int32_t* matched_out) {
+    if (pool == nullptr) return fail(PKV_ERR_INVALID, "kv_prefix_acquire: pool is NULL");
+    if (n < 0) return fail(PKV_ERR_INVALID, "kv_prefix_acquire: negative count %d", n);
+    if (matched_out == nullptr)
+        return fail(PKV_ERR_INVALID, "kv_prefix_acquire: matched_out is NULL");
+    if (n > 0 && (keys == nullptr || ids_out == nullptr))
+        return fail(PKV_ERR_INVALID, "kv_prefix_acquire: NULL keys or ids_out");
+    int32_t m = 0;
+    for (; m < n; ++m) {
+        const auto it = pool->key_block.find(keys[m]);
+        if (it == pool->key_block.end()) break;
+        const int32_t b = it->second;
+        if (pool->ref[b] == 0) cached_unlink(pool, b);
+        pool->ref[b] += 1;
+        ids_out[m] = b;
+    }
+    *matched_out = m;
+    return PKV_OK;
 }
 
 }  // extern "C"

@@ -21,8 +21,8 @@ import torch
 from . import (BLOCK_SIZE, PKV_BF16, PKV_ERR_OOM, PKV_F16, PKV_FP8_E4M3, PkvError, PoolDesc,
                block_alloc, block_free,
                kv_block_copy, kv_cache_append, kv_pool_bytes, kv_pool_create, kv_pool_destroy,
-               kv_pool_free_list, kv_pool_num_free, kv_seq_extend, kv_seq_extend_cow,
-               kv_seq_fork,
+               kv_pool_free_list, kv_pool_num_free, kv_prefix_acquire, kv_prefix_register,
+               kv_seq_extend, kv_seq_extend_cow, kv_seq_fork,
                paged_attn_decode, paged_attn_decode_append, paged_attn_reduce,
                paged_attn_workspace_bytes)
 
@@ -200,7 +200,7 @@ class Sequence:
 class IterationPlan:
     """The bookkeeping of one iteration, before any GPU work."""
     finished: list = field(default_factory=list)   # (rid, sample) that left
-    admitted: list = field(default_factory=list)   # (spec, prompt slots int64)
+    admitted: list = field(default_factory=list)   # (spec, first prefilled token, its slots)
     preempted: list = field(default_factory=list)  # rids sent back to the queue
     batch: list = field(default_factory=list)      # the running Sequences, in order
     tables: np.ndarray = None                      # int32 [B, W] after the step's growth
@@ -234,16 +234,22 @@ class ContinuousBatcher:
         cache forces preemption), the most recently admitted request gives
         back every block of all its samples and returns to the head of the
         queue, to be prefilled again (recomputation); this repeats until the
-        step fits.
+        step fits;
+      * with prefix caching ("从零开始：..." third step), admission first takes
+        the cached blocks of the longest leading run of the prompt's block
+        keys (spec.block_keys), prefills only the tokens after them, and
+        registers its new full prompt blocks under their keys; if the request
+        then does not fit, the cached blocks are given back.
 
     plan() does the bookkeeping of an iteration on the host (block manager
     calls only); execute() then issues its GPU work on one stream: the prompt
     appends, the block copies, and one fused decode step per layer.
     """
 
-    def __init__(self, cache: PagedKVCache, max_blocks_per_seq: int):
+    def __init__(self, cache: PagedKVCache, max_blocks_per_seq: int, prefix_caching=False):
         self.cache = cache
         self.width = max_blocks_per_seq
+        self.prefix_caching = prefix_caching
         self.waiting = deque()
         self.running = []
         self.iteration = 0
@@ -267,12 +273,21 @@ class ContinuousBatcher:
         # 2-3. admit while the prompt fits above the reserve
         while self.waiting:
             spec = self.waiting[0]
-            need = -(-spec.prompt_len // BLOCK_SIZE)
-            if kv_pool_num_free(h) - need < len(self.running) + spec.samples:
+            nblk = -(-spec.prompt_len // BLOCK_SIZE)
+            hit = (kv_prefix_acquire(h, spec.block_keys) if self.prefix_caching
+                   else np.zeros(0, dtype=np.int32))
+            if kv_pool_num_free(h) - (nblk - hit.size) < len(self.running) + spec.samples:
+                if hit.size:
+                    block_free(h, hit)
                 break
             self.waiting.popleft()
             row = np.full(self.width, -1, dtype=np.int32)
-            slots = kv_seq_extend(h, row[None, :], [0], [spec.prompt_len])
+            row[:hit.size] = hit
+            first = int(hit.size) * BLOCK_SIZE
+            slots = kv_seq_extend(h, row[None, :], [first], [spec.prompt_len])
+            if self.prefix_caching and len(spec.block_keys) > hit.size:
+                kv_prefix_register(h, spec.block_keys[hit.size:], row[hit.size:len(spec.block_keys)])
+            need = nblk
             seqs = [Sequence(spec.rid, 0, row, spec.prompt_len, spec.gen_len)]
             for k in range(1, spec.samples):
                 r = np.full(self.width, -1, dtype=np.int32)
@@ -280,7 +295,7 @@ class ContinuousBatcher:
                 seqs.append(Sequence(spec.rid, k, r, spec.prompt_len, spec.gen_len))
             self.running.extend(seqs)
             self._specs[spec.rid] = spec
-            p.admitted.append((spec, slots))
+            p.admitted.append((spec, first, slots))
         # 4. the decode step's growth: one token per running sequence
         while self.running:
             tables = np.stack([s.row for s in self.running])
@@ -310,22 +325,26 @@ class ContinuousBatcher:
             block_free(self.cache.handle, s.row[:s.num_blocks])
         self.running = [s for s in self.running if s.rid != rid]
         # admitted this iteration: its prompt appends are dropped with it
-        p.admitted = [(a, sl) for a, sl in p.admitted if a.rid != rid]
+        p.admitted = [a for a in p.admitted if a[0].rid != rid]
         p.preempted.append(rid)
         self.waiting.appendleft(spec)
 
     def execute(self, plan: IterationPlan, prompt_kv, step_inputs, num_q_heads: int,
                 scale=None, k_scale=None, v_scale=None, workspace=None, stream=None):
-        """The iteration's GPU work. prompt_kv(spec, layer) -> (k, v) rows of a
-        prompt; step_inputs(layer, batch_size) -> (q, k_new, v_new). Returns the
-        decode outputs, one [B, Hq, D] tensor per layer."""
+        """The iteration's GPU work. prompt_kv(spec, layer) -> (k, v): the rows
+        of a whole prompt (those after the cached blocks are written);
+        step_inputs(layer, batch_size) -> (q, k_new, v_new). Returns the decode
+        outputs, one [B, Hq, D] tensor per layer."""
         h = self.cache.handle
         desc = self.cache.desc
-        for spec, slots in plan.admitted:
+        for spec, first, slots in plan.admitted:
+            if slots.size == 0:  # every prompt block came from the cache
+                continue
             dev_slots = torch.from_numpy(slots).to(self.cache.buf.device)
             for layer in range(desc.num_layers):
                 k, v = prompt_kv(spec, layer)
-                kv_cache_append(h, layer, k, v, dev_slots, k_scale, v_scale, stream)
+                kv_cache_append(h, layer, k[first:], v[first:], dev_slots, k_scale, v_scale,
+                                stream)
         outs = []
         if not plan.batch:
             return outs

@@ -23,9 +23,10 @@ class OracleSeq:
 
 
 class OracleBatcher:
-    def __init__(self, num_blocks, width):
+    def __init__(self, num_blocks, width, prefix_caching=False):
         self.model = A.AllocatorModel(num_blocks, BS)
         self.width = width
+        self.prefix_caching = prefix_caching
         self.waiting = deque()
         self.running = []
         self.specs = {}
@@ -47,18 +48,25 @@ class OracleBatcher:
         while self.waiting:
             spec = self.waiting[0]
             need = -(-spec.prompt_len // BS)
-            if m.num_free() - need < len(self.running) + spec.samples:
+            hit = m.acquire(spec.block_keys) if self.prefix_caching else []
+            if m.num_free() - (need - len(hit)) < len(self.running) + spec.samples:
+                if hit:
+                    m.free(hit)
                 break
             self.waiting.popleft()
             row = [-1] * self.width
-            slots = m.extend([row], [0], [spec.prompt_len])
+            row[:len(hit)] = hit
+            first = len(hit) * BS
+            slots = m.extend([row], [first], [spec.prompt_len])
+            if self.prefix_caching and len(spec.block_keys) > len(hit):
+                m.register(spec.block_keys[len(hit):], row[len(hit):len(spec.block_keys)])
             self.running.append(OracleSeq(spec.rid, 0, row, spec.prompt_len, spec.gen_len))
             for k in range(1, spec.samples):
                 r = [-1] * self.width
                 m.fork(row, r, need)
                 self.running.append(OracleSeq(spec.rid, k, r, spec.prompt_len, spec.gen_len))
             self.specs[spec.rid] = spec
-            admitted.append((spec, slots))
+            admitted.append((spec, first, slots))
         slots, copies, preempted = [], [], []
         while self.running:
             rows = [list(s.row) for s in self.running]
@@ -72,7 +80,7 @@ class OracleBatcher:
                 for s in [s for s in self.running if s.rid == rid]:
                     m.free(s.row[: -(-s.length // BS)])
                 self.running = [s for s in self.running if s.rid != rid]
-                admitted = [(a, sl) for a, sl in admitted if a.rid != rid]
+                admitted = [a for a in admitted if a[0].rid != rid]
                 preempted.append(rid)
                 self.waiting.appendleft(self.specs[rid])
                 continue

@@ -14,14 +14,21 @@ from tests.oracle_loop import OracleBatcher
 
 # 18 blocks: the largest request (4 prompt blocks, 3 samples each growing by
 # 3 blocks plus a copy) fits alone, so preemption always makes progress.
-@pytest.mark.parametrize("seed,num_blocks", [(0, 40), (1, 64), (2, 24), (3, 200), (4, 18)])
-def test_loop_bookkeeping_matches_oracle(seed, num_blocks):
-    trace = W.request_trace("batching_host", seed, 60, max_prompt=60, max_gen=40)
+@pytest.mark.parametrize("seed,num_blocks,caching", [
+    (0, 40, False), (1, 64, False), (2, 24, False), (3, 200, False), (4, 18, False),
+    (5, 40, True), (6, 24, True), (7, 120, True)])
+def test_loop_bookkeeping_matches_oracle(seed, num_blocks, caching):
+    """With caching, the trace's requests come in prefix groups sharing a
+    48-token system prompt, admitted through the prefix cache."""
+    groups = (3, 48) if caching else (0, 0)
+    trace = W.request_trace("batching_host", seed, 60, max_prompt=60, max_gen=40,
+                            prefix_groups=groups[0], shared_tokens=groups[1])
     width = -(-(60 + 40) // 16)
     cache = PagedKVCache(1, num_blocks, 2, 64, "f16", device=None)  # bookkeeping only
-    prod, orc = ContinuousBatcher(cache, width), OracleBatcher(num_blocks, width)
+    prod = ContinuousBatcher(cache, width, prefix_caching=caching)
+    orc = OracleBatcher(num_blocks, width, prefix_caching=caching)
     pending = list(trace)
-    copies = admitted = finished = preempted = 0
+    copies = admitted = finished = preempted = reused = 0
     for it in range(3000):
         while pending and pending[0].arrival <= it:
             prod.submit(pending[0])
@@ -30,9 +37,9 @@ def test_loop_bookkeeping_matches_oracle(seed, num_blocks):
         fin, adm, batch, slots, cps, pre = orc.plan()
         assert p.finished == fin and p.preempted == pre
         preempted += len(pre)
-        assert [s.rid for s, _ in p.admitted] == [s.rid for s, _ in adm]
-        for (_, a), (_, b) in zip(p.admitted, adm):
-            assert np.array_equal(a, np.array(b, dtype=np.int64))
+        assert [(a[0].rid, a[1]) for a in p.admitted] == [(a[0].rid, a[1]) for a in adm]
+        for a, b in zip(p.admitted, adm):
+            assert np.array_equal(a[2], np.array(b[2], dtype=np.int64))
         assert [(s.rid, s.sample, s.length) for s in p.batch] == \
             [(s.rid, s.sample, s.length) for s in batch]
         if batch:
@@ -40,6 +47,8 @@ def test_loop_bookkeeping_matches_oracle(seed, num_blocks):
             assert np.array_equal(p.slots, np.array(slots, dtype=np.int64))
             assert list(zip(p.copy_src.tolist(), p.copy_dst.tolist())) == cps
         assert list(P.kv_pool_free_list(cache.handle)) == orc.model.free_stack
+        assert list(P.kv_pool_cached_list(cache.handle)) == orc.model.cached
+        reused += sum(a[1] // 16 for a in adm)
         copies += len(cps)
         admitted += len(adm)
         for s in p.batch:  # a sequence never outgrows its row: it reaches prompt + gen
@@ -53,4 +62,6 @@ def test_loop_bookkeeping_matches_oracle(seed, num_blocks):
     if num_blocks == 18:
         assert preempted > 0  # this pool does run out
     assert P.kv_pool_num_free(cache.handle) == num_blocks  # every block came back
+    if caching:
+        assert reused > 0  # prompts were served from the cache
     cache.close()

@@ -29,7 +29,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 23, names
     out = subprocess.run(["nm", "-D", "--defined-only", P.library_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -54,6 +54,7 @@ class Both:
 
     def check(self):
         assert list(P.kv_pool_free_list(self.pool)) == self.model.free_stack
+        assert list(P.kv_pool_cached_list(self.pool)) == self.model.cached
         refs = [P.block_refcount(self.pool, b) for b in range(self.n)]
         assert refs == self.model.ref
         assert P.kv_pool_num_free(self.pool) == self.model.num_free()
@@ -119,6 +120,18 @@ class Both:
         dst = [b for _, b in copies]
         return (np.array(t, dtype=np.int32), np.array(slots, dtype=np.int64),
                 np.array(src, dtype=np.int32), np.array(dst, dtype=np.int32))
+
+    def c_register(self, keys, ids):
+        return P.kv_prefix_register(self.pool, keys, np.array(ids, dtype=np.int32))
+
+    def m_register(self, keys, ids):
+        return self.model.register(keys, ids)
+
+    def c_acquire(self, keys):
+        return P.kv_prefix_acquire(self.pool, keys)
+
+    def m_acquire(self, keys):
+        return np.array(self.model.acquire(keys), dtype=np.int32)
 
     def c_fork(self, src, n):
         dst = np.full(len(src), -1, dtype=np.int32)
@@ -234,6 +247,47 @@ def test_cpp_copy_on_write_matches_model_on_random_traces(seed):
                 tables[nid] = (list(dst), length)
                 nid += 1
     assert copies > 0
+    P.kv_pool_destroy(b.pool)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_cpp_prefix_cache_matches_model_on_random_traces(seed):
+    """Registration, acquisition, release to the cached list and eviction on
+    allocation: returned ids, the free stack, the cached list and every
+    refcount agree with the model after every call."""
+    rng = np.random.default_rng(200 + seed)
+    n = int(rng.integers(4, 40))
+    b = Both(n)
+    live = []     # lists of ids held by a "request"
+    keys = [int(k) for k in rng.integers(1, 2**62, size=30)]
+    hits = evictions = 0
+    for _ in range(400):
+        op = rng.choice(["alloc", "register", "acquire", "free", "extend"])
+        if op == "alloc":
+            before = P.kv_pool_num_cached(b.pool)
+            exc, ids = b.call("alloc", int(rng.integers(1, 5)))
+            if exc is None:
+                live.append(list(ids))
+                evictions += max(0, before - P.kv_pool_num_cached(b.pool))
+        elif op == "register" and live:
+            ids = live[int(rng.integers(0, len(live)))]
+            ks = [keys[int(i)] for i in rng.integers(0, len(keys), size=len(ids))]
+            b.call("register", ks, ids)
+        elif op == "acquire":
+            start = int(rng.integers(0, len(keys) - 4))
+            exc, ids = b.call("acquire", keys[start:start + int(rng.integers(1, 5))])
+            if exc is None and len(ids):
+                hits += len(ids)
+                live.append(list(ids))
+        elif op == "free" and live:
+            b.call("free", live.pop(int(rng.integers(0, len(live)))))
+        elif op == "extend":
+            exc, res = b.call("extend", [[-1] * 4], [0], [int(rng.integers(1, 64))])
+            if exc is None:
+                live.append([x for x in res[0][0] if x >= 0])
+        elif op == "register":
+            b.call("register", [keys[0]], [n + 5])  # out of range
+    assert hits > 0 and evictions > 0
     P.kv_pool_destroy(b.pool)
 
 

@@ -34,25 +34,32 @@ def _gpu(require_gpu):
     torch.cuda.synchronize()
 
 
-# The last pool is tight enough that the loop preempts (three times on this
-# trace) yet holds the largest request alone.
-@pytest.mark.parametrize("dt,hq,hkv,dim,num_blocks,max_gen", [
-    ("f16", 2, 2, 64, 48, 12), ("bf16", 8, 2, 128, 30, 12), ("f16", 4, 4, 128, 16, 40)])
-def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen):
-    name = f"batching_{dt}_{hq}_{hkv}_{dim}_{num_blocks}"
+# The third pool is tight enough that the loop preempts (three times on this
+# trace) yet holds the largest request alone. The last two run with prefix
+# caching: requests in groups sharing a 48-token system prompt, admitted
+# through the cache (the second pool small enough to evict cached blocks).
+@pytest.mark.parametrize("dt,hq,hkv,dim,num_blocks,max_gen,caching", [
+    ("f16", 2, 2, 64, 48, 12, False), ("bf16", 8, 2, 128, 30, 12, False),
+    ("f16", 4, 4, 128, 16, 40, False), ("bf16", 8, 2, 128, 40, 12, True),
+    ("f16", 2, 2, 64, 20, 12, True)])
+def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching):
+    name = f"batching_{dt}_{hq}_{hkv}_{dim}_{num_blocks}_{caching}"
     say(name)
     layers, max_prompt = 2, 40
-    width = -(-(max_prompt + max_gen) // 16)
-    trace = W.request_trace(name, 0, 24, max_prompt, max_gen)
+    width = -(-(max_prompt + 48 + max_gen) // 16)
+    groups = (3, 48) if caching else (0, 0)
+    trace = W.request_trace(name, 0, 24, max_prompt, max_gen, prefix_groups=groups[0],
+                            shared_tokens=groups[1])
     cache = PagedKVCache(layers, num_blocks, hkv, dim, dt, "cuda", fill_byte=H.POISON)
-    prod, orc = ContinuousBatcher(cache, width), OracleBatcher(num_blocks, width)
+    prod = ContinuousBatcher(cache, width, prefix_caching=caching)
+    orc = OracleBatcher(num_blocks, width, prefix_caching=caching)
     host = np.full(opool.pool_bytes(layers, num_blocks, 16, hkv, dim, dt), H.POISON, dtype=np.uint8)
     p6 = opool.view_pool(host, layers, num_blocks, 16, hkv, dim, dt)
     scale = float(np.float32(1.0 / np.sqrt(dim)))
     wsb = P.paged_attn_workspace_bytes(1, hq, dim, 1, 0)
     workspace = torch.empty(wsb // 4, dtype=torch.float32, device="cuda")
     pending = list(trace)
-    steps = preempted = copies = 0
+    steps = preempted = copies = reused = 0
     for it in range(1000):
         while pending and pending[0].arrival <= it:
             prod.submit(pending[0])
@@ -64,10 +71,11 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen):
             [(s.rid, s.sample, s.length) for s in batch]
         preempted += len(pre)
         copies += len(cps)
+        reused += sum(a[1] // 16 for a in adm)
 
         def prompt_kv(spec, layer):
-            return tuple(W.prompt_rows(name, 0, spec.rid, layer, w, spec.prompt_len, hkv, dim, dt,
-                                       "cuda") for w in ("k", "v"))
+            return tuple(W.keyed_prompt_rows(name, 0, spec, layer, w, hkv, dim, dt, "cuda")
+                         for w in ("k", "v"))
 
         def step_inputs(layer, n):
             return (W.step_rows(name, 0, it, layer, "q", n, hq, dim, dt, "cuda"),
@@ -76,10 +84,10 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen):
 
         outs = prod.execute(p, prompt_kv, step_inputs, hq, scale,
                             workspace=workspace if it % 2 else None)
-        for spec, sl in adm:
+        for spec, first, sl in adm:
             for layer in range(layers):
                 k, v = prompt_kv(spec, layer)
-                opool.append(p6, layer, H.raw16(k), H.raw16(v), dt, dt, sl)
+                opool.append(p6, layer, H.raw16(k[first:]), H.raw16(v[first:]), dt, dt, sl)
         if batch:
             steps += 1
             assert np.array_equal(p.slots, np.array(slots, dtype=np.int64))
@@ -99,8 +107,11 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen):
                 raise AssertionError(f"{name} it {it}: {bad.size} pool bytes differ")
         if not (pending or prod.running or prod.waiting):
             break
-    assert not prod.running and not pending and steps > 0 and copies > 0
+    assert not prod.running and not pending and steps > 0
+    assert copies > 0 or caching
     if num_blocks == 16:
         assert preempted > 0
-    say(f"{name}: {steps} steps, {copies} copies, {preempted} preemptions")
+    if caching:
+        assert reused > 0
+    say(f"{name}: {steps} steps, {copies} copies, {preempted} preemptions, {reused} cached blocks")
     cache.close()

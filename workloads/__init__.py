@@ -16,7 +16,8 @@ used here.
 """
 
 from .configs import CONFIGS, Config, scaled  # noqa: F401
-from .requests import RequestSpec, prompt_rows, request_trace, step_rows  # noqa: F401
+from .requests import (RequestSpec, keyed_prompt_rows, prompt_rows, request_trace,  # noqa: F401
+                       step_rows)
 from .gen import (  # noqa: F401
     context_lengths,
     fp8_scales,
