@@ -359,13 +359,15 @@ def block_copy_rate(cfg, pairs: int, iters: int, stream) -> dict:
             "frac_hbm": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def serving_rate(cfg, iters: int, stream) -> dict:
+def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False) -> dict:
     """The continuous-batching loop (ContinuousBatcher) over a seeded request
-    stream shaped like the workload: prompts drawn from its context lengths,
-    8 to 128 generated tokens, a third of the requests with 2-3 samples, and
-    a pool of the workload's size (so requests queue and, at times, are
-    preempted). Inputs are drawn before the timed region; the region holds
-    the bookkeeping (host) and the GPU work of every iteration."""
+    stream shaped like the workload: prompts of up to its longest context, 1 to
+    128 generated tokens, a third of the requests with 2-3 samples, 4 arrivals
+    per iteration and a pool of the workload's size (so requests queue and, at
+    times, are preempted). groups = (G, T): prompts in G prefix groups sharing
+    their first T tokens (a system prompt); caching: admit through the prefix
+    cache. Inputs are drawn before the timed region, which holds the
+    bookkeeping (host) and the GPU work of every iteration."""
     import torch
 
     import workloads as W
@@ -373,16 +375,13 @@ def serving_rate(cfg, iters: int, stream) -> dict:
 
     lens = W.context_lengths(cfg, 0)
     max_prompt, max_gen = int(lens.max()), 128
+    max_prompt = max(max_prompt, groups[1])
     nb = cfg.pool_blocks or blocks_needed(cfg, lens)
     width = -(-(max_prompt + max_gen) // BS)
     trace = W.request_trace(cfg.name + "_serve", 0, 4 * iters, max_prompt, max_gen,
-                            mean_gap=0.25)
-    rng = np.random.default_rng(0)
-    lo = int(lens.min())
-    trace = [W.RequestSpec(r.rid, r.arrival, int(rng.integers(lo, max_prompt + 1)),
-                           max(8, r.gen_len), r.samples) for r in trace]
+                            mean_gap=0.25, prefix_groups=groups[0], shared_tokens=groups[1])
     cache = PagedKVCache(cfg.layers, nb, cfg.kv_heads, cfg.head_dim, cfg.kv_dtype, "cuda")
-    loop = ContinuousBatcher(cache, width)
+    loop = ContinuousBatcher(cache, width, prefix_caching=caching)
     dt = cfg.src_dtype
     kp = W.normal((max_prompt, cfg.kv_heads, cfg.head_dim), dt, 1, "cuda")
     vp = W.normal((max_prompt, cfg.kv_heads, cfg.head_dim), dt, 2, "cuda")
@@ -405,7 +404,7 @@ def serving_rate(cfg, iters: int, stream) -> dict:
 
     pending = list(trace)
     host_s = 0.0
-    tokens = copies = preempted = 0
+    tokens = copies = preempted = prefill = reused = 0
     batches = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -418,6 +417,8 @@ def serving_rate(cfg, iters: int, stream) -> dict:
         loop.execute(plan, prompt_kv, step_inputs, cfg.q_heads, k_scale=k_scale,
                      v_scale=v_scale, workspace=workspace, stream=stream)
         tokens += len(plan.batch)
+        prefill += sum(int(a[2].size) for a in plan.admitted)
+        reused += sum(a[1] // BS for a in plan.admitted)
         batches.append(len(plan.batch))
         copies += len(plan.copy_src) if plan.copy_src is not None else 0
         preempted += len(plan.preempted)
@@ -429,6 +430,8 @@ def serving_rate(cfg, iters: int, stream) -> dict:
             "host_plan_us_per_iteration": round(host_s / iters * 1e6, 1),
             "mean_batch": round(float(np.mean(batches)), 2), "max_batch": int(max(batches)),
             "copies": copies, "preemptions": preempted, "pool_blocks": nb,
+            "prefix_caching": caching, "prefix_groups": list(groups),
+            "prefill_tokens": prefill, "cached_blocks_reused": reused,
             "requests_admitted": 4 * iters - len(pending) - len(loop.waiting)}
 
 
@@ -454,6 +457,11 @@ def main(argv=None):
     ap.add_argument("--serve", type=int, default=0, metavar="ITERS",
                     help="also run the continuous-batching loop for ITERS iterations on a "
                          "request stream of the workload's shape and report its rates")
+    ap.add_argument("--serve-prefix", default=None, metavar="GROUPS,TOKENS",
+                    help="serving stream with prompts in GROUPS prefix groups sharing their "
+                         "first TOKENS tokens")
+    ap.add_argument("--serve-caching", action="store_true",
+                    help="run the serving loop with prefix caching")
     ap.add_argument("--unfused", action="store_true",
                     help="run a step as kv_cache_append + paged_attn_decode instead of the "
                          "fused paged_attn_decode_append")
@@ -597,7 +605,8 @@ def main(argv=None):
         },
     }
     if args.serve > 0:
-        result["serving"] = serving_rate(cfg, args.serve, stream)
+        groups = tuple(int(x) for x in args.serve_prefix.split(",")) if args.serve_prefix else (0, 0)
+        result["serving"] = serving_rate(cfg, args.serve, stream, groups, args.serve_caching)
     if args.block_copy > 0:
         result["block_copy"] = block_copy_rate(cfg, args.block_copy, args.steps, stream)
     if not args.no_cpu_baseline:
