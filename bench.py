@@ -51,17 +51,17 @@ KERNEL_SOURCES = {
                                            "common.h")),
 }
 MEASURED_TRAFFIC = {  # workload -> counters of its decode kernel
-    "llama13b_layer": {  # FETCH 367,313.7 KiB x 1.99988 + WRITE 960.0 KiB
-        "kernel": "valu", "bytes": 753_195_730,
-        "sources_sha256": "aade371398348d39c3c1eda88f024714e41064af8896a021aa4b0ea186847666",
+    "llama13b_layer": {  # FETCH 367,317.2 KiB x 1.99988 + WRITE 960.0 KiB
+        "kernel": "valu", "bytes": 753_203_615,
+        "sources_sha256": "90b812eec938fafa75c0ce42c67f458fb9bb357b7492cce527d8d4940d8edccc",
         "summary": "profiles/decode_kernel_llama13b_layer.md"},
-    "longctx_fp8": {  # FETCH 715,690.3 KiB x 1.99998 + WRITE 5,754.9 KiB
-        "kernel": "valu", "bytes": 1_471_608_580,
-        "sources_sha256": "aade371398348d39c3c1eda88f024714e41064af8896a021aa4b0ea186847666",
+    "longctx_fp8": {  # FETCH 715,694.3 KiB x 1.99998 + WRITE 5,755.0 KiB
+        "kernel": "valu", "bytes": 1_471_616_875,
+        "sources_sha256": "90b812eec938fafa75c0ce42c67f458fb9bb357b7492cce527d8d4940d8edccc",
         "summary": "profiles/decode_kernel_longctx_fp8.md"},
-    "gqa_prefix": {  # streaming kernel: FETCH 408,802.7 KiB x 1.99994 + WRITE 12,218.5 KiB
-        "kernel": "balanced", "bytes": 849_715_881,
-        "sources_sha256": "bfbec6de60d3ef665a3b3db0b473e33a0f095acc01299f0a12f897e39f7b3872",
+    "gqa_prefix": {  # streaming kernel: FETCH 408,992.4 KiB x 1.99995 + WRITE 12,219.0 KiB
+        "kernel": "balanced", "bytes": 850_105_846,
+        "sources_sha256": "5536736bab3814e0938ac46d9ce49efaaa1b37f48b8c3c3434578b0796b867ea",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
 }
 
@@ -435,6 +435,48 @@ def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False) -> dict:
             "requests_admitted": 4 * iters - len(pending) - len(loop.waiting)}
 
 
+def window_rate(ws, window: int, steps: int, stream, fused: bool, full_us: float) -> dict:
+    """The step with a sliding window of `window` tokens on the same caches:
+    per layer, the decode call (storing the new tokens when fused) and the
+    reduce, timed back to back over the replicas like the full-context step.
+    Bytes are those of the attended tokens, min(L, window) per sequence."""
+    import torch
+
+    cfg = ws[0].cfg
+    esz = 1 if cfg.kv_dtype == "e4m3" else 2
+    per_token = cfg.kv_heads * cfg.head_dim * 2 * esz
+    attended = [int(np.minimum(w.lens, window).astype(np.int64).sum()) * per_token for w in ws]
+    for w in ws:
+        w.batch.window = window
+    try:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(len(ws)):  # warm-up
+            ws[i].step(stream=stream)
+        torch.cuda.synchronize()
+        a.record(stream)
+        n = 0
+        for i in range(steps):
+            w = ws[i % len(ws)]
+            for layer in range(cfg.layers):
+                if fused:
+                    w.decode_append(layer, stream)
+                else:
+                    w.decode(layer, stream)
+                w.reduce(stream)
+                n += 1
+        b.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        for w in ws:
+            w.batch.window = 0
+    us = a.elapsed_time(b) / n * 1e3
+    per_call = sum(attended) / len(attended)
+    return {"window": window, "attended_bytes_per_layer": int(per_call),
+            "us_per_layer": round(us, 3), "GB/s": round(per_call / (us * 1e-6) / 1e9, 2),
+            "seqs_per_s_per_layer": round(cfg.batch / (us * 1e-6), 1),
+            "full_context_us_per_layer": round(full_us, 3)}
+
+
 def P_workspace_bytes(cfg) -> int:
     import paged_kv_cache_450_amd as P
     return P.paged_attn_workspace_bytes(1, cfg.q_heads, cfg.head_dim, 1, 0)
@@ -462,6 +504,9 @@ def main(argv=None):
                          "first TOKENS tokens")
     ap.add_argument("--serve-caching", action="store_true",
                     help="run the serving loop with prefix caching")
+    ap.add_argument("--window", default=None, metavar="W[,W...]",
+                    help="also time the step with a sliding window of W tokens "
+                         "(paged_attn_decode_window) on the same caches")
     ap.add_argument("--unfused", action="store_true",
                     help="run a step as kv_cache_append + paged_attn_decode instead of the "
                          "fused paged_attn_decode_append")
@@ -604,6 +649,10 @@ def main(argv=None):
             "algorithmic_bytes": int(per_layer_unique),
         },
     }
+    if args.window:
+        result["window"] = [window_rate(ws, int(x), args.steps, stream, fused,
+                                        decode_us + reduce_us)
+                            for x in args.window.split(",")]
     if args.serve > 0:
         groups = tuple(int(x) for x in args.serve_prefix.split(",")) if args.serve_prefix else (0, 0)
         result["serving"] = serving_rate(cfg, args.serve, stream, groups, args.serve_caching)

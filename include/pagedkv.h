@@ -247,6 +247,18 @@ int32_t kv_pool_num_cached(const pkv_pool* pool);
  * the number of cached blocks (or -1 for NULL / bad arguments). */
 int32_t kv_pool_cached_list(const pkv_pool* pool, int32_t* out, int32_t cap);
 
+/* Sliding window: release the blocks of each sequence that lie wholly before
+ * its window ([P2] "vLLM 也不是银弹：...", third pitfall), so that a long
+ * sequence holds at most ceil(window / 16) + 1 blocks. For sequence i (host
+ * arrays): every block j with 16 * (j + 1) <= context_lens[i] - window whose
+ * table entry is not -1 loses one reference and its entry becomes -1.
+ * *num_released_out receives the number of references released.
+ * Errors: INVALID (NULL arrays, window <= 0, an id out of range), STATE (a
+ * free block). On error nothing changes. */
+pkv_status kv_seq_trim(pkv_pool* pool, int32_t num_seqs, int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t window,
+                       int32_t* num_released_out);
+
 /* Write each token's K and V into its slot of one layer ([P2]
  * "PagedAttention：...": the cache grows by slots as tokens are produced;
  * third pitfall: FP8 KV cache).
@@ -359,6 +371,27 @@ pkv_status paged_attn_decode_append(const pkv_pool* pool, int32_t layer, const v
                                     const float* k_scale, const float* v_scale,
                                     int32_t max_context_len, int32_t partition_size,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Sliding-window decode ([P2] "vLLM 也不是银弹：真实部署中的坑", third pitfall:
+ * for long contexts the pages point to sliding-window attention and to FP8 KV).
+ * paged_attn_decode (new_k == new_v == NULL) or paged_attn_decode_append
+ * (both given) where sequence i attends over its last `window` tokens only:
+ * positions [max(0, L_i - window), L_i). window == 0: the whole context.
+ * Table entries of blocks wholly before the window are never read (they may
+ * be -1, see kv_seq_trim). With partition_size > 0, partitions wholly before
+ * the window leave empty partials (l = 0), which paged_attn_reduce ignores.
+ * Every other argument, the output and the errors are those of the two
+ * calls; additional error: INVALID (negative window, only one of new_k /
+ * new_v given). */
+pkv_status paged_attn_decode_window(const pkv_pool* pool, int32_t layer, const void* new_k,
+                                    const void* new_v, int32_t src_dtype, const void* q,
+                                    int32_t q_dtype, void* out, const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, float scale,
+                                    const float* k_scale, const float* v_scale,
+                                    int32_t max_context_len, int32_t partition_size,
+                                    void* workspace, size_t workspace_bytes, int32_t window,
+                                    hipStream_t stream);
 
 /* Merge the partitions a partitioned paged_attn_decode left in workspace
  * into out (device [num_seqs][num_q_heads][head_dim] of out_dtype F16 or BF16):

@@ -193,6 +193,34 @@ class AllocatorModel:
                 slots.append(int(row[pos // bs]) * bs + pos % bs)
         return slots, copies
 
+    def trim(self, tables, lens, window: int) -> int:
+        """Sliding window: release every block of sequence i that lies wholly
+        before its window (16 * (j + 1) <= lens[i] - window) and whose entry
+        is not -1; the entry becomes -1. Returns the references released."""
+        if window <= 0 or len(tables) != len(lens):
+            raise AllocError(INVALID, "bad window or lengths")
+        need = {}
+        for row, n in zip(tables, lens):
+            for j in range(min(max(0, int(n) - window) // self.block_size, len(row))):
+                b = int(row[j])
+                if b == -1:
+                    continue
+                if not 0 <= b < self.num_blocks:
+                    raise AllocError(INVALID, "block id out of range")
+                need[b] = need.get(b, 0) + 1
+        for b, c in need.items():
+            if self.ref[b] < c:
+                raise AllocError(STATE, "releasing a block more times than it is held")
+        released = 0
+        for row, n in zip(tables, lens):
+            for j in range(min(max(0, int(n) - window) // self.block_size, len(row))):
+                if int(row[j]) == -1:
+                    continue
+                self._release(int(row[j]))
+                row[j] = -1
+                released += 1
+        return released
+
     # -- prefix caching ----------------------------------------------------------
     def register(self, keys, ids) -> int:
         """Name live blocks by content keys; returns how many pairs were taken."""

@@ -12,6 +12,12 @@ the plain definition of attention on the gathered, logically contiguous K/V:
 for every query head h, with kv head g = h // (Hq / Hkv) (contiguous query
 head groups share one kv head; reading taken where the pages are silent).
 
+Sliding window ([P2] "vLLM 也不是银弹：...", third pitfall, names it as a
+long-context remedy; the form is the usual one, reading taken): with a window
+of W tokens a sequence of length L attends over positions [max(0, L - W), L)
+only, i.e. the same definition on the last W tokens; the blocks wholly before
+them are not read at all (their table entries may be gone).
+
 Split-K (not on the pages; the long-context path of this library): the
 context is cut into partitions of PS tokens; partition p covers tokens
 [p*PS, min((p+1)*PS, L)) and yields m_p = max s, l_p = sum exp(s - m_p) and
@@ -51,6 +57,21 @@ def gather(pool6: np.ndarray, layer: int, table_row, context_len: int):
     return out[0], out[1]
 
 
+def gather_range(pool6: np.ndarray, layer: int, table_row, lo: int, hi: int):
+    """Raw K and V of positions [lo, hi) of one sequence: two [hi - lo, Hkv, D]
+    arrays. Reads only the ids of blocks lo // BS .. ceil(hi / BS) - 1."""
+    block_size = pool6.shape[4]
+    j0, j1 = lo // block_size, -(-hi // block_size)
+    ids = np.asarray(table_row[j0:j1], dtype=np.int64)
+    out = []
+    for c in (0, 1):
+        tiles = pool6[layer, c, ids]  # [nb, Hkv, BS, D]
+        seq = tiles.transpose(0, 2, 1, 3).reshape(ids.size * block_size,
+                                                  tiles.shape[1], tiles.shape[3])
+        out.append(seq[lo - j0 * block_size: hi - j0 * block_size])
+    return out[0], out[1]
+
+
 def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
     """softmax(scale * q K^T) V per query head.
 
@@ -71,17 +92,22 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndar
 
 
 def paged_decode(pool6, layer, q_f64, block_tables, context_lens, scale, kv_dtype,
-                 k_scale=None, v_scale=None) -> np.ndarray:
+                 k_scale=None, v_scale=None, window: int = 0) -> np.ndarray:
     """Decode attention for a batch: out[i] = attend(q[i], K_i, V_i) in float64.
 
     q_f64: [B, Hq, D] float64. block_tables: [B, max_blocks] ints.
-    context_lens: [B]; a sequence of length 0 gives zeros.
+    context_lens: [B]; a sequence of length 0 gives zeros. window > 0: each
+    sequence attends over its last `window` positions only.
     """
     num_seqs = q_f64.shape[0]
     out = np.zeros(q_f64.shape, dtype=np.float64)
     for i in range(num_seqs):
         length = int(context_lens[i])
-        k_raw, v_raw = gather(pool6, layer, block_tables[i], length)
+        if window > 0:
+            k_raw, v_raw = gather_range(pool6, layer, block_tables[i], max(0, length - window),
+                                        length)
+        else:
+            k_raw, v_raw = gather(pool6, layer, block_tables[i], length)
         k = kv_to_f64(k_raw, kv_dtype, k_scale)
         v = kv_to_f64(v_raw, kv_dtype, v_scale)
         out[i] = attend(q_f64[i], k, v, scale)

@@ -80,6 +80,9 @@ def _load():
         "kv_prefix_register": (i32, [vp, ctypes.POINTER(ctypes.c_uint64), p_i32, i32, p_i32]),
         "kv_prefix_acquire": (i32, [vp, ctypes.POINTER(ctypes.c_uint64), i32, p_i32, p_i32]),
         "kv_pool_num_cached": (i32, [vp]),
+        "kv_seq_trim": (i32, [vp, i32, p_i32, i32, p_i32, i32, p_i32]),
+        "paged_attn_decode_window": (i32, [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, i32,
+                                           i32, f32, vp, vp, i32, i32, vp, sz, i32, vp]),
         "kv_pool_cached_list": (i32, [vp, p_i32, i32]),
         "kv_cache_append": (i32, [vp, i32, vp, vp, i32, vp, i32, vp, vp, vp]),
         "paged_attn_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
@@ -254,6 +257,21 @@ def kv_seq_extend_cow(pool, block_tables: np.ndarray, cur_lens, new_lens):
     return slots, src[:n.value].copy(), dst[:n.value].copy()
 
 
+def kv_seq_trim(pool, block_tables: np.ndarray, context_lens, window: int) -> int:
+    """Release the blocks wholly before each sequence's window (entries become
+    -1 in place); returns the number of references released."""
+    bt = _host_i32(block_tables, writable=True)
+    if bt.ndim != 2:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]")
+    lens = _host_i32(context_lens).reshape(-1)
+    if lens.size != bt.shape[0]:
+        raise ValueError("one length per table row")
+    n = ctypes.c_int32(0)
+    _check(lib.kv_seq_trim(pool, bt.shape[0], _i32_ptr(bt), bt.shape[1], _i32_ptr(lens), window,
+                           ctypes.byref(n)))
+    return n.value
+
+
 # -------------------------------------------------------------- kernels ----
 def _torch():
     import torch
@@ -366,6 +384,30 @@ def paged_attn_decode_append(pool, layer: int, new_k, new_v, q, out, block_table
         _ptr(out), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), q.shape[0],
         q.shape[1], float(scale), _ptr(k_scale), _ptr(v_scale), max_context_len, partition_size,
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def paged_attn_decode_window(pool, layer: int, q, out, block_tables, context_lens, scale: float,
+                             max_context_len: int, window: int, partition_size: int = 0,
+                             workspace=None, k_scale=None, v_scale=None, new_k=None, new_v=None,
+                             stream=None) -> None:
+    """Sliding-window decode: each sequence attends over its last `window` tokens
+    (0: all); with new_k / new_v the step also stores the new tokens."""
+    torch = _torch()
+    _dev(q, "q"); _dev(out, "out"); _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32); _dev(workspace, "workspace")
+    _dev(k_scale, "k_scale", torch.float32); _dev(v_scale, "v_scale", torch.float32)
+    _dev(new_k, "new_k"); _dev(new_v, "new_v")
+    if q.dim() != 3 or block_tables.dim() != 2:
+        raise ValueError("q must be [B, Hq, D] and block_tables [B, W]")
+    if out is not None and (out.shape != q.shape or out.dtype != q.dtype):
+        raise ValueError("out must match q")
+    src = _dtype_code(new_k) if new_k is not None else _dtype_code(q)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.paged_attn_decode_window(
+        pool, layer, _ptr(new_k), _ptr(new_v), src, _ptr(q), _dtype_code(q), _ptr(out),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), q.shape[0], q.shape[1],
+        float(scale), _ptr(k_scale), _ptr(v_scale), max_context_len, partition_size,
+        _ptr(workspace), ws_bytes, window, _stream(stream)))
 
 
 def paged_attn_reduce(workspace, out, context_lens, max_context_len: int, partition_size: int,

@@ -224,7 +224,7 @@ pkv_status decode_impl(const char* fn, const pkv_pool* pool, int32_t layer, cons
                        int32_t num_q_heads, float scale, const float* k_scale,
                        const float* v_scale, int32_t max_context_len, int32_t partition_size,
                        void* workspace, size_t workspace_bytes, const void* new_k,
-                       const void* new_v, hipStream_t stream) {
+                       const void* new_v, int32_t window, hipStream_t stream) {
     using pkv::fail;
     if (pool == nullptr) return fail(PKV_ERR_INVALID, "%s: pool is NULL", fn);
     const pkv_pool_desc& d = pool->desc;
@@ -251,6 +251,7 @@ pkv_status decode_impl(const char* fn, const pkv_pool* pool, int32_t layer, cons
                     partition_size);
     if (!std::isfinite(scale))
         return fail(PKV_ERR_INVALID, "%s: scale is not finite", fn);
+    if (window < 0) return fail(PKV_ERR_INVALID, "%s: negative window %d", fn, window);
     if (max_blocks_per_seq > (1 << 26))
         return fail(PKV_ERR_INVALID, "%s: max_blocks_per_seq too large", fn);
     if (num_seqs == 0) return PKV_OK;
@@ -281,6 +282,7 @@ pkv_status decode_impl(const char* fn, const pkv_pool* pool, int32_t layer, cons
     prm.scale_log2 = scale * pkv::dev::kLog2e;
     prm.new_k = static_cast<const uint8_t*>(new_k);
     prm.new_v = static_cast<const uint8_t*>(new_v);
+    prm.window = window;
 
     uint32_t parts = 1;
     if (partition_size > 0) {
@@ -379,7 +381,7 @@ extern "C" pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, con
     return decode_impl("paged_attn_decode", pool, layer, q, q_dtype, out, block_tables,
                        max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale, k_scale,
                        v_scale, max_context_len, partition_size, workspace, workspace_bytes,
-                       nullptr, nullptr, stream);
+                       nullptr, nullptr, 0, stream);
 }
 
 extern "C" pkv_status paged_attn_decode_append(
@@ -400,5 +402,28 @@ extern "C" pkv_status paged_attn_decode_append(
     return decode_impl(fn, pool, layer, q, q_dtype, out, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_q_heads, scale, k_scale, v_scale,
                        max_context_len, partition_size, workspace, workspace_bytes, new_k, new_v,
-                       stream);
+                       0, stream);
+}
+
+extern "C" pkv_status paged_attn_decode_window(
+    const pkv_pool* pool, int32_t layer, const void* new_k, const void* new_v, int32_t src_dtype,
+    const void* q, int32_t q_dtype, void* out, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, float scale, const float* k_scale, const float* v_scale,
+    int32_t max_context_len, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    int32_t window, hipStream_t stream) {
+    using pkv::fail;
+    const char* fn = "paged_attn_decode_window";
+    if ((new_k == nullptr) != (new_v == nullptr))
+        return fail(PKV_ERR_INVALID, "%s: new_k and new_v must both be given or both be NULL", fn);
+    if (new_k != nullptr) {
+        if (src_dtype != q_dtype)
+            return fail(PKV_ERR_INVALID, "%s: the new tokens' dtype must equal the q dtype", fn);
+        if ((reinterpret_cast<uintptr_t>(new_k) | reinterpret_cast<uintptr_t>(new_v)) % 16 != 0)
+            return fail(PKV_ERR_INVALID, "%s: new_k and new_v must be 16-byte aligned", fn);
+    }
+    return decode_impl(fn, pool, layer, q, q_dtype, out, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, k_scale, v_scale,
+                       max_context_len, partition_size, workspace, workspace_bytes, new_k, new_v,
+                       window, stream);
 }

@@ -29,19 +29,30 @@ using namespace pkv::dev;
 // per split, which costs more than the launch).
 
 // Issue-side walker over the tiles of the batch in (sequence, kv head, block)
-// order, holding the block ids of the current sequence's table row: blocks
-// 0..127 of the row stay in registers for the row's other heads, later blocks
-// rotate through a second pair of 64-id chunks.
+// order, holding the block ids of the current sequence's table row: the first
+// 128 blocks from the window's start stay in registers for the row's other
+// heads, later blocks rotate through a second pair of 64-id chunks. Without a
+// sliding window a sequence's tiles are its blocks 0 .. nblk-1; with one,
+// jlo .. nblk-1.
 struct TileWalk {
-    int s, g, j, nblk;   // current tile: sequence, kv head, block
+    int s, g, j, nblk;   // current tile: sequence, kv head, block; blocks end at nblk
+    int jlo, lo;         // first block read, first token attended (sliding window)
     int L;               // tokens of sequence s as read here
-    int64_t a_sg;        // global index of tile (s, g, 0)
+    int64_t a_sg;        // global index of tile (s, g, jlo)
     int chunk;           // sequences 64*chunk .. +63 have their lengths in lens
     int lens;            // per lane: tokens of sequence 64*chunk + lane
-    int row0_a, row0_b;  // ids of blocks 0..63 and 64..127 of row s (per lane)
+    int rbase;           // jlo rounded down to 64: row0_* start there
+    int row0_a, row0_b;  // ids of blocks rbase .. +63 and +64 .. +127 of row s (per lane)
     int ids_a, ids_b;    // ids of blocks base .. base+127 (per lane, two chunks)
     int base;
 };
+
+__device__ __forceinline__ void walk_set_seq(const DecodeParams& p, TileWalk& t, int L) {
+    t.L = L;
+    t.nblk = (L + 15) >> 4;
+    t.lo = window_lo(p, L);
+    t.jlo = t.lo >> 4;
+}
 
 __device__ __forceinline__ int walk_row_ids(const DecodeParams& p, const TileWalk& t, int j0,
                                             int lane) {
@@ -50,11 +61,12 @@ __device__ __forceinline__ int walk_row_ids(const DecodeParams& p, const TileWal
 }
 
 __device__ __forceinline__ void walk_enter_row(const DecodeParams& p, TileWalk& t, int lane) {
-    t.row0_a = walk_row_ids(p, t, 0, lane);
-    t.row0_b = walk_row_ids(p, t, 64, lane);
+    t.rbase = t.jlo & ~63;
+    t.row0_a = walk_row_ids(p, t, t.rbase, lane);
+    t.row0_b = walk_row_ids(p, t, t.rbase + 64, lane);
     t.base = t.j & ~63;
-    t.ids_a = t.base == 0 ? t.row0_a : walk_row_ids(p, t, t.base, lane);
-    t.ids_b = t.base == 0 ? t.row0_b : walk_row_ids(p, t, t.base + 64, lane);
+    t.ids_a = t.base == t.rbase ? t.row0_a : walk_row_ids(p, t, t.base, lane);
+    t.ids_b = t.base == t.rbase ? t.row0_b : walk_row_ids(p, t, t.base + 64, lane);
 }
 
 // Block id of the current tile.
@@ -70,10 +82,10 @@ __device__ __forceinline__ int walk_id(const DecodeParams& p, TileWalk& t, int l
 // Step to the next tile. Returns true when it starts a new segment.
 __device__ __forceinline__ void walk_advance(const DecodeParams& p, TileWalk& t, int lane) {
     if (++t.j < t.nblk) return;
-    t.j = 0;
-    t.a_sg += t.nblk;
-    if (++t.g < p.num_kv_heads) {  // same row, next head: blocks 0..127 are at hand
-        t.base = 0;
+    t.j = t.jlo;
+    t.a_sg += t.nblk - t.jlo;
+    if (++t.g < p.num_kv_heads) {  // same row, next head: its first 128 blocks are at hand
+        t.base = t.rbase;
         t.ids_a = t.row0_a;
         t.ids_b = t.row0_b;
         return;
@@ -89,18 +101,18 @@ __device__ __forceinline__ void walk_advance(const DecodeParams& p, TileWalk& t,
             const int jj = t.chunk * 64 + lane;
             t.lens = jj < p.num_seqs ? seq_tokens(p, jj) : 0;
         }
-        t.L = __builtin_amdgcn_readlane(t.lens, t.s & 63);
-        t.nblk = (t.L + 15) >> 4;
+        walk_set_seq(p, t, __builtin_amdgcn_readlane(t.lens, t.s & 63));
     } while (t.nblk == 0 && t.s + 1 < p.num_seqs);
+    t.j = t.jlo;
     walk_enter_row(p, t, lane);
 }
 
 // Ring-slot description of an issued tile (all wave-uniform).
 struct SlotInfo {
-    int nvalid;       // context tokens in the tile (0 past the end of the range)
+    int nvalid, nlo;  // attended tokens of the tile: [nlo, nvalid) (nvalid 0 past the range)
     int flags;        // bit 0: first tile of a segment, bit 1: last tile of a segment
-    int s, g, nblk;   // its segment's sequence, kv head and block count
-    int64_t a_sg;     // global index of tile (s, g, 0)
+    int s, g, ntiles; // its segment's sequence, kv head and tile count
+    int64_t a_sg;     // global index of the segment's first tile
 };
 
 template <int D>
@@ -140,10 +152,10 @@ struct ValuMath {
         for (int e = 0; e < kEpl; ++e) x.st.o[0][e] = 0.0f;
     }
     template <bool kPartial>
-    __device__ static void consume(State& x, const TileT& t, int nvalid, const QT& q, float sscale,
-                                   int lane) {
+    __device__ static void consume(State& x, const TileT& t, int nvalid, int nlo, const QT& q,
+                                   float sscale, int lane) {
         const QT qs[1] = {q};
-        consume_tile<KV, D, 1, kPartial>(x.st, t, nvalid, qs, sscale, lane / kLpt);
+        consume_tile<KV, D, 1, kPartial>(x.st, t, nvalid, nlo, qs, sscale, lane / kLpt);
     }
     // Merge the rows of the wave; afterwards lanes of row 0 hold dims
     // col*EPL .. +EPL, and every lane holds m and l.
@@ -242,10 +254,10 @@ struct MfmaMath {
         x.lsum = 0.0f;
     }
     template <bool kPartial>
-    __device__ static void consume(State& x, const TileT& t, int nvalid, const QT&, float sscale,
-                                   int lane) {
-        mfma_consume<KV, D, kPartial>(t, nvalid, QLds<D>{x.qlds}, x.o, x.m, x.lsum, sscale, x.stage,
-                                      lane);
+    __device__ static void consume(State& x, const TileT& t, int nvalid, int nlo, const QT&,
+                                   float sscale, int lane) {
+        mfma_consume<KV, D, kPartial>(t, nvalid, nlo, QLds<D>{x.qlds}, x.o, x.m, x.lsum, sscale,
+                                      x.stage, lane);
     }
     __device__ static void finish(State& x) {
         x.lsum += __shfl_xor(x.lsum, 16);
@@ -292,7 +304,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
     int64_t total = 0;
     for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
         const int jj = c0 + lane;
-        total += wave_sum(jj < p.num_seqs ? (seq_tokens(p, jj) + 15) >> 4 : 0);
+        total += wave_sum(jj < p.num_seqs ? window_blocks(p, seq_tokens(p, jj)) : 0);
     }
     total *= p.num_kv_heads;
     // R non-empty ranges: with fewer tiles than waves the surplus waves idle,
@@ -311,7 +323,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
         for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {  // t0 < total: some chunk holds it
             const int jj = c0 + lane;
             const int len = jj < p.num_seqs ? seq_tokens(p, jj) : 0;
-            const int tiles = ((len + 15) >> 4) * p.num_kv_heads;
+            const int tiles = window_blocks(p, len) * p.num_kv_heads;
             const int incl = wave_incl_scan(tiles, lane);
             const uint64_t hit = __ballot(jj < p.num_seqs && carry + incl > t0);
             if (hit) {
@@ -319,13 +331,13 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
                 tw.s = c0 + ln;
                 tw.chunk = c0 >> 6;
                 tw.lens = len;
-                tw.L = __builtin_amdgcn_readlane(len, ln);
-                tw.nblk = (tw.L + 15) >> 4;
+                walk_set_seq(p, tw, __builtin_amdgcn_readlane(len, ln));
+                const int nt = tw.nblk - tw.jlo;  // tiles per head
                 const int64_t a_s = carry + __builtin_amdgcn_readlane(incl - tiles, ln);
                 const int64_t off = t0 - a_s;
-                tw.g = static_cast<int>(off / tw.nblk);
-                tw.j = static_cast<int>(off % tw.nblk);
-                tw.a_sg = a_s + static_cast<int64_t>(tw.g) * tw.nblk;
+                tw.g = static_cast<int>(off / nt);
+                tw.j = tw.jlo + static_cast<int>(off % nt);
+                tw.a_sg = a_s + static_cast<int64_t>(tw.g) * nt;
                 found = true;
                 break;
             }
@@ -355,27 +367,29 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
     auto issue = [&](typename M::TileT& tt, SlotInfo& info, typename M::QT& qq, int kn) {
         if (kn >= n) {
             info.nvalid = 0;
+            info.nlo = 0;
             info.flags = 0;
-            const TileRef r = tile_ref(p, p.k_plane, p.v_plane, bstride, M::kTB, -1, 0, 0);
+            const TileRef r = tile_ref(p, p.k_plane, p.v_plane, bstride, M::kTB, -1, 0, 0, 0);
             M::issue(tt, r, lane);
             return;
         }
         if (kn > 0) walk_advance(p, tw, lane);
-        const bool first = kn == 0 || tw.j == 0;
+        const bool first = kn == 0 || tw.j == tw.jlo;
         const bool last = kn == n - 1 || tw.j == tw.nblk - 1;
         info.flags = (first ? 1 : 0) | (last ? 2 : 0);
         info.s = tw.s;
         info.g = tw.g;
-        info.nblk = tw.nblk;
+        info.ntiles = tw.nblk - tw.jlo;
         info.a_sg = tw.a_sg;
         if constexpr (M::kPrefetchQ) {
             if (first) M::fetch_q(p, qq, tw.s, tw.g, lane);
         }
         const uint8_t* kpl = p.k_plane + static_cast<size_t>(tw.g) * M::kTB;
         const uint8_t* vpl = p.v_plane + static_cast<size_t>(tw.g) * M::kTB;
-        const TileRef r =
-            tile_ref(p, kpl, vpl, bstride, M::kTB, walk_id(p, tw, lane), tw.j * 16, tw.L);
+        const TileRef r = tile_ref(p, kpl, vpl, bstride, M::kTB, walk_id(p, tw, lane), tw.j * 16,
+                                   tw.L, tw.lo);
         info.nvalid = r.nvalid;
+        info.nlo = r.nlo;
         M::issue(tt, r, lane);
     };
 
@@ -391,14 +405,14 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
                 else
                     M::fetch_q_lds(p, st, cur.s, cur.g, lane);
             }
-            if (cur.nvalid == 16)
-                M::template consume<false>(st, tr[x], 16, q, p.scale_log2, lane);
+            if (cur.nvalid == 16 && cur.nlo == 0)
+                M::template consume<false>(st, tr[x], 16, 0, q, p.scale_log2, lane);
             else if (cur.nvalid > 0)
-                M::template consume<true>(st, tr[x], cur.nvalid, q, p.scale_log2, lane);
+                M::template consume<true>(st, tr[x], cur.nvalid, cur.nlo, q, p.scale_log2, lane);
             if (cur.flags & 2) {
                 // End of a segment: write the output, or the partial of a split context.
                 M::finish(st);
-                if (cur.a_sg >= t0 && cur.a_sg + cur.nblk <= t1) {
+                if (cur.a_sg >= t0 && cur.a_sg + cur.ntiles <= t1) {
                     M::store_out(p, st, cur.s, cur.g, lane);
                 } else {  // split context: slot 0 if it began before this range, else 1
                     const int slot = (cur.a_sg <= t0) ? 0 : 1;
@@ -423,14 +437,14 @@ template <int KV, int D, int G>
 __global__ __launch_bounds__(256) void balanced_merge_kernel(const DecodeParams p) {
     constexpr int SS = SlotGeoB<D>::kStride;
     const int g = blockIdx.x, s = blockIdx.y, lane = threadIdx.x & 63;
-    int64_t total = 0, before = 0;  // blocks of the batch, and of sequences < s
+    int64_t total = 0, before = 0;  // tiles per head of the batch, and of sequences < s
     for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
         const int jj = c0 + lane;
-        const int nb = jj < p.num_seqs ? (seq_tokens(p, jj) + 15) >> 4 : 0;
+        const int nb = jj < p.num_seqs ? window_blocks(p, seq_tokens(p, jj)) : 0;
         total += wave_sum(nb);
         before += wave_sum(jj < s ? nb : 0);
     }
-    const int nblk = (seq_tokens(p, s) + 15) >> 4;
+    const int nblk = window_blocks(p, seq_tokens(p, s));
     uint16_t* out = static_cast<uint16_t*>(p.out) +
                     (static_cast<size_t>(s) * p.num_q_heads + g * G) * D;
     const int t = threadIdx.x;

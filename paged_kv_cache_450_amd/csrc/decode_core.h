@@ -44,7 +44,18 @@ struct DecodeParams {
     // [B][Hkv][D] of the 16-bit source dtype (the q dtype).
     const uint8_t* new_k;
     const uint8_t* new_v;
+    int32_t window;           // > 0: attend over the last `window` tokens only
 };
+
+// First token a sequence of L tokens attends over (sliding window).
+__device__ __forceinline__ int window_lo(const DecodeParams& p, int L) {
+    return p.window > 0 ? max(0, L - p.window) : 0;
+}
+
+// Blocks a decode reads of a sequence of L tokens: [window_lo / 16, ceil(L / 16)).
+__device__ __forceinline__ int window_blocks(const DecodeParams& p, int L) {
+    return ((L + 15) >> 4) - (window_lo(p, L) >> 4);
+}
 
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
 // return zeros without touching memory, so a tile that is not part of the
@@ -157,13 +168,14 @@ __device__ __forceinline__ void combine_waves(const DecodeParams& p, int s, int 
     }
 }
 
-// The work of one wave: sequence s, its length L as this kernel reads it, and
-// its tiles, the logical blocks b0 + w + k*NW for k < n (the partition's
-// blocks dealt round robin to the NW waves of the workgroup). newk: the index
-// of the tile holding the token a fused append writes (position L - 1), when
-// this wave reads it; else -1.
+// The work of one wave: sequence s, its length L as this kernel reads it, the
+// first token it attends over (lo, > 0 with a sliding window), and its tiles,
+// the logical blocks b0 + w + k*NW for k < n (the partition's blocks from the
+// window's first on, dealt round robin to the NW waves of the workgroup).
+// newk: the index of the tile holding the token a fused append writes
+// (position L - 1), when this wave reads it; else -1.
 struct WaveWork {
-    int s, L, b0, n, newk;
+    int s, L, lo, b0, n, newk;
 };
 
 // Grid (kv head, sequence, partition), kv head fastest. Workgroups are dealt
@@ -187,13 +199,16 @@ __device__ __forceinline__ bool locate_work(const DecodeParams& p, int g, int pa
         L = min(Lr, p.max_blocks * 16);
     }
     const int nblk = (L + 15) >> 4;
-    int b0 = 0, b1 = nblk;
+    const int lo = window_lo(p, L);
+    int b0 = lo >> 4, b1 = nblk;
     if (p.blocks_per_part > 0) {
-        b0 = part * p.blocks_per_part;
-        b1 = min(b0 + p.blocks_per_part, nblk);
-        if (b0 >= nblk) {
-            // No tokens in this partition. If the reduce will still read it
-            // (a table row narrower than the context), leave an empty partial.
+        const int pb0 = part * p.blocks_per_part;
+        b1 = min(pb0 + p.blocks_per_part, nblk);
+        b0 = max(pb0, lo >> 4);
+        if (b0 >= b1) {
+            // No tokens in this partition (past the table's reach, or before
+            // the window). If the reduce will still read it, leave an empty
+            // partial.
             const int ps = p.blocks_per_part * 16;
             if (part < (Lr + ps - 1) / ps) {
                 for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
@@ -210,6 +225,7 @@ __device__ __forceinline__ bool locate_work(const DecodeParams& p, int g, int pa
     const int span = b1 - b0;
     ww.s = s;
     ww.L = L;
+    ww.lo = lo;
     ww.b0 = b0 + w;
     ww.n = span > w ? (span - w + NW - 1) / NW : 0;
     // The fused append writes position L - 1 only when the context is whole
@@ -251,17 +267,18 @@ struct BlockIds {
     }
 };
 
-// Descriptors of the K and V tiles of block `id` for kv head g, and the number
-// of context tokens in it. An id outside the pool, or past the end (-1), gives
-// size-0 descriptors and no tokens.
+// Descriptors of the K and V tiles of block `id` for kv head g, and the
+// tile's attended tokens [nlo, nvalid): the context ends before token nvalid,
+// a sliding window starts at token nlo (0 without one). An id outside the pool,
+// or past the end (-1), gives size-0 descriptors and no tokens.
 struct TileRef {
     __amdgpu_buffer_rsrc_t k, v;
-    int nvalid;
+    int nvalid, nlo;
 };
 
 __device__ __forceinline__ TileRef tile_ref(const DecodeParams& p, const uint8_t* kpl,
                                             const uint8_t* vpl, size_t bstride, int tile_bytes,
-                                            int id, int first_token, int L) {
+                                            int id, int first_token, int L, int lo) {
     const bool ok = static_cast<uint32_t>(id) < static_cast<uint32_t>(p.num_blocks);
     const size_t off = static_cast<size_t>(ok ? id : 0) * bstride;
     const int bytes = ok ? tile_bytes : 0;
@@ -269,6 +286,7 @@ __device__ __forceinline__ TileRef tile_ref(const DecodeParams& p, const uint8_t
     t.k = tile_rsrc(kpl + off, bytes);
     t.v = tile_rsrc(vpl + off, bytes);
     t.nvalid = ok ? min(L - first_token, 16) : 0;
+    t.nlo = ok ? min(max(lo - first_token, 0), 16) : 0;
     return t;
 }
 

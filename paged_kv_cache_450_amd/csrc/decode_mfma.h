@@ -83,8 +83,10 @@ struct QLds {
     }
 };
 
+// Attended tokens of the tile: [nlo, nvalid) (kPartial: the masked form).
 template <int KV, int D, bool kPartial, class QSrc>
-__device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid, const QSrc& qsrc,
+__device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid, int nlo,
+                                             const QSrc& qsrc,
                                              f32x4_t (&o)[MfmaGeo<D>::kNd], float& m, float& lsum,
                                              float sscale, uint8_t* stage, int lane) {
     using Gm = MfmaGeo<D>;
@@ -98,7 +100,8 @@ __device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid, c
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         sc[r] = sacc[r] * sscale;
-        if constexpr (kPartial) sc[r] = (4 * kg + r < nvalid) ? sc[r] : -INFINITY;
+        if constexpr (kPartial)
+            sc[r] = (4 * kg + r < nvalid && 4 * kg + r >= nlo) ? sc[r] : -INFINITY;
     }
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -148,7 +151,7 @@ __device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid, c
         const int tok = i * (64 / kLanesPerRow) + lane / kLanesPerRow;
         uint4 v = t.v[i];
         if constexpr (kPartial) {
-            if (tok >= nvalid) v = make_uint4(0u, 0u, 0u, 0u);
+            if (tok >= nvalid || tok < nlo) v = make_uint4(0u, 0u, 0u, 0u);
         }
         *reinterpret_cast<uint4*>(stage + tok * Gm::kPitch + (lane % kLanesPerRow) * 16) = v;
     }
@@ -218,10 +221,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
     const int voff = lane * 16;                     // + 1024*i: natural rows
 
     MfmaTile<D> t[NBUF];
-    int nv[NBUF];
-    auto issue = [&](MfmaTile<D>& tt, int& nvalid, int kn) {
-        const TileRef r = tile_ref(p, kpl, vpl, bstride, TB, ids.next(kn), (ww.b0 + kn * NW) * 16, L);
+    int nv[NBUF], nl[NBUF];
+    auto issue = [&](MfmaTile<D>& tt, int& nvalid, int& nlo, int kn) {
+        const TileRef r = tile_ref(p, kpl, vpl, bstride, TB, ids.next(kn), (ww.b0 + kn * NW) * 16,
+                                   L, ww.lo);
         nvalid = r.nvalid;
+        nlo = r.nlo;
 #pragma unroll
         for (int c = 0; c < NK; ++c) tt.k[c] = rsrc_load16(r.k, koff + 64 * c);
 #pragma unroll
@@ -229,15 +234,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
     };
 
 #pragma unroll
-    for (int x = 0; x < NBUF; ++x) issue(t[x], nv[x], x);
+    for (int x = 0; x < NBUF; ++x) issue(t[x], nv[x], nl[x], x);
     for (int k0 = 0; k0 < n; k0 += NBUF) {
 #pragma unroll
         for (int x = 0; x < NBUF; ++x) {
-            if (nv[x] == 16)
-                mfma_consume<KV, D, false>(t[x], 16, qr, o, m, lsum, sscale, stage, lane);
+            if (nv[x] == 16 && nl[x] == 0)
+                mfma_consume<KV, D, false>(t[x], 16, 0, qr, o, m, lsum, sscale, stage, lane);
             else
-                mfma_consume<KV, D, true>(t[x], nv[x], qr, o, m, lsum, sscale, stage, lane);
-            issue(t[x], nv[x], k0 + x + NBUF);
+                mfma_consume<KV, D, true>(t[x], nv[x], nl[x], qr, o, m, lsum, sscale, stage, lane);
+            issue(t[x], nv[x], nl[x], k0 + x + NBUF);
         }
     }
 

@@ -125,15 +125,17 @@ struct SoftmaxState {
     float o[G][Geo<KV, D>::kEpl];     // running sum of exp2(s - m) * v, this lane's dims
 };
 
-// Fold one tile into the lane's online-softmax state. nvalid = number of
-// leading tokens of the tile that belong to the context (0..16). kPartial
-// selects the masked form, needed only when nvalid < 16 (the last block of a
-// context, or a tile outside the context): tokens past nvalid get score -inf
-// and their V bytes, which may be stale or NaN, are replaced by zeros.
+// Fold one tile into the lane's online-softmax state. The tile's attended
+// tokens are [nlo, nvalid) (nvalid: the context ends; nlo: a sliding window
+// starts). kPartial selects the masked form, needed only when that is not the
+// whole tile (the last block of a context, the window's first block, or a
+// tile outside the context): other tokens get score -inf and their V bytes,
+// which may be stale or NaN, are replaced by zeros.
 template <int KV, int D, int G, bool kPartial>
 __device__ __forceinline__ void consume_tile(SoftmaxState<KV, D, G>& st, const Tile<KV, D>& t,
-                                             int nvalid, const QSlice<KV, D> (&qs)[G],
-                                             float sscale, int row) {
+                                             int nvalid, int nlo,
+                                             const QSlice<KV, D> (&qs)[G], float sscale,
+                                             int row) {
     using Gm = Geo<KV, D>;
     constexpr int EPL = Gm::kEpl, LPT = Gm::kLpt, TPI = Gm::kTpi, NLD = Gm::kNld;
     float sc[G][NLD];
@@ -147,7 +149,8 @@ __device__ __forceinline__ void consume_tile(SoftmaxState<KV, D, G>& st, const T
         for (int h = 0; h < G; ++h) sc[h][i] = group_sum<LPT>(sc[h][i]) * sscale;
     bool valid[NLD];
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) valid[i] = !kPartial || (i * TPI + row) < nvalid;
+    for (int i = 0; i < NLD; ++i)
+        valid[i] = !kPartial || ((i * TPI + row) < nvalid && (i * TPI + row) >= nlo);
     if constexpr (kPartial) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i)
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
     const int voff = lane * 16;
 
     Tile<KV, D> t[NBUF];
-    int nv[NBUF];
+    int nv[NBUF], nl[NBUF];
     // Fused append: the wave that reads the new token's tile fetches its
     // source rows first and parks them in LDS once they land (by then the
     // ring's first tiles are in flight behind them).
@@ -278,10 +281,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
     if (kFused && ww.newk >= 0) ns.fetch(p, s, g, lane);
     int new_id = -1;
     // Issue the loads of tile kn into a ring slot.
-    auto issue = [&](Tile<KV, D>& tt, int& nvalid, int kn) {
+    auto issue = [&](Tile<KV, D>& tt, int& nvalid, int& nlo, int kn) {
         const int id = ids.next(kn);
-        const TileRef r = tile_ref(p, kpl, vpl, bstride, TB, id, (ww.b0 + kn * NW) * 16, L);
+        const TileRef r =
+            tile_ref(p, kpl, vpl, bstride, TB, id, (ww.b0 + kn * NW) * 16, L, ww.lo);
         nvalid = r.nvalid;
+        nlo = r.nlo;  // > 0 only on a sliding window's first tile
         if (kFused && kn == ww.newk) new_id = id;
 #pragma unroll
         for (int i = 0; i < NLD; ++i) tt.k[i] = rsrc_load16(r.k, voff + i * 1024);
@@ -290,7 +295,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
     };
 
 #pragma unroll
-    for (int x = 0; x < NBUF; ++x) issue(t[x], nv[x], x);
+    for (int x = 0; x < NBUF; ++x) issue(t[x], nv[x], nl[x], x);
     if (kFused && ww.newk >= 0) ns.stash(new_rows[w], lane);
     for (int k0 = 0; k0 < n; k0 += NBUF) {
 #pragma unroll
@@ -305,11 +310,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
                 patch_natural<LPT>(t[x].v, vc, off, lane);
                 store_new_row<LPT>(p, g, new_id, off, TB, kc, vc, lane);
             }
-            if (nv[x] == 16)
-                consume_tile<KV, D, G, false>(st, t[x], 16, qs, sscale, row);
+            if (nv[x] == 16 && nl[x] == 0)
+                consume_tile<KV, D, G, false>(st, t[x], 16, 0, qs, sscale, row);
             else
-                consume_tile<KV, D, G, true>(st, t[x], nv[x], qs, sscale, row);
-            issue(t[x], nv[x], k0 + x + NBUF);
+                consume_tile<KV, D, G, true>(st, t[x], nv[x], nl[x], qs, sscale, row);
+            issue(t[x], nv[x], nl[x], k0 + x + NBUF);
         }
     }
 

@@ -11,6 +11,7 @@
 // Fixed-size blocks make any free block as good as any other, so a stack gives
 // O(1) alloc and free; reference counts give sharing without copies.
 
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -315,6 +316,48 @@ pkv_status kv_seq_extend_cow(pkv_pool* pool, int32_t num_seqs, int32_t* block_ta
     return extend_impl("kv_seq_extend_cow", pool, num_seqs, block_tables, max_blocks_per_seq,
                        cur_lens, new_lens, slot_mapping_out, true, copy_src_out, copy_dst_out,
                        num_copies_out);
+}
+
+pkv_status kv_seq_trim(pkv_pool* pool, int32_t num_seqs, int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t window,
+                       int32_t* num_released_out) {
+    if (pool == nullptr) return fail(PKV_ERR_INVALID, "kv_seq_trim: pool is NULL");
+    if (num_seqs < 0 || max_blocks_per_seq < 0 || window <= 0)
+        return fail(PKV_ERR_INVALID, "kv_seq_trim: bad sizes or window %d", window);
+    if (num_seqs > 0 && (block_tables == nullptr || context_lens == nullptr))
+        return fail(PKV_ERR_INVALID, "kv_seq_trim: NULL array");
+    const int32_t bs = pool->desc.block_size;
+    std::unordered_map<int32_t, int32_t> need;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+        const int64_t before = static_cast<int64_t>(context_lens[i]) - window;
+        const int64_t nj = before > 0 ? std::min<int64_t>(before / bs, max_blocks_per_seq) : 0;
+        const int32_t* row = block_tables + static_cast<int64_t>(i) * max_blocks_per_seq;
+        for (int64_t j = 0; j < nj; ++j) {
+            const int32_t b = row[j];
+            if (b == -1) continue;
+            if (b < 0 || b >= pool->desc.num_blocks)
+                return fail(PKV_ERR_INVALID, "kv_seq_trim: seq %d: block id %d out of range", i, b);
+            need[b] += 1;
+        }
+    }
+    for (const auto& kv : need)
+        if (pool->ref[kv.first] < kv.second)
+            return fail(PKV_ERR_STATE, "kv_seq_trim: block %d holds %d references, %d released",
+                        kv.first, pool->ref[kv.first], kv.second);
+    int32_t released = 0;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+        const int64_t before = static_cast<int64_t>(context_lens[i]) - window;
+        const int64_t nj = before > 0 ? std::min<int64_t>(before / bs, max_blocks_per_seq) : 0;
+        int32_t* row = block_tables + static_cast<int64_t>(i) * max_blocks_per_seq;
+        for (int64_t j = 0; j < nj; ++j) {
+            if (row[j] == -1) continue;
+            release(pool, row[j]);
+            row[j] = -1;
+            ++released;
+        }
+    }
+    if (num_released_out != nullptr) *num_released_out = released;
+    return PKV_OK;
 }
 
 int32_t kv_pool_num_cached(const pkv_pool* pool) {

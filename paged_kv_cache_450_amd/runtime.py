@@ -23,7 +23,8 @@ from . import (BLOCK_SIZE, PKV_BF16, PKV_ERR_OOM, PKV_F16, PKV_FP8_E4M3, PkvErro
                kv_block_copy, kv_cache_append, kv_pool_bytes, kv_pool_create, kv_pool_destroy,
                kv_pool_free_list, kv_pool_num_free, kv_prefix_acquire, kv_prefix_register,
                kv_seq_extend, kv_seq_extend_cow, kv_seq_fork,
-               paged_attn_decode, paged_attn_decode_append, paged_attn_reduce,
+               paged_attn_decode, paged_attn_decode_append, paged_attn_decode_window,
+               paged_attn_reduce,
                paged_attn_workspace_bytes)
 
 DTYPE_CODES = {"f16": PKV_F16, "bf16": PKV_BF16, "e4m3": PKV_FP8_E4M3}
@@ -120,13 +121,15 @@ class DecodeBatch:
     run(layer, q) issues paged_attn_decode and, when partitioned, paged_attn_reduce
     on one stream; the output is self.out. decode_append(layer, q, k, v) is the
     fused form that also stores each sequence's new token. A single pass (partition_size 0) is
-    balanced across the GPU unless balanced=False.
+    balanced across the GPU unless balanced=False. window > 0: every sequence
+    attends over its last `window` tokens only (paged_attn_decode_window).
     """
 
     def __init__(self, cache: PagedKVCache, tables: np.ndarray, lens, num_q_heads: int,
                  q_dtype, partition_size: int = 0, scale=None, k_scale=None, v_scale=None,
-                 max_context_len=None, device="cuda", balanced: bool = True):
+                 max_context_len=None, device="cuda", balanced: bool = True, window: int = 0):
         self.cache = cache
+        self.window = window
         lens = np.asarray(lens, dtype=np.int32)
         self.num_seqs = lens.size
         self.tables = torch.from_numpy(np.ascontiguousarray(tables, dtype=np.int32)).to(device)
@@ -153,6 +156,13 @@ class DecodeBatch:
             self.workspace = None
 
     def decode(self, layer: int, q, stream=None):
+        if self.window > 0:
+            paged_attn_decode_window(self.cache.handle, layer, q,
+                                     None if self.partition_size else self.out, self.tables,
+                                     self.lens, self.scale, self.max_context_len, self.window,
+                                     self.partition_size, self.workspace, self.k_scale,
+                                     self.v_scale, stream=stream)
+            return
         paged_attn_decode(self.cache.handle, layer, q, None if self.partition_size else self.out,
                           self.tables, self.lens, self.scale, self.max_context_len,
                           self.partition_size, self.workspace, self.k_scale, self.v_scale, stream)
@@ -163,6 +173,13 @@ class DecodeBatch:
         want = (self.num_seqs, self.cache.desc.num_kv_heads, self.head_dim)
         if tuple(new_k.shape) != want or tuple(new_v.shape) != want:
             raise ValueError(f"new_k and new_v must be {want}")
+        if self.window > 0:
+            paged_attn_decode_window(self.cache.handle, layer, q,
+                                     None if self.partition_size else self.out, self.tables,
+                                     self.lens, self.scale, self.max_context_len, self.window,
+                                     self.partition_size, self.workspace, self.k_scale,
+                                     self.v_scale, new_k, new_v, stream)
+            return
         paged_attn_decode_append(self.cache.handle, layer, new_k, new_v, q,
                                  None if self.partition_size else self.out, self.tables,
                                  self.lens, self.scale, self.max_context_len,

@@ -29,7 +29,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 23, names
+    assert len(names) == 25, names
     out = subprocess.run(["nm", "-D", "--defined-only", P.library_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -132,6 +132,16 @@ class Both:
 
     def m_acquire(self, keys):
         return np.array(self.model.acquire(keys), dtype=np.int32)
+
+    def c_trim(self, rows, lens, window):
+        t = np.array(rows, dtype=np.int32).reshape(len(rows), -1)
+        n = P.kv_seq_trim(self.pool, t, np.array(lens, dtype=np.int32), window)
+        return t, n
+
+    def m_trim(self, rows, lens, window):
+        t = [list(r) for r in rows]
+        n = self.model.trim(t, lens, window)
+        return np.array(t, dtype=np.int32).reshape(len(rows), -1), n
 
     def c_fork(self, src, n):
         dst = np.full(len(src), -1, dtype=np.int32)
@@ -288,6 +298,72 @@ def test_cpp_prefix_cache_matches_model_on_random_traces(seed):
         elif op == "register":
             b.call("register", [keys[0]], [n + 5])  # out of range
     assert hits > 0 and evictions > 0
+    P.kv_pool_destroy(b.pool)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_cpp_trim_matches_model_on_random_traces(seed):
+    """kv_seq_trim against the model, on sequences that grow, fork, finish
+    and register prefix keys while a sliding window trims them: tables, the
+    number released, the free stack, the cached list and every refcount agree
+    after every call, bad ids and over-release included."""
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(8, 60))
+    window = int(rng.choice([1, 15, 16, 17, 40]))
+    b = Both(n)
+    tables = {}
+    nid = released = 0
+    for _ in range(400):
+        op = rng.choice(["admit", "grow", "grow", "finish", "fork", "trim", "bad"])
+        if op == "admit":
+            exc, res = b.call("extend", [[-1] * 8], [0], [int(rng.integers(1, 60))])
+            if exc is None:
+                row = list(res[0][0])
+                tables[nid] = (row, int(sum(1 for x in row if x >= 0)) * 16)
+                full = [x for x in row if x >= 0][:-1]
+                b.call("register", [int(k) for k in rng.integers(1, 50, size=len(full))], full)
+                tables[nid] = (row, len(full) * 16 + 1)
+                nid += 1
+        elif op == "grow" and tables:
+            for r in sorted(tables):
+                row, length = tables[r]
+                new = min(length + int(rng.integers(0, 6)), 128)
+                exc, res = b.call("extend_cow", [row], [length], [new])
+                if exc is None:
+                    tables[r] = (list(res[0][0]), new)
+        elif op == "finish" and tables:
+            r = list(tables)[int(rng.integers(0, len(tables)))]
+            row, length = tables.pop(r)
+            b.call("free", [x for x in row if x >= 0])
+        elif op == "fork" and tables:
+            r = list(tables)[int(rng.integers(0, len(tables)))]
+            row, length = tables[r]
+            nb = -(-length // 16)
+            if all(x >= 0 for x in row[:nb]):
+                exc, dst = b.call("fork", row, nb)
+                if exc is None:
+                    tables[nid] = (list(dst), length)
+                    nid += 1
+        elif op == "trim" and tables:
+            rids = sorted(tables)
+            exc, res = b.call("trim", [tables[r][0] for r in rids],
+                              [tables[r][1] for r in rids], window)
+            assert exc is None
+            released += res[1]
+            for k, r in enumerate(rids):
+                tables[r] = (list(res[0][k]), tables[r][1])
+        elif op == "bad" and tables:
+            r = list(tables)[int(rng.integers(0, len(tables)))]
+            row, length = tables[r]
+            exc, _ = b.call("trim", [row[:1] + [n + 2] + row[2:]], [128], 1)
+            assert exc == P.PKV_ERR_INVALID
+            if row[0] >= 0:  # one more release of a block than it holds
+                k = P.block_refcount(b.pool, row[0]) + 1
+                exc, _ = b.call("trim", [[row[0]]] * k, [17] * k, 1)
+                assert exc == P.PKV_ERR_STATE
+            exc, _ = b.call("trim", [row], [length], 0)
+            assert exc == P.PKV_ERR_INVALID
+    assert released > 0
     P.kv_pool_destroy(b.pool)
 
 
