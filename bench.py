@@ -359,29 +359,80 @@ def block_copy_rate(cfg, pairs: int, iters: int, stream) -> dict:
             "frac_hbm": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False) -> dict:
+def swap_rate(cfg, blocks: int, iters: int, stream) -> dict:
+    """kv_swap_out of `blocks` random blocks (every layer, K and V) of a pool of
+    the workload's geometry into pinned host slots, and kv_swap_in back, each
+    timed over `iters` calls back to back with one event pair; bytes = one
+    slot per block each way. For reference, the copy engine's rate on a
+    contiguous device <-> pinned host copy of the same size."""
+    import torch
+
+    import paged_kv_cache_450_amd as P
+    from paged_kv_cache_450_amd.runtime import PagedKVCache
+
+    cache = PagedKVCache(cfg.layers, 2 * blocks, cfg.kv_heads, cfg.head_dim, cfg.kv_dtype,
+                         "cuda", fill_byte=1)
+    h = cache.handle
+    slot = P.kv_swap_slot_bytes(h)
+    host = torch.empty(blocks * slot, dtype=torch.uint8, pin_memory=True)
+    rng = np.random.default_rng(0)
+    ids = rng.permutation(2 * blocks)[:blocks].astype(np.int32)
+    slots = rng.permutation(blocks).astype(np.int32)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters * 1e3
+
+    out_us = timed(lambda: P.kv_swap_out(h, ids, slots, host, stream))
+    in_us = timed(lambda: P.kv_swap_in(h, slots, ids, host, stream))
+    dev = torch.empty(blocks * slot, dtype=torch.uint8, device="cuda")
+    with torch.cuda.stream(stream):
+        d2h_us = timed(lambda: host.copy_(dev, non_blocking=True))
+        h2d_us = timed(lambda: dev.copy_(host, non_blocking=True))
+    moved = blocks * slot
+    cache.close()
+
+    def gbs(us):
+        return round(moved / (us * 1e-6) / 1e9, 2)
+    return {"blocks": blocks, "bytes_per_block": slot, "out_us": round(out_us, 2),
+            "out_GBs": gbs(out_us), "in_us": round(in_us, 2), "in_GBs": gbs(in_us),
+            "copy_engine_d2h_GBs": gbs(d2h_us), "copy_engine_h2d_GBs": gbs(h2d_us)}
+
+
+def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False, swap_slots=0,
+                 pool_blocks=0, max_gen=128) -> dict:
     """The continuous-batching loop (ContinuousBatcher) over a seeded request
     stream shaped like the workload: prompts of up to its longest context, 1 to
-    128 generated tokens, a third of the requests with 2-3 samples, 4 arrivals
+    max_gen generated tokens, a third of the requests with 2-3 samples, 4 arrivals
     per iteration and a pool of the workload's size (so requests queue and, at
     times, are preempted). groups = (G, T): prompts in G prefix groups sharing
     their first T tokens (a system prompt); caching: admit through the prefix
-    cache. Inputs are drawn before the timed region, which holds the
-    bookkeeping (host) and the GPU work of every iteration."""
+    cache; swap_slots: preempt into a swap space of that many pinned host slots
+    (else by recomputation); pool_blocks > 0: a pool of that many blocks
+    instead (a tight pool forces preemption). Inputs are drawn before the timed region, which
+    holds the bookkeeping (host) and the GPU work of every iteration."""
     import torch
 
     import workloads as W
-    from paged_kv_cache_450_amd.runtime import ContinuousBatcher, PagedKVCache
+    from paged_kv_cache_450_amd.runtime import ContinuousBatcher, PagedKVCache, SwapSpace
 
     lens = W.context_lengths(cfg, 0)
-    max_prompt, max_gen = int(lens.max()), 128
+    max_prompt = int(lens.max())
     max_prompt = max(max_prompt, groups[1])
-    nb = cfg.pool_blocks or blocks_needed(cfg, lens)
+    nb = pool_blocks or cfg.pool_blocks or blocks_needed(cfg, lens)
     width = -(-(max_prompt + max_gen) // BS)
     trace = W.request_trace(cfg.name + "_serve", 0, 4 * iters, max_prompt, max_gen,
                             mean_gap=0.25, prefix_groups=groups[0], shared_tokens=groups[1])
     cache = PagedKVCache(cfg.layers, nb, cfg.kv_heads, cfg.head_dim, cfg.kv_dtype, "cuda")
-    loop = ContinuousBatcher(cache, width, prefix_caching=caching)
+    swap = SwapSpace(cache, swap_slots) if swap_slots else None
+    loop = ContinuousBatcher(cache, width, prefix_caching=caching, swap=swap)
     dt = cfg.src_dtype
     kp = W.normal((max_prompt, cfg.kv_heads, cfg.head_dim), dt, 1, "cuda")
     vp = W.normal((max_prompt, cfg.kv_heads, cfg.head_dim), dt, 2, "cuda")
@@ -404,13 +455,17 @@ def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False) -> dict:
 
     pending = list(trace)
     host_s = 0.0
-    tokens = copies = preempted = prefill = reused = 0
+    tokens = copies = preempted = prefill = reused = swapped_out = swapped_blocks = done = 0
+    discarded = 0  # tokens generated by requests that recomputation then restarted
     batches = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for it in range(iters):
         while pending and pending[0].arrival <= it:
             loop.submit(pending.pop(0))
+        gen = {}
+        for sq in loop.running:
+            gen[sq.rid] = gen.get(sq.rid, 0) + sq.generated
         h0 = time.perf_counter()
         plan = loop.plan()
         host_s += time.perf_counter() - h0
@@ -422,14 +477,21 @@ def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False) -> dict:
         batches.append(len(plan.batch))
         copies += len(plan.copy_src) if plan.copy_src is not None else 0
         preempted += len(plan.preempted)
+        discarded += sum(gen.get(r, 0) for r in plan.preempted)
+        swapped_out += len(plan.swapped_out)
+        done += len(plan.finished)
+        swapped_blocks += len(plan.swap_out_ids) + len(plan.swap_in_ids)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     cache.close()
     return {"iterations": iters, "decode_tokens": tokens, "tokens_per_s": round(tokens / wall, 1),
+            "sequences_finished": done, "sequences_finished_per_s": round(done / wall, 1),
             "ms_per_iteration": round(wall / iters * 1e3, 4),
             "host_plan_us_per_iteration": round(host_s / iters * 1e6, 1),
             "mean_batch": round(float(np.mean(batches)), 2), "max_batch": int(max(batches)),
-            "copies": copies, "preemptions": preempted, "pool_blocks": nb,
+            "copies": copies, "preemptions": preempted, "tokens_discarded": discarded,
+            "max_gen": max_gen, "swap_slots": swap_slots,
+            "swapped_out": swapped_out, "blocks_swapped": swapped_blocks, "pool_blocks": nb,
             "prefix_caching": caching, "prefix_groups": list(groups),
             "prefill_tokens": prefill, "cached_blocks_reused": reused,
             "requests_admitted": 4 * iters - len(pending) - len(loop.waiting)}
@@ -504,6 +566,15 @@ def main(argv=None):
                          "first TOKENS tokens")
     ap.add_argument("--serve-caching", action="store_true",
                     help="run the serving loop with prefix caching")
+    ap.add_argument("--swap", type=int, default=0, metavar="N",
+                    help="also time kv_swap_out / kv_swap_in of N blocks of the workload's "
+                         "geometry to and from pinned host memory")
+    ap.add_argument("--serve-swap", type=int, default=0, metavar="SLOTS",
+                    help="run the serving loop with a swap space of SLOTS host slots")
+    ap.add_argument("--serve-blocks", type=int, default=0, metavar="N",
+                    help="run the serving loop on a pool of N blocks")
+    ap.add_argument("--serve-gen", type=int, default=128, metavar="N",
+                    help="longest generation of the serving stream's requests")
     ap.add_argument("--window", default=None, metavar="W[,W...]",
                     help="also time the step with a sliding window of W tokens "
                          "(paged_attn_decode_window) on the same caches")
@@ -655,7 +726,10 @@ def main(argv=None):
                             for x in args.window.split(",")]
     if args.serve > 0:
         groups = tuple(int(x) for x in args.serve_prefix.split(",")) if args.serve_prefix else (0, 0)
-        result["serving"] = serving_rate(cfg, args.serve, stream, groups, args.serve_caching)
+        result["serving"] = serving_rate(cfg, args.serve, stream, groups, args.serve_caching,
+                                         args.serve_swap, args.serve_blocks, args.serve_gen)
+    if args.swap > 0:
+        result["swap"] = swap_rate(cfg, args.swap, args.steps, stream)
     if args.block_copy > 0:
         result["block_copy"] = block_copy_rate(cfg, args.block_copy, args.steps, stream)
     if not args.no_cpu_baseline:

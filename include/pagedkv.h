@@ -211,6 +211,42 @@ pkv_status kv_seq_extend_cow(pkv_pool* pool, int32_t num_seqs, int32_t* block_ta
 pkv_status kv_block_copy(const pkv_pool* pool, const int32_t* src_ids, const int32_t* dst_ids,
                          int32_t n, hipStream_t stream);
 
+/* Swapping blocks to host memory ([P2] "vLLM 也不是银弹：真实部署中的坑" and
+ * "从零开始：vLLM 部署的实战建议", second step: when the cache runs short,
+ * running requests are preempted and their blocks swapped out, to come back
+ * when blocks free up).
+ *
+ * Swap space is a caller-owned buffer of host memory, pinned (hipHostMalloc;
+ * memory registered after the fact or pageable memory is rejected), divided
+ * into slots of kv_swap_slot_bytes(pool) bytes. Slot s holds one block of
+ * every layer, K and V, as [num_layers][2][num_kv_heads][16][head_dim]
+ * elements of the pool's dtype, starting at byte s * kv_swap_slot_bytes. The
+ * GPU reads and writes the pinned pages directly; the calls are enqueued on
+ * stream and allocate nothing (ids and slots travel as kernel arguments, 128
+ * pairs per launch). The host must not touch the slots involved until the
+ * stream has passed the call. Block bookkeeping is the caller's: swap a
+ * request's blocks out, then block_free them; block_alloc fresh ids, then swap
+ * the slots in to them. */
+
+/* Bytes of one swap slot: 2 * num_layers * num_kv_heads * 16 * head_dim *
+ * element size; 0 for a NULL pool. */
+size_t kv_swap_slot_bytes(const pkv_pool* pool);
+
+/* Slot host_slots[i] := block block_ids[i], for i < n (host int32 arrays).
+ * host_buf / host_buf_bytes: the swap space. Blocks may repeat; slots must be
+ * distinct.
+ * Errors: INVALID (NULL pool, base or arrays, negative n, ids or slots out of
+ *   range, a repeated slot, a buffer that is not one pinned host allocation of
+ *   host_buf_bytes bytes), HIP. n == 0 does nothing. */
+pkv_status kv_swap_out(const pkv_pool* pool, const int32_t* block_ids, const int32_t* host_slots,
+                       int32_t n, void* host_buf, size_t host_buf_bytes, hipStream_t stream);
+
+/* Block block_ids[i] := slot host_slots[i], for i < n. Slots may repeat;
+ * blocks must be distinct. Errors as kv_swap_out (a repeated block instead of
+ * a repeated slot). */
+pkv_status kv_swap_in(const pkv_pool* pool, const int32_t* host_slots, const int32_t* block_ids,
+                      int32_t n, const void* host_buf, size_t host_buf_bytes, hipStream_t stream);
+
 /* Prefix caching ([P2] "PagedAttention：...": requests with the same prompt
  * prefix share its physical blocks; "从零开始：vLLM 部署的实战建议", third step:
  * prefix caching). The caller names the contents of a full block with a

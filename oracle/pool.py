@@ -12,7 +12,9 @@ the one used here is this library's contract:
     lives at element offset ((((l*2 + c)*NB + b)*Hkv + h)*BS + t)*D + d
 
 so one (l, c, b, h) tile of BS x D elements is contiguous and one block id
-names the same block in every layer.
+names the same block in every layer. A swap slot s of host memory holds one
+block of every layer, element (l, c, h, t, d) at offset
+((((s*L + l)*2 + c)*Hkv + h)*BS + t)*D + d.
 
 [P2], "真正吃显存的是 KV Cache，不是模型权重": per request the cache holds a
 K and a V vector per token, per layer and per head; the section works the
@@ -111,3 +113,22 @@ def copy_blocks(pool6: np.ndarray, src_ids, dst_ids) -> None:
     dst = np.asarray(dst_ids, dtype=np.int64)
     if src.size:
         pool6[:, :, dst] = pool6[:, :, src]
+
+
+def swap_out(pool6: np.ndarray, host: np.ndarray, block_ids, host_slots) -> None:
+    """Swapping out ("vLLM 也不是银弹：..."): host[slots[i]] := every layer's K
+    and V of block ids[i]. host: [S, L, 2, Hkv, BS, D] raw codes, one slot per
+    block of the whole model; slots are distinct."""
+    ids = np.asarray(block_ids, dtype=np.int64)
+    slots = np.asarray(host_slots, dtype=np.int64)
+    for b, s in zip(ids, slots):
+        host[s] = pool6[:, :, b]
+
+
+def swap_in(pool6: np.ndarray, host: np.ndarray, host_slots, block_ids) -> None:
+    """Swapping in: every layer's K and V of block ids[i] := host[slots[i]];
+    blocks are distinct."""
+    ids = np.asarray(block_ids, dtype=np.int64)
+    slots = np.asarray(host_slots, dtype=np.int64)
+    for s, b in zip(slots, ids):
+        pool6[:, :, b] = host[s]

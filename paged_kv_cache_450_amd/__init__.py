@@ -77,6 +77,9 @@ def _load():
         "kv_seq_extend_cow": (i32, [vp, i32, p_i32, i32, p_i32, p_i32, p_i64, p_i32, p_i32,
                                     p_i32]),
         "kv_block_copy": (i32, [vp, p_i32, p_i32, i32, vp]),
+        "kv_swap_slot_bytes": (sz, [vp]),
+        "kv_swap_out": (i32, [vp, p_i32, p_i32, i32, vp, sz, vp]),
+        "kv_swap_in": (i32, [vp, p_i32, p_i32, i32, vp, sz, vp]),
         "kv_prefix_register": (i32, [vp, ctypes.POINTER(ctypes.c_uint64), p_i32, i32, p_i32]),
         "kv_prefix_acquire": (i32, [vp, ctypes.POINTER(ctypes.c_uint64), i32, p_i32, p_i32]),
         "kv_pool_num_cached": (i32, [vp]),
@@ -333,6 +336,46 @@ def kv_block_copy(pool, src_ids, dst_ids, stream=None) -> None:
     if src.size != dst.size:
         raise ValueError("one destination per source")
     _check(lib.kv_block_copy(pool, _i32_ptr(src), _i32_ptr(dst), src.size, _stream(stream)))
+
+
+def kv_swap_slot_bytes(pool) -> int:
+    """Bytes of one swap slot: one block of every layer, K and V."""
+    return int(lib.kv_swap_slot_bytes(pool))
+
+
+def _swap_buffer(host_buf):
+    """(address, bytes) of a swap space: a pinned uint8 CPU tensor, or an
+    (address, bytes) pair of pinned host memory."""
+    if isinstance(host_buf, tuple):
+        return host_buf
+    torch = _torch()
+    if not isinstance(host_buf, torch.Tensor) or host_buf.device.type != "cpu":
+        raise ValueError("host_buf must be a pinned CPU tensor")
+    if not host_buf.is_pinned() or not host_buf.is_contiguous():
+        raise ValueError("host_buf must be pinned and contiguous")
+    return host_buf.data_ptr(), host_buf.numel() * host_buf.element_size()
+
+
+def kv_swap_out(pool, block_ids, host_slots, host_buf, stream=None) -> None:
+    """Swap slot host_slots[i] := block block_ids[i] (host ids), on stream."""
+    ids = _host_i32(block_ids).reshape(-1)
+    slots = _host_i32(host_slots).reshape(-1)
+    if ids.size != slots.size:
+        raise ValueError("one slot per block")
+    addr, nbytes = _swap_buffer(host_buf)
+    _check(lib.kv_swap_out(pool, _i32_ptr(ids), _i32_ptr(slots), ids.size, addr, nbytes,
+                           _stream(stream)))
+
+
+def kv_swap_in(pool, host_slots, block_ids, host_buf, stream=None) -> None:
+    """Block block_ids[i] := swap slot host_slots[i] (host ids), on stream."""
+    ids = _host_i32(block_ids).reshape(-1)
+    slots = _host_i32(host_slots).reshape(-1)
+    if ids.size != slots.size:
+        raise ValueError("one block per slot")
+    addr, nbytes = _swap_buffer(host_buf)
+    _check(lib.kv_swap_in(pool, _i32_ptr(slots), _i32_ptr(ids), ids.size, addr, nbytes,
+                          _stream(stream)))
 
 
 def paged_attn_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,

@@ -19,10 +19,11 @@ import numpy as np
 import torch
 
 from . import (BLOCK_SIZE, PKV_BF16, PKV_ERR_OOM, PKV_F16, PKV_FP8_E4M3, PkvError, PoolDesc,
-               block_alloc, block_free,
+               block_alloc, block_free, block_incref,
                kv_block_copy, kv_cache_append, kv_pool_bytes, kv_pool_create, kv_pool_destroy,
                kv_pool_free_list, kv_pool_num_free, kv_prefix_acquire, kv_prefix_register,
-               kv_seq_extend, kv_seq_extend_cow, kv_seq_fork,
+               kv_seq_extend, kv_seq_extend_cow, kv_seq_fork, kv_swap_in, kv_swap_out,
+               kv_swap_slot_bytes,
                paged_attn_decode, paged_attn_decode_append, paged_attn_decode_window,
                paged_attn_reduce,
                paged_attn_workspace_bytes)
@@ -225,6 +226,50 @@ class IterationPlan:
     slots: np.ndarray = None                       # int64 [B], the new tokens' slots
     copy_src: np.ndarray = None                    # copy-on-write pairs
     copy_dst: np.ndarray = None
+    swapped_in: list = field(default_factory=list)   # rids back from the swap space
+    swapped_out: list = field(default_factory=list)  # rids sent to the swap space
+    swap_in_slots: list = field(default_factory=list)  # slot -> fresh block, in order
+    swap_in_ids: list = field(default_factory=list)
+    swap_out_ids: list = field(default_factory=list)   # block -> slot, in order
+    swap_out_slots: list = field(default_factory=list)
+
+
+class SwapSpace:
+    """Host memory for swapped-out blocks: num_slots slots of
+    kv_swap_slot_bytes(pool) bytes each, in one pinned allocation, and a LIFO
+    stack of free slots that starts [num_slots - 1, ..., 0] (the first slots
+    taken are 0, 1, 2, ...). pinned=False keeps the bookkeeping only."""
+
+    def __init__(self, cache: PagedKVCache, num_slots: int, pinned: bool = True):
+        self.slot_bytes = kv_swap_slot_bytes(cache.handle)
+        self.num_slots = num_slots
+        self.buf = (torch.empty(num_slots * self.slot_bytes, dtype=torch.uint8, pin_memory=True)
+                    if pinned and num_slots > 0 else None)
+        self.free = list(range(num_slots - 1, -1, -1))
+
+    def num_free(self) -> int:
+        return len(self.free)
+
+    def take(self, n: int) -> list:
+        return [self.free.pop() for _ in range(n)]
+
+    def give(self, slots) -> None:
+        self.free.extend(int(x) for x in slots)
+
+
+def distinct_blocks(seqs):
+    """The distinct block ids the sequences' rows hold, in order of first
+    appearance, and per sequence the index into them of each row entry."""
+    order, index, maps = [], {}, []
+    for s in seqs:
+        m = []
+        for b in s.row[:s.num_blocks].tolist():
+            if b not in index:
+                index[b] = len(order)
+                order.append(b)
+            m.append(index[b])
+        maps.append(np.array(m, dtype=np.int64))
+    return order, maps
 
 
 class ContinuousBatcher:
@@ -256,17 +301,33 @@ class ContinuousBatcher:
         the cached blocks of the longest leading run of the prompt's block
         keys (spec.block_keys), prefills only the tokens after them, and
         registers its new full prompt blocks under their keys; if the request
-        then does not fit, the cached blocks are given back.
+        then does not fit, the cached blocks are given back;
+      * with a swap space ("vLLM 也不是银弹：..." and "从零开始：..." second
+        step name swapping out as the alternative to recomputation), a
+        preempted request that was not admitted in the same iteration, and
+        whose distinct blocks fit in the free host slots, is swapped out: its
+        distinct blocks, in order of first appearance over its samples' rows,
+        each take a slot, and it waits in the swapped list ordered by request
+        id. Swapped requests come back before anything is admitted: while the
+        first one's distinct blocks plus one block per running sequence (its
+        own included) are free, it takes fresh blocks and the references its
+        rows held, and gives back its slots; waiting requests are admitted
+        only when none is swapped out.
 
     plan() does the bookkeeping of an iteration on the host (block manager
     calls only); execute() then issues its GPU work on one stream: the prompt
-    appends, the block copies, and one fused decode step per layer.
+    appends, the block copies, and one fused decode step per layer; swap-ins
+    go first and swap-outs next, before anything can write the blocks they
+    read or the slots they fill.
     """
 
-    def __init__(self, cache: PagedKVCache, max_blocks_per_seq: int, prefix_caching=False):
+    def __init__(self, cache: PagedKVCache, max_blocks_per_seq: int, prefix_caching=False,
+                 swap: SwapSpace = None):
         self.cache = cache
         self.width = max_blocks_per_seq
         self.prefix_caching = prefix_caching
+        self.swap = swap
+        self.swapped = []  # (rid, seqs, maps, slots), ordered by rid
         self.waiting = deque()
         self.running = []
         self.iteration = 0
@@ -287,8 +348,27 @@ class ContinuousBatcher:
             else:
                 keep.append(s)
         self.running = keep
-        # 2-3. admit while the prompt fits above the reserve
-        while self.waiting:
+        # 2. swapped-out requests come back first
+        while self.swapped:
+            rid, seqs, maps, slots = self.swapped[0]
+            if kv_pool_num_free(h) - len(slots) < len(self.running) + len(seqs):
+                break
+            self.swapped.pop(0)
+            ids = block_alloc(h, len(slots))
+            counts = np.zeros(len(slots), dtype=np.int64)
+            for s, mp in zip(seqs, maps):
+                s.row[:mp.size] = ids[mp]
+                np.add.at(counts, mp, 1)
+            extra = np.repeat(ids, counts - 1)
+            if extra.size:
+                block_incref(h, extra)
+            p.swap_in_slots += slots
+            p.swap_in_ids += ids.tolist()
+            self.swap.give(slots)
+            self.running.extend(seqs)
+            p.swapped_in.append(rid)
+        # 3. admit while the prompt fits above the reserve, once none is swapped out
+        while self.waiting and not self.swapped:
             spec = self.waiting[0]
             nblk = -(-spec.prompt_len // BLOCK_SIZE)
             hit = (kv_prefix_acquire(h, spec.block_keys) if self.prefix_caching
@@ -338,9 +418,20 @@ class ContinuousBatcher:
     def _preempt_last(self, p: IterationPlan) -> None:
         rid = self.running[-1].rid
         spec = self._specs[rid]
-        for s in [s for s in self.running if s.rid == rid]:
+        seqs = [s for s in self.running if s.rid == rid]
+        order, maps = distinct_blocks(seqs)
+        for s in seqs:
             block_free(self.cache.handle, s.row[:s.num_blocks])
         self.running = [s for s in self.running if s.rid != rid]
+        if (self.swap is not None and len(order) <= self.swap.num_free()
+                and all(a[0].rid != rid for a in p.admitted)):
+            slots = self.swap.take(len(order))
+            p.swap_out_ids += order
+            p.swap_out_slots += slots
+            self.swapped.append((rid, seqs, maps, slots))
+            self.swapped.sort(key=lambda x: x[0])
+            p.swapped_out.append(rid)
+            return
         # admitted this iteration: its prompt appends are dropped with it
         p.admitted = [a for a in p.admitted if a[0].rid != rid]
         p.preempted.append(rid)
@@ -354,6 +445,10 @@ class ContinuousBatcher:
         outputs, one [B, Hq, D] tensor per layer."""
         h = self.cache.handle
         desc = self.cache.desc
+        if plan.swap_in_ids:
+            kv_swap_in(h, plan.swap_in_slots, plan.swap_in_ids, self.swap.buf, stream)
+        if plan.swap_out_ids:
+            kv_swap_out(h, plan.swap_out_ids, plan.swap_out_slots, self.swap.buf, stream)
         for spec, first, slots in plan.admitted:
             if slots.size == 0:  # every prompt block came from the cache
                 continue

@@ -7,6 +7,17 @@ while prompt blocks plus one block per running sequence fit, fork the extra
 samples over every prompt block, grow every running sequence by one token with
 copy on write, and while that growth does not fit send the latest request back
 to the head of the queue (recomputation).
+
+With a swap space of S host slots (a LIFO stack starting [S-1, ..., 0]), a
+preempted request that was not admitted in the same iteration and whose
+distinct blocks fit in the free slots is swapped out instead: its distinct
+blocks, in order of first appearance over its samples' rows, each take a
+slot, and the request waits, by request id, in the swapped list. Swapped
+requests come back first: at the start of admission, while the first one's
+distinct blocks plus one block per running sequence (its own included) are
+free, it takes fresh blocks (one alloc), the references its rows hold, and
+gives its slots back in order; waiting requests are admitted only when no
+request is swapped out.
 """
 
 from collections import deque
@@ -22,14 +33,34 @@ class OracleSeq:
         self.length, self.gen_len, self.generated = length, gen_len, 0
 
 
+def distinct_blocks(seqs):
+    """Distinct block ids over the rows, in order of first appearance, and
+    per sequence the index of each row entry in that list."""
+    order, index, maps = [], {}, []
+    for s in seqs:
+        m = []
+        for b in s.row[: -(-s.length // BS)]:
+            if b not in index:
+                index[b] = len(order)
+                order.append(b)
+            m.append(index[b])
+        maps.append(m)
+    return order, maps
+
+
 class OracleBatcher:
-    def __init__(self, num_blocks, width, prefix_caching=False):
+    def __init__(self, num_blocks, width, prefix_caching=False, swap_slots=0):
         self.model = A.AllocatorModel(num_blocks, BS)
         self.width = width
         self.prefix_caching = prefix_caching
         self.waiting = deque()
         self.running = []
         self.specs = {}
+        self.swap_free = list(range(swap_slots - 1, -1, -1)) if swap_slots else None
+        self.swapped = []   # (rid, seqs, maps, slots), by rid
+        self.swap_in = []   # this iteration's (slot, block) pairs
+        self.swap_out = []  # this iteration's (block, slot) pairs
+        self.swapped_in, self.swapped_out = [], []
 
     def submit(self, spec):
         self.waiting.append(spec)
@@ -45,7 +76,26 @@ class OracleBatcher:
             else:
                 still.append(s)
         self.running = still
-        while self.waiting:
+        self.swap_in, self.swap_out, self.swapped_in, self.swapped_out = [], [], [], []
+        while self.swapped:
+            rid, seqs, maps, slots = self.swapped[0]
+            if m.num_free() - len(slots) < len(self.running) + len(seqs):
+                break
+            self.swapped.pop(0)
+            ids = m.alloc(len(slots))
+            extra = []
+            for s, mp in zip(seqs, maps):
+                for j, u in enumerate(mp):
+                    s.row[j] = ids[u]
+                    extra.append(ids[u])
+            for b in ids:  # one reference came with the alloc
+                extra.remove(b)
+            m.incref(extra)
+            self.swap_in += list(zip(slots, ids))
+            self.swap_free.extend(slots)
+            self.running.extend(seqs)
+            self.swapped_in.append(rid)
+        while self.waiting and not self.swapped:
             spec = self.waiting[0]
             need = -(-spec.prompt_len // BS)
             hit = m.acquire(spec.block_keys) if self.prefix_caching else []
@@ -75,11 +125,21 @@ class OracleBatcher:
                 slots, copies = m.extend_cow(rows, cur, [c + 1 for c in cur])
             except A.AllocError as e:
                 assert e.code == A.OOM
-                # recompute: the latest request goes back to the head of the queue
                 rid = self.running[-1].rid
-                for s in [s for s in self.running if s.rid == rid]:
+                seqs = [s for s in self.running if s.rid == rid]
+                order, maps = distinct_blocks(seqs)
+                for s in seqs:
                     m.free(s.row[: -(-s.length // BS)])
                 self.running = [s for s in self.running if s.rid != rid]
+                if (self.swap_free is not None and len(order) <= len(self.swap_free)
+                        and all(a[0].rid != rid for a in admitted)):
+                    hslots = [self.swap_free.pop() for _ in order]
+                    self.swap_out += list(zip(order, hslots))
+                    self.swapped.append((rid, seqs, maps, hslots))
+                    self.swapped.sort(key=lambda x: x[0])
+                    self.swapped_out.append(rid)
+                    continue
+                # recompute: the latest request goes back to the head of the queue
                 admitted = [a for a in admitted if a[0].rid != rid]
                 preempted.append(rid)
                 self.waiting.appendleft(self.specs[rid])

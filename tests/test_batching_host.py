@@ -8,27 +8,32 @@ import pytest
 
 import paged_kv_cache_450_amd as P
 import workloads as W
-from paged_kv_cache_450_amd.runtime import ContinuousBatcher, PagedKVCache
+from paged_kv_cache_450_amd.runtime import ContinuousBatcher, PagedKVCache, SwapSpace
 from tests.oracle_loop import OracleBatcher
 
 
 # 18 blocks: the largest request (4 prompt blocks, 3 samples each growing by
 # 3 blocks plus a copy) fits alone, so preemption always makes progress.
-@pytest.mark.parametrize("seed,num_blocks,caching", [
-    (0, 40, False), (1, 64, False), (2, 24, False), (3, 200, False), (4, 18, False),
-    (5, 40, True), (6, 24, True), (7, 120, True)])
-def test_loop_bookkeeping_matches_oracle(seed, num_blocks, caching):
+@pytest.mark.parametrize("seed,num_blocks,caching,swap_slots", [
+    (0, 40, False, 0), (1, 64, False, 0), (2, 24, False, 0), (3, 200, False, 0),
+    (4, 18, False, 0), (5, 40, True, 0), (6, 24, True, 0), (7, 120, True, 0),
+    (4, 18, False, 64), (12, 18, False, 8), (12, 18, False, 2), (6, 24, True, 16),
+    (14, 20, True, 40)])
+def test_loop_bookkeeping_matches_oracle(seed, num_blocks, caching, swap_slots):
     """With caching, the trace's requests come in prefix groups sharing a
-    48-token system prompt, admitted through the prefix cache."""
+    48-token system prompt, admitted through the prefix cache. With swap
+    slots, preempted requests go to the swap space when they fit there (a
+    small space forces the fallback to recomputation too)."""
     groups = (3, 48) if caching else (0, 0)
     trace = W.request_trace("batching_host", seed, 60, max_prompt=60, max_gen=40,
                             prefix_groups=groups[0], shared_tokens=groups[1])
     width = -(-(60 + 40) // 16)
     cache = PagedKVCache(1, num_blocks, 2, 64, "f16", device=None)  # bookkeeping only
-    prod = ContinuousBatcher(cache, width, prefix_caching=caching)
-    orc = OracleBatcher(num_blocks, width, prefix_caching=caching)
+    swap = SwapSpace(cache, swap_slots, pinned=False) if swap_slots else None
+    prod = ContinuousBatcher(cache, width, prefix_caching=caching, swap=swap)
+    orc = OracleBatcher(num_blocks, width, prefix_caching=caching, swap_slots=swap_slots)
     pending = list(trace)
-    copies = admitted = finished = preempted = reused = 0
+    copies = admitted = finished = preempted = reused = swapped = 0
     for it in range(3000):
         while pending and pending[0].arrival <= it:
             prod.submit(pending[0])
@@ -36,7 +41,13 @@ def test_loop_bookkeeping_matches_oracle(seed, num_blocks, caching):
         p = prod.plan()
         fin, adm, batch, slots, cps, pre = orc.plan()
         assert p.finished == fin and p.preempted == pre
+        assert p.swapped_in == orc.swapped_in and p.swapped_out == orc.swapped_out
+        assert list(zip(p.swap_in_slots, p.swap_in_ids)) == orc.swap_in
+        assert list(zip(p.swap_out_ids, p.swap_out_slots)) == orc.swap_out
+        if swap:
+            assert swap.free == orc.swap_free
         preempted += len(pre)
+        swapped += len(orc.swapped_out)
         assert [(a[0].rid, a[1]) for a in p.admitted] == [(a[0].rid, a[1]) for a in adm]
         for a, b in zip(p.admitted, adm):
             assert np.array_equal(a[2], np.array(b[2], dtype=np.int64))
@@ -57,10 +68,14 @@ def test_loop_bookkeeping_matches_oracle(seed, num_blocks, caching):
         if not pending and not prod.running and not prod.waiting:
             break
     # every request ran to the end; preempted ones were admitted again
-    assert admitted == len(trace) + preempted and not prod.running
+    assert admitted == len(trace) + preempted and not prod.running and not prod.swapped
     assert copies > 0 and finished > 0
-    if num_blocks == 18:
+    if num_blocks == 18 and not swap_slots:
         assert preempted > 0  # this pool does run out
+    if swap_slots:
+        assert swapped > 0 and swap.num_free() == swap_slots
+    if swap_slots == 2:
+        assert preempted > 0  # too few slots: some preemptions recompute
     assert P.kv_pool_num_free(cache.handle) == num_blocks  # every block came back
     if caching:
         assert reused > 0  # prompts were served from the cache

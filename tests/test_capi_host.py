@@ -29,7 +29,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 25, names
+    assert len(names) == 28, names
     out = subprocess.run(["nm", "-D", "--defined-only", P.library_path()], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -458,6 +458,57 @@ def test_kernel_entry_points_validate_before_touching_the_gpu():
     assert lib.paged_attn_decode_append(pool, 0, None, None, P.PKV_F16, 16, P.PKV_F16, 16, 16, 4,
                                         16, 0, 2, 1.0, None, None, 64, 0, None, 0,
                                         None) == P.PKV_OK
+    P.kv_pool_destroy(pool)
+
+
+def test_swap_calls_validate_before_touching_the_gpu():
+    """kv_swap_out / kv_swap_in fail on host-side checks before any launch;
+    a buffer that is not pinned host memory is refused (here there is no
+    device at all, so no buffer passes)."""
+    import torch
+    lib = P.lib
+    desc = P.PoolDesc(2, 8, 16, 2, 64, P.PKV_F16)
+    slot = 2 * 2 * 2 * 16 * 64 * 2
+    pool = P.kv_pool_create(desc, None, 0)
+    assert P.kv_swap_slot_bytes(pool) == slot
+    assert P.kv_swap_slot_bytes(None) == 0
+    ids = np.array([1, 2], dtype=np.int32)
+    host = np.zeros(4 * slot, dtype=np.uint8)
+    hb = host.ctypes.data
+
+    def call(fn, pool_, a, b, n, buf=hb, nbytes=host.nbytes):
+        a = np.asarray(a, dtype=np.int32)
+        b = np.asarray(b, dtype=np.int32)
+        return getattr(lib, fn)(pool_, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                b.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n, buf, nbytes,
+                                None)
+
+    assert call("kv_swap_out", pool, ids, [0, 1], 2) == P.PKV_ERR_INVALID
+    assert "no device memory" in P.pkv_last_error()
+    P.kv_pool_destroy(pool)
+    pool = P.kv_pool_create(desc, 1 << 40, P.kv_pool_bytes(desc))
+    cases = [
+        ("kv_swap_out", None, ids, [0, 1], 2, hb, host.nbytes, "pool is NULL"),
+        ("kv_swap_out", pool, ids, [0, 1], -1, hb, host.nbytes, "negative"),
+        ("kv_swap_out", pool, [1, 8], [0, 1], 2, hb, host.nbytes, "out of range"),
+        ("kv_swap_out", pool, ids, [0, 4], 2, hb, host.nbytes, "slot 4 out of range"),
+        ("kv_swap_out", pool, ids, [3, 3], 2, hb, host.nbytes, "destination twice"),
+        ("kv_swap_out", pool, ids, [0, 1], 2, None, host.nbytes, "holds no slot"),
+        ("kv_swap_out", pool, ids, [0, 1], 2, hb, slot - 1, "holds no slot"),
+        ("kv_swap_out", pool, ids, [0, 1], 2, hb, host.nbytes, "not one pinned host allocation"),
+        ("kv_swap_in", pool, [0, 0], [5, 5], 2, hb, host.nbytes, "destination twice"),
+        ("kv_swap_in", pool, [0, 9], [5, 6], 2, hb, host.nbytes, "slot 9 out of range"),
+        ("kv_swap_in", pool, [0, 0], [5, 6], 2, hb, host.nbytes, "not one pinned host allocation"),
+    ]
+    for fn, pl, a, b, n, buf, nbytes, msg in cases:  # a, b: (blocks, slots) out, (slots, blocks) in
+        assert call(fn, pl, a, b, n, buf, nbytes) == P.PKV_ERR_INVALID, (fn, msg)
+        assert msg in P.pkv_last_error(), (msg, P.pkv_last_error())
+    # slots may repeat on the way in, blocks on the way out: only the pinned check refuses
+    assert call("kv_swap_out", pool, [4, 4], [0, 1], 2) == P.PKV_ERR_INVALID
+    assert "pinned" in P.pkv_last_error()
+    assert call("kv_swap_out", pool, ids, [0, 1], 0) == P.PKV_OK
+    with pytest.raises(ValueError):
+        P.kv_swap_out(pool, ids, [0, 1], torch.zeros(4 * slot, dtype=torch.uint8))
     P.kv_pool_destroy(pool)
 
 

@@ -17,7 +17,7 @@ import paged_kv_cache_450_amd as P
 import workloads as W
 from oracle import attention as oattn
 from oracle import pool as opool
-from paged_kv_cache_450_amd.runtime import ContinuousBatcher, PagedKVCache
+from paged_kv_cache_450_amd.runtime import ContinuousBatcher, PagedKVCache, SwapSpace
 from tests import harness as H
 from tests.oracle_loop import OracleBatcher
 
@@ -38,28 +38,36 @@ def _gpu(require_gpu):
 # trace) yet holds the largest request alone. The last two run with prefix
 # caching: requests in groups sharing a 48-token system prompt, admitted
 # through the cache (the second pool small enough to evict cached blocks).
-@pytest.mark.parametrize("dt,hq,hkv,dim,num_blocks,max_gen,caching", [
-    ("f16", 2, 2, 64, 48, 12, False), ("bf16", 8, 2, 128, 30, 12, False),
-    ("f16", 4, 4, 128, 16, 40, False), ("bf16", 8, 2, 128, 40, 12, True),
-    ("f16", 2, 2, 64, 20, 12, True)])
-def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching):
+# The last three preempt into a swap space of pinned host memory (swap-outs
+# and swap-ins through kv_swap_out / kv_swap_in), with prefix caching on two.
+@pytest.mark.parametrize("dt,hq,hkv,dim,num_blocks,max_gen,caching,swap_slots", [
+    ("f16", 2, 2, 64, 48, 12, False, 0), ("bf16", 8, 2, 128, 30, 12, False, 0),
+    ("f16", 4, 4, 128, 16, 40, False, 0), ("bf16", 8, 2, 128, 40, 12, True, 0),
+    ("f16", 2, 2, 64, 20, 12, True, 0), ("f16", 4, 4, 128, 16, 40, False, 64),
+    ("bf16", 8, 2, 128, 18, 40, True, 64), ("f16", 2, 2, 64, 14, 40, True, 32)])
+def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching, swap_slots):
     name = f"batching_{dt}_{hq}_{hkv}_{dim}_{num_blocks}_{caching}"
-    say(name)
+    say(f"{name} swap_slots={swap_slots}")
     layers, max_prompt = 2, 40
     width = -(-(max_prompt + 48 + max_gen) // 16)
     groups = (3, 48) if caching else (0, 0)
     trace = W.request_trace(name, 0, 24, max_prompt, max_gen, prefix_groups=groups[0],
                             shared_tokens=groups[1])
     cache = PagedKVCache(layers, num_blocks, hkv, dim, dt, "cuda", fill_byte=H.POISON)
-    prod = ContinuousBatcher(cache, width, prefix_caching=caching)
-    orc = OracleBatcher(num_blocks, width, prefix_caching=caching)
+    swap = SwapSpace(cache, swap_slots) if swap_slots else None
+    prod = ContinuousBatcher(cache, width, prefix_caching=caching, swap=swap)
+    orc = OracleBatcher(num_blocks, width, prefix_caching=caching, swap_slots=swap_slots)
     host = np.full(opool.pool_bytes(layers, num_blocks, 16, hkv, dim, dt), H.POISON, dtype=np.uint8)
     p6 = opool.view_pool(host, layers, num_blocks, 16, hkv, dim, dt)
+    if swap:
+        swap.buf.fill_(H.POISON)
+        oswap = np.full((swap_slots, layers, 2, hkv, 16, dim), np.iinfo(p6.dtype).max,
+                        dtype=p6.dtype)
     scale = float(np.float32(1.0 / np.sqrt(dim)))
     wsb = P.paged_attn_workspace_bytes(1, hq, dim, 1, 0)
     workspace = torch.empty(wsb // 4, dtype=torch.float32, device="cuda")
     pending = list(trace)
-    steps = preempted = copies = reused = 0
+    steps = preempted = copies = reused = swapped = 0
     for it in range(1000):
         while pending and pending[0].arrival <= it:
             prod.submit(pending[0])
@@ -67,6 +75,10 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching
         p = prod.plan()
         fin, adm, batch, slots, cps, pre = orc.plan()
         assert p.finished == fin and p.preempted == pre
+        assert p.swapped_in == orc.swapped_in and p.swapped_out == orc.swapped_out
+        assert list(zip(p.swap_in_slots, p.swap_in_ids)) == orc.swap_in
+        assert list(zip(p.swap_out_ids, p.swap_out_slots)) == orc.swap_out
+        swapped += len(orc.swapped_out)
         assert [(s.rid, s.sample, s.length) for s in p.batch] == \
             [(s.rid, s.sample, s.length) for s in batch]
         preempted += len(pre)
@@ -84,6 +96,10 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching
 
         outs = prod.execute(p, prompt_kv, step_inputs, hq, scale,
                             workspace=workspace if it % 2 else None)
+        if orc.swap_in:
+            opool.swap_in(p6, oswap, *zip(*orc.swap_in))
+        if orc.swap_out:
+            opool.swap_out(p6, oswap, *zip(*orc.swap_out))
         for spec, first, sl in adm:
             for layer in range(layers):
                 k, v = prompt_kv(spec, layer)
@@ -99,19 +115,25 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching
                 opool.append(p6, layer, H.raw16(kn), H.raw16(vn), dt, dt, slots)
                 ref = oattn.paged_decode(p6, layer, H.q_f64(q, dt), tables, lens, scale, dt)
                 H.assert_close(H.out_f64(outs[layer], dt), ref, dt, f"{name} it {it} layer {layer}")
-        if it % 5 == 0 or not (pending or prod.running or prod.waiting):
+        if (it % 5 == 0 or orc.swap_in or orc.swap_out
+                or not (pending or prod.running or prod.waiting or prod.swapped)):
             torch.cuda.synchronize()
             got = cache.buf.cpu().numpy()
             if not np.array_equal(got, host):
                 bad = np.flatnonzero(got != host)
                 raise AssertionError(f"{name} it {it}: {bad.size} pool bytes differ")
-        if not (pending or prod.running or prod.waiting):
+            if swap and not np.array_equal(swap.buf.numpy(), oswap.reshape(-1).view(np.uint8)):
+                raise AssertionError(f"{name} it {it}: swap space differs")
+        if not (pending or prod.running or prod.waiting or prod.swapped):
             break
     assert not prod.running and not pending and steps > 0
     assert copies > 0 or caching
-    if num_blocks == 16:
+    if num_blocks == 16 and not swap_slots:
         assert preempted > 0
     if caching:
         assert reused > 0
-    say(f"{name}: {steps} steps, {copies} copies, {preempted} preemptions, {reused} cached blocks")
+    if swap:
+        assert swapped > 0 and not prod.swapped and swap.num_free() == swap_slots
+    say(f"{name}: {steps} steps, {copies} copies, {preempted} preemptions, {swapped} swaps, "
+        f"{reused} cached blocks")
     cache.close()
