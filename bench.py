@@ -51,17 +51,17 @@ KERNEL_SOURCES = {
                                            "common.h")),
 }
 MEASURED_TRAFFIC = {  # workload -> counters of its decode kernel
-    "llama13b_layer": {  # FETCH 367,317.2 KiB x 1.99988 + WRITE 960.0 KiB
-        "kernel": "valu", "bytes": 753_203_615,
-        "sources_sha256": "90b812eec938fafa75c0ce42c67f458fb9bb357b7492cce527d8d4940d8edccc",
+    "llama13b_layer": {  # FETCH 367,297.2 KiB x 1.99992 + WRITE 960.0 KiB
+        "kernel": "valu", "bytes": 753_177_003,
+        "sources_sha256": "0afcdca6b4860c46430002feddd0a62efb828977ab6bf094007028e63c7aa37d",
         "summary": "profiles/decode_kernel_llama13b_layer.md"},
-    "longctx_fp8": {  # FETCH 715,694.3 KiB x 1.99998 + WRITE 5,755.0 KiB
-        "kernel": "valu", "bytes": 1_471_616_875,
-        "sources_sha256": "90b812eec938fafa75c0ce42c67f458fb9bb357b7492cce527d8d4940d8edccc",
+    "longctx_fp8": {  # FETCH 715,694.3 KiB x 1.99998 + WRITE 5,754.6 KiB
+        "kernel": "valu", "bytes": 1_471_616_465,
+        "sources_sha256": "0afcdca6b4860c46430002feddd0a62efb828977ab6bf094007028e63c7aa37d",
         "summary": "profiles/decode_kernel_longctx_fp8.md"},
-    "gqa_prefix": {  # streaming kernel: FETCH 408,992.4 KiB x 1.99995 + WRITE 12,219.0 KiB
-        "kernel": "balanced", "bytes": 850_105_846,
-        "sources_sha256": "5536736bab3814e0938ac46d9ce49efaaa1b37f48b8c3c3434578b0796b867ea",
+    "gqa_prefix": {  # streaming kernel: FETCH 409,090.2 KiB x 1.99995 + WRITE 12,219.7 KiB
+        "kernel": "balanced", "bytes": 850_307_011,
+        "sources_sha256": "c8a6905b28a7535238e1265a87ecbeba8d48d7aaae72797d8ac243c687df74d5",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
 }
 

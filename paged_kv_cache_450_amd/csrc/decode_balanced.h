@@ -428,14 +428,16 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
 // Second kernel of the balanced single pass: one workgroup per (kv head,
 // sequence). It recomputes the split of the batch into R ranges, and for a
 // context that was split merges the partials its waves left in their slots;
-// it also writes the zeros of an empty context. Contexts held by one wave
-// were written by the streaming kernel and are left alone. A thread owns 4
-// dims of one head; a long context is split over tens of waves, so both
-// passes over the partials (their maximum, then the weighted sum) keep
-// several independent loads in flight.
+// contexts written whole by one wave were stored by the streaming kernel and
+// are left alone. A thread owns 4 dims of one head and merges the partials
+// online, eight at a time: the loads of a group are all issued before any is
+// used, and the running (max, sum, output) is rescaled when a group raises the
+// maximum, so a context split over up to eight waves costs one round trip to
+// memory after the lengths.
 template <int KV, int D, int G>
 __global__ __launch_bounds__(256) void balanced_merge_kernel(const DecodeParams p) {
     constexpr int SS = SlotGeoB<D>::kStride;
+    constexpr int kGroup = 8;
     const int g = blockIdx.x, s = blockIdx.y, lane = threadIdx.x & 63;
     int64_t total = 0, before = 0;  // tiles per head of the batch, and of sequences < s
     for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
@@ -463,26 +465,43 @@ __global__ __launch_bounds__(256) void balanced_merge_kernel(const DecodeParams 
     for (int idx = t; idx < G * D / 4; idx += 256) {
         const int h = idx / (D / 4), d = (idx % (D / 4)) * 4;
         const float* base = p.slots + static_cast<size_t>(h) * SS;
-        auto part = [&](int v) -> const float* {
-            const int slot = v == wa ? slot_a : 0;
-            return base + static_cast<size_t>(v * 2 + slot) * G * SS;
-        };
-        float mx = -INFINITY;
-#pragma unroll 8
-        for (int v = wa; v <= wb; ++v) mx = fmaxf(mx, part(v)[D]);
-        const float ms = (mx == -INFINITY) ? 0.0f : mx;
-        float wsum = 0.0f;
+        float run_m = -INFINITY, run_l = 0.0f;
         float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll 4
-        for (int v = wa; v <= wb; ++v) {
-            const float* hs = part(v);
-            const float4 ov = *reinterpret_cast<const float4*>(hs + d);
-            const float wv = hs[D + 1] * fast_exp2(hs[D] - ms);
-            wsum += wv;
-            acc = make_float4(fmaf(wv, ov.x, acc.x), fmaf(wv, ov.y, acc.y), fmaf(wv, ov.z, acc.z),
-                              fmaf(wv, ov.w, acc.w));
+        for (int v0 = wa; v0 <= wb; v0 += kGroup) {
+            float mv[kGroup], lv[kGroup];
+            float4 ov[kGroup];
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) {
+                const int v = v0 + i;
+                if (v <= wb) {
+                    const int slot = v == wa ? slot_a : 0;
+                    const float* hs = base + static_cast<size_t>(v * 2 + slot) * G * SS;
+                    ov[i] = *reinterpret_cast<const float4*>(hs + d);
+                    mv[i] = hs[D];
+                    lv[i] = hs[D + 1];
+                } else {
+                    ov[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    mv[i] = -INFINITY;
+                    lv[i] = 0.0f;
+                }
+            }
+            float mx = run_m;
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) mx = fmaxf(mx, mv[i]);
+            const float ms = (mx == -INFINITY) ? 0.0f : mx;
+            const float a = fast_exp2(run_m - ms);  // 0 while nothing has been merged
+            run_l *= a;
+            acc = make_float4(acc.x * a, acc.y * a, acc.z * a, acc.w * a);
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) {
+                const float wv = lv[i] * fast_exp2(mv[i] - ms);
+                run_l += wv;
+                acc = make_float4(fmaf(wv, ov[i].x, acc.x), fmaf(wv, ov[i].y, acc.y),
+                                  fmaf(wv, ov[i].z, acc.z), fmaf(wv, ov[i].w, acc.w));
+            }
+            run_m = mx;
         }
-        const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+        const float inv = run_l > 0.0f ? 1.0f / run_l : 0.0f;
         *reinterpret_cast<uint2*>(out + h * D + d) =
             make_uint2(pack2<KV>(acc.x * inv, acc.y * inv), pack2<KV>(acc.z * inv, acc.w * inv));
     }
