@@ -407,7 +407,7 @@ def swap_rate(cfg, blocks: int, iters: int, stream) -> dict:
 
 
 def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False, swap_slots=0,
-                 pool_blocks=0, max_gen=128) -> dict:
+                 pool_blocks=0, max_gen=128, window=0) -> dict:
     """The continuous-batching loop (ContinuousBatcher) over a seeded request
     stream shaped like the workload: prompts of up to its longest context, 1 to
     max_gen generated tokens, a third of the requests with 2-3 samples, 4 arrivals
@@ -415,7 +415,8 @@ def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False, swap_slo
     times, are preempted). groups = (G, T): prompts in G prefix groups sharing
     their first T tokens (a system prompt); caching: admit through the prefix
     cache; swap_slots: preempt into a swap space of that many pinned host slots
-    (else by recomputation); pool_blocks > 0: a pool of that many blocks
+    (else by recomputation); window > 0: a sliding window of that many tokens
+    (blocks before it released every iteration); pool_blocks > 0: a pool of that many blocks
     instead (a tight pool forces preemption). Inputs are drawn before the timed region, which
     holds the bookkeeping (host) and the GPU work of every iteration."""
     import torch
@@ -432,7 +433,7 @@ def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False, swap_slo
                             mean_gap=0.25, prefix_groups=groups[0], shared_tokens=groups[1])
     cache = PagedKVCache(cfg.layers, nb, cfg.kv_heads, cfg.head_dim, cfg.kv_dtype, "cuda")
     swap = SwapSpace(cache, swap_slots) if swap_slots else None
-    loop = ContinuousBatcher(cache, width, prefix_caching=caching, swap=swap)
+    loop = ContinuousBatcher(cache, width, prefix_caching=caching, swap=swap, window=window)
     dt = cfg.src_dtype
     kp = W.normal((max_prompt, cfg.kv_heads, cfg.head_dim), dt, 1, "cuda")
     vp = W.normal((max_prompt, cfg.kv_heads, cfg.head_dim), dt, 2, "cuda")
@@ -457,6 +458,7 @@ def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False, swap_slo
     host_s = 0.0
     tokens = copies = preempted = prefill = reused = swapped_out = swapped_blocks = done = 0
     discarded = 0  # tokens generated by requests that recomputation then restarted
+    released = 0   # block references released by the window
     batches = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -480,6 +482,7 @@ def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False, swap_slo
         discarded += sum(gen.get(r, 0) for r in plan.preempted)
         swapped_out += len(plan.swapped_out)
         done += len(plan.finished)
+        released += plan.trimmed
         swapped_blocks += len(plan.swap_out_ids) + len(plan.swap_in_ids)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -490,7 +493,8 @@ def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False, swap_slo
             "host_plan_us_per_iteration": round(host_s / iters * 1e6, 1),
             "mean_batch": round(float(np.mean(batches)), 2), "max_batch": int(max(batches)),
             "copies": copies, "preemptions": preempted, "tokens_discarded": discarded,
-            "max_gen": max_gen, "swap_slots": swap_slots,
+            "max_gen": max_gen, "swap_slots": swap_slots, "window": window,
+            "blocks_released_by_window": released,
             "swapped_out": swapped_out, "blocks_swapped": swapped_blocks, "pool_blocks": nb,
             "prefix_caching": caching, "prefix_groups": list(groups),
             "prefill_tokens": prefill, "cached_blocks_reused": reused,
@@ -575,6 +579,8 @@ def main(argv=None):
                     help="run the serving loop on a pool of N blocks")
     ap.add_argument("--serve-gen", type=int, default=128, metavar="N",
                     help="longest generation of the serving stream's requests")
+    ap.add_argument("--serve-window", type=int, default=0, metavar="W",
+                    help="run the serving loop with a sliding window of W tokens")
     ap.add_argument("--window", default=None, metavar="W[,W...]",
                     help="also time the step with a sliding window of W tokens "
                          "(paged_attn_decode_window) on the same caches")
@@ -727,7 +733,8 @@ def main(argv=None):
     if args.serve > 0:
         groups = tuple(int(x) for x in args.serve_prefix.split(",")) if args.serve_prefix else (0, 0)
         result["serving"] = serving_rate(cfg, args.serve, stream, groups, args.serve_caching,
-                                         args.serve_swap, args.serve_blocks, args.serve_gen)
+                                         args.serve_swap, args.serve_blocks, args.serve_gen,
+                                         args.serve_window)
     if args.swap > 0:
         result["swap"] = swap_rate(cfg, args.swap, args.steps, stream)
     if args.block_copy > 0:

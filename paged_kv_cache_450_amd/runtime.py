@@ -22,7 +22,7 @@ from . import (BLOCK_SIZE, PKV_BF16, PKV_ERR_OOM, PKV_F16, PKV_FP8_E4M3, PkvErro
                block_alloc, block_free, block_incref,
                kv_block_copy, kv_cache_append, kv_pool_bytes, kv_pool_create, kv_pool_destroy,
                kv_pool_free_list, kv_pool_num_free, kv_prefix_acquire, kv_prefix_register,
-               kv_seq_extend, kv_seq_extend_cow, kv_seq_fork, kv_swap_in, kv_swap_out,
+               kv_seq_extend, kv_seq_extend_cow, kv_seq_fork, kv_seq_trim, kv_swap_in, kv_swap_out,
                kv_swap_slot_bytes,
                paged_attn_decode, paged_attn_decode_append, paged_attn_decode_window,
                paged_attn_reduce,
@@ -232,6 +232,7 @@ class IterationPlan:
     swap_in_ids: list = field(default_factory=list)
     swap_out_ids: list = field(default_factory=list)   # block -> slot, in order
     swap_out_slots: list = field(default_factory=list)
+    trimmed: int = 0                                   # block references a window released
 
 
 class SwapSpace:
@@ -259,17 +260,27 @@ class SwapSpace:
 
 def distinct_blocks(seqs):
     """The distinct block ids the sequences' rows hold, in order of first
-    appearance, and per sequence the index into them of each row entry."""
+    appearance, and per sequence the index into them of each row entry (-1
+    where a sliding window has released the block)."""
     order, index, maps = [], {}, []
     for s in seqs:
         m = []
         for b in s.row[:s.num_blocks].tolist():
+            if b < 0:
+                m.append(-1)
+                continue
             if b not in index:
                 index[b] = len(order)
                 order.append(b)
             m.append(index[b])
         maps.append(np.array(m, dtype=np.int64))
     return order, maps
+
+
+def held_blocks(s) -> np.ndarray:
+    """The block ids a sequence's row holds (entries a window released skipped)."""
+    r = s.row[:s.num_blocks]
+    return r[r >= 0]
 
 
 class ContinuousBatcher:
@@ -312,7 +323,11 @@ class ContinuousBatcher:
         first one's distinct blocks plus one block per running sequence (its
         own included) are free, it takes fresh blocks and the references its
         rows held, and gives back its slots; waiting requests are admitted
-        only when none is swapped out.
+        only when none is swapped out;
+      * with a sliding window of W tokens ("vLLM 也不是银弹：..."), every
+        iteration, after the growth, releases the blocks wholly before each
+        running sequence's last W positions (kv_seq_trim; their row entries
+        become -1), and the step attends over the last W positions only.
 
     plan() does the bookkeeping of an iteration on the host (block manager
     calls only); execute() then issues its GPU work on one stream: the prompt
@@ -322,11 +337,12 @@ class ContinuousBatcher:
     """
 
     def __init__(self, cache: PagedKVCache, max_blocks_per_seq: int, prefix_caching=False,
-                 swap: SwapSpace = None):
+                 swap: SwapSpace = None, window: int = 0):
         self.cache = cache
         self.width = max_blocks_per_seq
         self.prefix_caching = prefix_caching
         self.swap = swap
+        self.window = window
         self.swapped = []  # (rid, seqs, maps, slots), ordered by rid
         self.waiting = deque()
         self.running = []
@@ -343,7 +359,7 @@ class ContinuousBatcher:
         keep = []
         for s in self.running:
             if s.generated >= s.gen_len:
-                block_free(h, s.row[:s.num_blocks])
+                block_free(h, held_blocks(s))
                 p.finished.append((s.rid, s.sample))
             else:
                 keep.append(s)
@@ -357,8 +373,8 @@ class ContinuousBatcher:
             ids = block_alloc(h, len(slots))
             counts = np.zeros(len(slots), dtype=np.int64)
             for s, mp in zip(seqs, maps):
-                s.row[:mp.size] = ids[mp]
-                np.add.at(counts, mp, 1)
+                s.row[:mp.size] = np.where(mp >= 0, ids[np.maximum(mp, 0)], -1)
+                np.add.at(counts, mp[mp >= 0], 1)
             extra = np.repeat(ids, counts - 1)
             if extra.size:
                 block_incref(h, extra)
@@ -406,6 +422,8 @@ class ContinuousBatcher:
                 self._preempt_last(p)
         p.batch = list(self.running)
         if p.batch:
+            if self.window > 0:
+                p.trimmed = kv_seq_trim(h, tables, cur + 1, self.window)
             for k, s in enumerate(p.batch):
                 s.row[:] = tables[k]
                 s.length += 1
@@ -421,7 +439,7 @@ class ContinuousBatcher:
         seqs = [s for s in self.running if s.rid == rid]
         order, maps = distinct_blocks(seqs)
         for s in seqs:
-            block_free(self.cache.handle, s.row[:s.num_blocks])
+            block_free(self.cache.handle, held_blocks(s))
         self.running = [s for s in self.running if s.rid != rid]
         if (self.swap is not None and len(order) <= self.swap.num_free()
                 and all(a[0].rid != rid for a in p.admitted)):
@@ -470,7 +488,11 @@ class ContinuousBatcher:
             q, kn, vn = step_inputs(layer, len(plan.batch))
             out = torch.empty((len(plan.batch), num_q_heads, desc.head_dim), dtype=q.dtype,
                               device=dev)
-            paged_attn_decode_append(h, layer, kn, vn, q, out, tables, lens, sc, max_ctx, 0,
-                                     workspace, k_scale, v_scale, stream)
+            if self.window > 0:
+                paged_attn_decode_window(h, layer, q, out, tables, lens, sc, max_ctx, self.window,
+                                         0, workspace, k_scale, v_scale, kn, vn, stream)
+            else:
+                paged_attn_decode_append(h, layer, kn, vn, q, out, tables, lens, sc, max_ctx, 0,
+                                         workspace, k_scale, v_scale, stream)
             outs.append(out)
         return outs

@@ -18,6 +18,10 @@ distinct blocks plus one block per running sequence (its own included) are
 free, it takes fresh blocks (one alloc), the references its rows hold, and
 gives its slots back in order; waiting requests are admitted only when no
 request is swapped out.
+
+With a sliding window of W tokens, every iteration after the growth releases
+the blocks wholly before each running sequence's last W positions
+(AllocatorModel.trim; row entries become -1).
 """
 
 from collections import deque
@@ -33,13 +37,20 @@ class OracleSeq:
         self.length, self.gen_len, self.generated = length, gen_len, 0
 
 
+def held(s):
+    return [b for b in s.row[: -(-s.length // BS)] if b >= 0]
+
+
 def distinct_blocks(seqs):
     """Distinct block ids over the rows, in order of first appearance, and
-    per sequence the index of each row entry in that list."""
+    per sequence the index of each row entry in that list (-1: released)."""
     order, index, maps = [], {}, []
     for s in seqs:
         m = []
         for b in s.row[: -(-s.length // BS)]:
+            if b < 0:
+                m.append(-1)
+                continue
             if b not in index:
                 index[b] = len(order)
                 order.append(b)
@@ -49,7 +60,7 @@ def distinct_blocks(seqs):
 
 
 class OracleBatcher:
-    def __init__(self, num_blocks, width, prefix_caching=False, swap_slots=0):
+    def __init__(self, num_blocks, width, prefix_caching=False, swap_slots=0, window=0):
         self.model = A.AllocatorModel(num_blocks, BS)
         self.width = width
         self.prefix_caching = prefix_caching
@@ -61,6 +72,8 @@ class OracleBatcher:
         self.swap_in = []   # this iteration's (slot, block) pairs
         self.swap_out = []  # this iteration's (block, slot) pairs
         self.swapped_in, self.swapped_out = [], []
+        self.window = window
+        self.trimmed = 0
 
     def submit(self, spec):
         self.waiting.append(spec)
@@ -71,12 +84,13 @@ class OracleBatcher:
         still = []
         for s in self.running:
             if s.generated >= s.gen_len:
-                m.free(s.row[: -(-s.length // BS)])
+                m.free(held(s))
                 finished.append((s.rid, s.sample))
             else:
                 still.append(s)
         self.running = still
         self.swap_in, self.swap_out, self.swapped_in, self.swapped_out = [], [], [], []
+        self.trimmed = 0
         while self.swapped:
             rid, seqs, maps, slots = self.swapped[0]
             if m.num_free() - len(slots) < len(self.running) + len(seqs):
@@ -86,8 +100,9 @@ class OracleBatcher:
             extra = []
             for s, mp in zip(seqs, maps):
                 for j, u in enumerate(mp):
-                    s.row[j] = ids[u]
-                    extra.append(ids[u])
+                    s.row[j] = ids[u] if u >= 0 else -1
+                    if u >= 0:
+                        extra.append(ids[u])
             for b in ids:  # one reference came with the alloc
                 extra.remove(b)
             m.incref(extra)
@@ -129,7 +144,7 @@ class OracleBatcher:
                 seqs = [s for s in self.running if s.rid == rid]
                 order, maps = distinct_blocks(seqs)
                 for s in seqs:
-                    m.free(s.row[: -(-s.length // BS)])
+                    m.free(held(s))
                 self.running = [s for s in self.running if s.rid != rid]
                 if (self.swap_free is not None and len(order) <= len(self.swap_free)
                         and all(a[0].rid != rid for a in admitted)):
@@ -144,6 +159,8 @@ class OracleBatcher:
                 preempted.append(rid)
                 self.waiting.appendleft(self.specs[rid])
                 continue
+            self.trimmed = (m.trim(rows, [c + 1 for c in cur], self.window)
+                            if self.window else 0)
             for s, r in zip(self.running, rows):
                 s.row = r
                 s.length += 1

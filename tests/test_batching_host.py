@@ -14,26 +14,29 @@ from tests.oracle_loop import OracleBatcher
 
 # 18 blocks: the largest request (4 prompt blocks, 3 samples each growing by
 # 3 blocks plus a copy) fits alone, so preemption always makes progress.
-@pytest.mark.parametrize("seed,num_blocks,caching,swap_slots", [
-    (0, 40, False, 0), (1, 64, False, 0), (2, 24, False, 0), (3, 200, False, 0),
-    (4, 18, False, 0), (5, 40, True, 0), (6, 24, True, 0), (7, 120, True, 0),
-    (4, 18, False, 64), (12, 18, False, 8), (12, 18, False, 2), (6, 24, True, 16),
-    (14, 20, True, 40)])
-def test_loop_bookkeeping_matches_oracle(seed, num_blocks, caching, swap_slots):
+@pytest.mark.parametrize("seed,num_blocks,caching,swap_slots,window", [
+    (0, 40, False, 0, 0), (1, 64, False, 0, 0), (2, 24, False, 0, 0), (3, 200, False, 0, 0),
+    (4, 18, False, 0, 0), (5, 40, True, 0, 0), (6, 24, True, 0, 0), (7, 120, True, 0, 0),
+    (4, 18, False, 64, 0), (12, 18, False, 8, 0), (12, 18, False, 2, 0), (6, 24, True, 16, 0),
+    (14, 20, True, 40, 0), (4, 18, False, 0, 40), (12, 18, False, 8, 33), (6, 24, True, 16, 17),
+    (3, 30, True, 0, 1), (12, 14, False, 32, 40)])
+def test_loop_bookkeeping_matches_oracle(seed, num_blocks, caching, swap_slots, window):
     """With caching, the trace's requests come in prefix groups sharing a
     48-token system prompt, admitted through the prefix cache. With swap
     slots, preempted requests go to the swap space when they fit there (a
-    small space forces the fallback to recomputation too)."""
+    small space forces the fallback to recomputation too). With a window,
+    every iteration releases the blocks before each sequence's window."""
     groups = (3, 48) if caching else (0, 0)
     trace = W.request_trace("batching_host", seed, 60, max_prompt=60, max_gen=40,
                             prefix_groups=groups[0], shared_tokens=groups[1])
     width = -(-(60 + 40) // 16)
     cache = PagedKVCache(1, num_blocks, 2, 64, "f16", device=None)  # bookkeeping only
     swap = SwapSpace(cache, swap_slots, pinned=False) if swap_slots else None
-    prod = ContinuousBatcher(cache, width, prefix_caching=caching, swap=swap)
-    orc = OracleBatcher(num_blocks, width, prefix_caching=caching, swap_slots=swap_slots)
+    prod = ContinuousBatcher(cache, width, prefix_caching=caching, swap=swap, window=window)
+    orc = OracleBatcher(num_blocks, width, prefix_caching=caching, swap_slots=swap_slots,
+                        window=window)
     pending = list(trace)
-    copies = admitted = finished = preempted = reused = swapped = 0
+    copies = admitted = finished = preempted = reused = swapped = trimmed = 0
     for it in range(3000):
         while pending and pending[0].arrival <= it:
             prod.submit(pending[0])
@@ -48,6 +51,8 @@ def test_loop_bookkeeping_matches_oracle(seed, num_blocks, caching, swap_slots):
             assert swap.free == orc.swap_free
         preempted += len(pre)
         swapped += len(orc.swapped_out)
+        assert p.trimmed == orc.trimmed
+        trimmed += p.trimmed
         assert [(a[0].rid, a[1]) for a in p.admitted] == [(a[0].rid, a[1]) for a in adm]
         for a, b in zip(p.admitted, adm):
             assert np.array_equal(a[2], np.array(b[2], dtype=np.int64))
@@ -70,10 +75,13 @@ def test_loop_bookkeeping_matches_oracle(seed, num_blocks, caching, swap_slots):
     # every request ran to the end; preempted ones were admitted again
     assert admitted == len(trace) + preempted and not prod.running and not prod.swapped
     assert copies > 0 and finished > 0
-    if num_blocks == 18 and not swap_slots:
+    if num_blocks == 18 and not swap_slots and not window:
         assert preempted > 0  # this pool does run out
     if swap_slots:
-        assert swapped > 0 and swap.num_free() == swap_slots
+        assert swap.num_free() == swap_slots
+        assert swapped > 0 or window  # a window can relieve the pool enough
+    if window:
+        assert trimmed > 0
     if swap_slots == 2:
         assert preempted > 0  # too few slots: some preemptions recompute
     assert P.kv_pool_num_free(cache.handle) == num_blocks  # every block came back

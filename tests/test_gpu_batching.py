@@ -38,16 +38,21 @@ def _gpu(require_gpu):
 # trace) yet holds the largest request alone. The last two run with prefix
 # caching: requests in groups sharing a 48-token system prompt, admitted
 # through the cache (the second pool small enough to evict cached blocks).
-# The last three preempt into a swap space of pinned host memory (swap-outs
-# and swap-ins through kv_swap_out / kv_swap_in), with prefix caching on two.
-@pytest.mark.parametrize("dt,hq,hkv,dim,num_blocks,max_gen,caching,swap_slots", [
-    ("f16", 2, 2, 64, 48, 12, False, 0), ("bf16", 8, 2, 128, 30, 12, False, 0),
-    ("f16", 4, 4, 128, 16, 40, False, 0), ("bf16", 8, 2, 128, 40, 12, True, 0),
-    ("f16", 2, 2, 64, 20, 12, True, 0), ("f16", 4, 4, 128, 16, 40, False, 64),
-    ("bf16", 8, 2, 128, 18, 40, True, 64), ("f16", 2, 2, 64, 14, 40, True, 32)])
-def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching, swap_slots):
+# Three preempt into a swap space of pinned host memory (swap-outs and
+# swap-ins through kv_swap_out / kv_swap_in), with prefix caching on two. The
+# last three run with a sliding window: blocks before each window released
+# every iteration (kv_seq_trim), the step through paged_attn_decode_window.
+@pytest.mark.parametrize("dt,hq,hkv,dim,num_blocks,max_gen,caching,swap_slots,window", [
+    ("f16", 2, 2, 64, 48, 12, False, 0, 0), ("bf16", 8, 2, 128, 30, 12, False, 0, 0),
+    ("f16", 4, 4, 128, 16, 40, False, 0, 0), ("bf16", 8, 2, 128, 40, 12, True, 0, 0),
+    ("f16", 2, 2, 64, 20, 12, True, 0, 0), ("f16", 4, 4, 128, 16, 40, False, 64, 0),
+    ("bf16", 8, 2, 128, 18, 40, True, 64, 0), ("f16", 2, 2, 64, 14, 40, True, 32, 0),
+    ("f16", 4, 4, 128, 16, 40, False, 0, 40), ("bf16", 8, 2, 128, 18, 40, True, 64, 33),
+    ("f16", 2, 2, 64, 14, 40, True, 32, 17)])
+def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching, swap_slots,
+                                  window):
     name = f"batching_{dt}_{hq}_{hkv}_{dim}_{num_blocks}_{caching}"
-    say(f"{name} swap_slots={swap_slots}")
+    say(f"{name} swap_slots={swap_slots} window={window}")
     layers, max_prompt = 2, 40
     width = -(-(max_prompt + 48 + max_gen) // 16)
     groups = (3, 48) if caching else (0, 0)
@@ -55,8 +60,9 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching
                             shared_tokens=groups[1])
     cache = PagedKVCache(layers, num_blocks, hkv, dim, dt, "cuda", fill_byte=H.POISON)
     swap = SwapSpace(cache, swap_slots) if swap_slots else None
-    prod = ContinuousBatcher(cache, width, prefix_caching=caching, swap=swap)
-    orc = OracleBatcher(num_blocks, width, prefix_caching=caching, swap_slots=swap_slots)
+    prod = ContinuousBatcher(cache, width, prefix_caching=caching, swap=swap, window=window)
+    orc = OracleBatcher(num_blocks, width, prefix_caching=caching, swap_slots=swap_slots,
+                        window=window)
     host = np.full(opool.pool_bytes(layers, num_blocks, 16, hkv, dim, dt), H.POISON, dtype=np.uint8)
     p6 = opool.view_pool(host, layers, num_blocks, 16, hkv, dim, dt)
     if swap:
@@ -67,7 +73,7 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching
     wsb = P.paged_attn_workspace_bytes(1, hq, dim, 1, 0)
     workspace = torch.empty(wsb // 4, dtype=torch.float32, device="cuda")
     pending = list(trace)
-    steps = preempted = copies = reused = swapped = 0
+    steps = preempted = copies = reused = swapped = trimmed = 0
     for it in range(1000):
         while pending and pending[0].arrival <= it:
             prod.submit(pending[0])
@@ -79,6 +85,8 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching
         assert list(zip(p.swap_in_slots, p.swap_in_ids)) == orc.swap_in
         assert list(zip(p.swap_out_ids, p.swap_out_slots)) == orc.swap_out
         swapped += len(orc.swapped_out)
+        assert p.trimmed == orc.trimmed
+        trimmed += p.trimmed
         assert [(s.rid, s.sample, s.length) for s in p.batch] == \
             [(s.rid, s.sample, s.length) for s in batch]
         preempted += len(pre)
@@ -113,7 +121,8 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching
             for layer in range(layers):
                 q, kn, vn = step_inputs(layer, len(batch))
                 opool.append(p6, layer, H.raw16(kn), H.raw16(vn), dt, dt, slots)
-                ref = oattn.paged_decode(p6, layer, H.q_f64(q, dt), tables, lens, scale, dt)
+                ref = oattn.paged_decode(p6, layer, H.q_f64(q, dt), tables, lens, scale, dt,
+                                         window=window)
                 H.assert_close(H.out_f64(outs[layer], dt), ref, dt, f"{name} it {it} layer {layer}")
         if (it % 5 == 0 or orc.swap_in or orc.swap_out
                 or not (pending or prod.running or prod.waiting or prod.swapped)):
@@ -128,12 +137,15 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching
             break
     assert not prod.running and not pending and steps > 0
     assert copies > 0 or caching
-    if num_blocks == 16 and not swap_slots:
+    if num_blocks == 16 and not swap_slots and not window:
         assert preempted > 0
     if caching:
         assert reused > 0
     if swap:
-        assert swapped > 0 and not prod.swapped and swap.num_free() == swap_slots
+        assert not prod.swapped and swap.num_free() == swap_slots
+        assert swapped > 0 or window
+    if window:
+        assert trimmed > 0
     say(f"{name}: {steps} steps, {copies} copies, {preempted} preemptions, {swapped} swaps, "
-        f"{reused} cached blocks")
+        f"{reused} cached blocks, {trimmed} blocks released by the window")
     cache.close()

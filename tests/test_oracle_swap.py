@@ -65,11 +65,11 @@ def test_round_trip_equals_block_copy():
 
 
 # ------------------------------------------------------------- the loop ----
-def run_trace(batcher_cls, seed, num_blocks, swap_slots, caching=False):
+def run_trace(batcher_cls, seed, num_blocks, swap_slots, caching=False, window=0):
     groups = (3, 48) if caching else (0, 0)
     trace = W.request_trace("batching_host", seed, 60, max_prompt=60, max_gen=40,
                             prefix_groups=groups[0], shared_tokens=groups[1])
-    o = batcher_cls(num_blocks, 7, prefix_caching=caching, swap_slots=swap_slots)
+    o = batcher_cls(num_blocks, 7, prefix_caching=caching, swap_slots=swap_slots, window=window)
     tok = np.full(num_blocks * BS, -1, dtype=np.int64)
     host = np.full((max(swap_slots, 1), BS), -1, dtype=np.int64)
 
@@ -106,15 +106,20 @@ def run_trace(batcher_cls, seed, num_blocks, swap_slots, caching=False):
         held = {}
         for s in batch:
             plen = o.specs[s.rid].prompt_len
-            for pos in range(s.length):
+            lo = max(0, s.length - window) if window else 0
+            for pos in range(lo, s.length):
                 got = tok[s.row[pos // BS] * BS + pos % BS]
                 assert got == expected(s.rid, s.sample, plen, pos), (it, s.rid, s.sample, pos)
-            for b in s.row[: -(-s.length // BS)]:
-                held[b] = held.get(b, 0) + 1
+            for j, b in enumerate(s.row[: -(-s.length // BS)]):
+                if b >= 0:
+                    held[b] = held.get(b, 0) + 1
+                else:  # only blocks wholly before the window are released
+                    assert window and BS * (j + 1) <= s.length - window, (it, s.rid, j)
         for rid, seqs, maps, hs in o.swapped:
             plen = o.specs[rid].prompt_len
             for s, mp in zip(seqs, maps):
-                for pos in range(s.length):
+                lo = max(0, s.length - window) if window else 0
+                for pos in range(lo, s.length):
                     got = host[hs[mp[pos // BS]], pos % BS]
                     assert got == expected(rid, s.sample, plen, pos), (it, rid, pos)
         for b in range(num_blocks):
@@ -130,6 +135,29 @@ def run_trace(batcher_cls, seed, num_blocks, swap_slots, caching=False):
     (14, 20, 40, True), (13, 18, 64, False)])
 def test_swap_trace_keeps_every_history(seed, num_blocks, swap_slots, caching):
     assert run_trace(OracleBatcher, seed, num_blocks, swap_slots, caching) > 0
+
+
+@pytest.mark.parametrize("seed,num_blocks,swap_slots,caching,window", [
+    (12, 18, 8, False, 33), (12, 14, 32, False, 40), (4, 18, 64, False, 24),
+    (6, 24, 16, True, 17), (3, 30, 0, True, 1)])
+def test_window_trace_keeps_every_window(seed, num_blocks, swap_slots, caching, window):
+    """The loop with a sliding window (blocks before each window released every
+    iteration), with swap and prefix caching: every running sequence gathers
+    the last W tokens of its history, released entries are only ever wholly
+    before the window, refcounts equal the references the rows hold."""
+    run_trace(OracleBatcher, seed, num_blocks, swap_slots, caching, window)
+
+
+def test_planted_eager_trim_fails_the_window_trace():
+    class Eager(OracleBatcher):  # releases one block too many
+        def plan(self):
+            self.window = max(1, self.window - BS)
+            try:
+                return super().plan()
+            finally:
+                self.window += BS
+    with pytest.raises(AssertionError):
+        run_trace(Eager, 12, 18, 8, False, 33)
 
 
 def test_planted_swap_in_mistakes_fail_the_trace():
