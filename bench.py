@@ -302,29 +302,48 @@ def cpu_baseline(w: Workload, budget_s: float):
         opool.append(p6, 0, raw(w.k_new[0][i:i + 1]), raw(w.v_new[0][i:i + 1]), cfg.src_dtype,
                      cfg.kv_dtype, ob.slots_new[i:i + 1], ks, vs)
         todo.append((i, opool.raw_to_f64(raw(w.q[0][i:i + 1]), cfg.q_dtype)))
-    # Whole passes over those sequences until about budget_s of oracle decode.
-    elapsed, done_bytes, seqs, passes = 0.0, 0, 0, 0
-    while elapsed < budget_s and todo:
-        for i, q in todo:
-            t0 = time.perf_counter()
-            oattn.paged_decode(p6, 0, q, ob.tables[i:i + 1], ob.lens[i:i + 1], scale,
-                               cfg.kv_dtype, ks, vs)
-            elapsed += time.perf_counter() - t0
-            done_bytes += int(ob.lens[i]) * cfg.kv_heads * cfg.head_dim * 2 * esz
-            seqs += 1
-            if elapsed >= budget_s:
-                break
-        passes += 1
-    return {
-        "value": round(done_bytes / elapsed / 1e9, 4),
-        "unit": "GB/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"{seqs} sequence decodes ({passes} passes over the {len(todo)} sequences of "
-                  f"{cfg.name} layer 0; {done_bytes / 1e6:.1f} MB of KV), fp64 numpy decode "
-                  f"only, {elapsed:.1f} s",
-        "seqs_per_s": round(seqs / elapsed, 3),
-    }
+    def run(budget):
+        """Whole passes over those sequences until about budget s of oracle decode."""
+        elapsed, done_bytes, seqs, passes = 0.0, 0, 0, 0
+        while elapsed < budget and todo:
+            for i, q in todo:
+                t0 = time.perf_counter()
+                oattn.paged_decode(p6, 0, q, ob.tables[i:i + 1], ob.lens[i:i + 1], scale,
+                                   cfg.kv_dtype, ks, vs)
+                elapsed += time.perf_counter() - t0
+                done_bytes += int(ob.lens[i]) * cfg.kv_heads * cfg.head_dim * 2 * esz
+                seqs += 1
+                if elapsed >= budget:
+                    break
+            passes += 1
+        return {"value": round(done_bytes / elapsed / 1e9, 4),
+                "seqs_per_s": round(seqs / elapsed, 3),
+                "sample": f"{seqs} sequence decodes ({passes} passes over the {len(todo)} "
+                          f"sequences of {cfg.name} layer 0; {done_bytes / 1e6:.1f} MB of KV), "
+                          f"fp64 numpy decode only, {elapsed:.1f} s"}
+
+    every = run(budget_s)
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            single = run(budget_s / 2)
+    except ImportError:
+        pass
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         "")
+    except OSError:
+        pass
+    out = {"value": every["value"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": every["sample"], "seqs_per_s": every["seqs_per_s"],
+           "cpu_count": os.cpu_count(), "cpu_model": model}
+    if single is not None:
+        out["single_thread"] = {"value": single["value"], "unit": "GB/s", "cores": 1,
+                                "seqs_per_s": single["seqs_per_s"], "sample": single["sample"]}
+    return out
 
 
 def block_copy_rate(cfg, pairs: int, iters: int, stream) -> dict:
@@ -677,6 +696,21 @@ def main(argv=None):
     append_us = per_launch_us(lambda w, l: w.append(l, stream))
     reduce_us = (per_launch_us(lambda w, l: w.reduce(stream))
                  if first.partition_size > 0 else 0.0)
+    # Distribution of the decode call's duration: one event pair around each of
+    # K launches (outside the timed region; each pair adds a little GPU time).
+    call_us = []
+    for i in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w = ws[i % reps]
+        a.record(stream)
+        if fused:
+            w.decode_append(i % nl, stream)
+        else:
+            w.decode(i % nl, stream)
+        b.record(stream)
+        call_us.append((a, b))
+    torch.cuda.synchronize()
+    call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in call_us])
     per_layer_bytes = sum(kv_bytes) / reps / nl
     # The roofline counts the bytes that must come from HBM: a shared prefix once.
     per_layer_unique = sum(kv_unique) / reps / nl
@@ -714,7 +748,12 @@ def main(argv=None):
         "seqs_per_s": round(cfg.batch / (ms_per_step * 1e-3), 1),
         "gpu_ms_per_step": round(gpu_ms_per_step, 5),
         "kernel_us": {"decode": round(decode_us, 3), "append_separate": round(append_us, 3),
-                      "reduce": round(reduce_us, 3)},
+                      "reduce": round(reduce_us, 3),
+                      "decode_p10_p50_p90": [round(float(np.percentile(call_us, q)), 3)
+                                             for q in (10, 50, 90)]},
+        "algorithmic_flops_per_step": int(4 * sum(int(w.lens.astype(np.int64).sum())
+                                                  for w in ws) / reps * cfg.q_heads
+                                          * cfg.head_dim * cfg.layers),
         "roofline": {
             "bound": "hbm",
             "kernel": decode_kernel_name(cfg, first),
