@@ -68,12 +68,27 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ml
             }
             wsum += wl;
             const int cnt = min(64, np - p0);
-            for (int k = 0; k < cnt; ++k) {
-                const float wk =
-                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k));
-                const float* op = o + (base + p0 + k) * D + lane * DPL;
+            // Eight partitions per round: their o loads are all issued before
+            // the first is used (one memory latency per round, not per partition).
+            for (int k0 = 0; k0 < cnt; k0 += 8) {
+                float ov[8][DPL];
 #pragma unroll
-                for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wk, op[e], acc[e]);
+                for (int u = 0; u < 8; ++u) {
+                    const float* op = o + (base + p0 + min(k0 + u, cnt - 1)) * D + lane * DPL;
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) ov[u][e] = op[e];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    // partitions past cnt re-read the last one and get weight 0
+                    const float wk = k0 + u < cnt
+                                         ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                                         __builtin_bit_cast(int, wl),
+                                                                         k0 + u))
+                                         : 0.0f;
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wk, ov[u][e], acc[e]);
+                }
             }
         }
     }
