@@ -88,7 +88,8 @@ class Workload:
     """One decode-step workload, product side: pool, tables, inputs, batch."""
 
     def __init__(self, cfg, seed=0, device="cuda", partition_size=None, fill_byte=None,
-                 placement_seed=None, keep_cached_inputs=True, balanced=None, fused=True):
+                 placement_seed=None, keep_cached_inputs=True, balanced=None, fused=True,
+                 shared_prefix=None):
         import torch
 
         import workloads as W
@@ -120,9 +121,15 @@ class Workload:
         self.k_cached, self.v_cached = [], []
         self.k_scale, self.v_scale = [], []
         n_cached = int(self.slots_cached.size)
+        balanced = cfg.balanced if balanced is None else balanced
+        # shared_prefix: the balanced single pass on a 16-bit cache reads the
+        # blocks its sequences share once (paged_attn_decode_prefix).
+        shared = cfg.shared_prefix if shared_prefix is None else shared_prefix
+        shared = bool(shared and balanced and self.partition_size == 0 and
+                      cfg.kv_dtype != "e4m3")
         self.batch = DecodeBatch(self.cache, self.tables, lens, cfg.q_heads, qdt,
-                                 self.partition_size, device=device,
-                                 balanced=cfg.balanced if balanced is None else balanced)
+                                 self.partition_size, device=device, balanced=balanced,
+                                 shared_prefix=shared)
         for layer in range(cfg.layers):
             kc = W.kv_tokens(cfg, seed, layer, "k", "cached", n_cached, device)
             vc = W.kv_tokens(cfg, seed, layer, "v", "cached", n_cached, device)
@@ -197,6 +204,8 @@ def decode_kernel_name(cfg, w) -> str:
     """The kernel(s) one paged_attn_decode call of this workload runs."""
     grouped = cfg.q_heads > cfg.kv_heads and cfg.kv_dtype != "e4m3"
     if w.partition_size == 0 and w.batch.balanced:
+        if w.batch.plan is not None and w.batch.plan.num_groups > 0:
+            return "prefix_kernel + decode_balanced_kernel + balanced_merge_kernel"
         return "decode_balanced_kernel + balanced_merge_kernel"
     return "decode_mfma_kernel" if grouped else "decode_kernel"
 
@@ -606,6 +615,9 @@ def main(argv=None):
     ap.add_argument("--unfused", action="store_true",
                     help="run a step as kv_cache_append + paged_attn_decode instead of the "
                          "fused paged_attn_decode_append")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="read blocks that several sequences share once per step "
+                         "(paged_attn_decode_prefix) instead of once per sequence")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -631,11 +643,14 @@ def main(argv=None):
     torch.cuda.set_device(0)
     fused = not args.unfused
     first = Workload(cfg, args.seed, "cuda", args.partition_size,
-                     keep_cached_inputs=False if args.no_cpu_baseline else "first", fused=fused)
+                     keep_cached_inputs=False if args.no_cpu_baseline else "first", fused=fused,
+                     shared_prefix=True if args.shared_prefix else None)
     pool_bytes = first.cache.nbytes
     reps = args.replicas or max(1, min(8, math.ceil(2e9 / max(pool_bytes, 1))))
     ws = [first] + [Workload(cfg, args.seed + r, "cuda", args.partition_size,
-                             keep_cached_inputs=False, fused=fused) for r in range(1, reps)]
+                             keep_cached_inputs=False, fused=fused,
+                             shared_prefix=True if args.shared_prefix else None)
+                    for r in range(1, reps)]
     kv_bytes = [w.kv_bytes() for w in ws]
     kv_unique = [w.kv_unique_bytes() for w in ws]
     stream = torch.cuda.current_stream()
@@ -738,6 +753,10 @@ def main(argv=None):
             "kv_dtype": cfg.kv_dtype, "q_dtype": cfg.q_dtype,
             "context_lens": list(cfg.lengths),
             "partition_size": first.partition_size,
+            "shared_prefix": ({"groups": first.batch.plan.num_groups,
+                               "members": int(first.batch.plan.group_offsets[-1]),
+                               "blocks": first.batch.plan.group_blocks.tolist()}
+                              if first.batch.plan is not None else None),
             "append": "fused into decode" if fused else "separate kernel",
             "replicas": reps, "pool_bytes_per_replica": pool_bytes,
             "kv_bytes_per_step": int(sum(kv_bytes) / reps),

@@ -429,6 +429,71 @@ pkv_status paged_attn_decode_window(const pkv_pool* pool, int32_t layer, const v
                                     void* workspace, size_t workspace_bytes, int32_t window,
                                     hipStream_t stream);
 
+/* Shared-prefix planning (host). [P2] "PagedAttention：...": sequences that
+ * share a prompt map the same physical blocks (refcounted), so a decode step
+ * can read those blocks once for all of them (paged_attn_decode_prefix).
+ * Groups sequences by the id of their first block (host arrays:
+ * block_tables [num_seqs][max_blocks_per_seq], context_lens [num_seqs]); a
+ * group's shared run P is the longest run of leading blocks that every member
+ * maps to the same ids, at most each member's full blocks before the block of
+ * its last token, (min(L_i, max_context_len, max_blocks_per_seq*16) - 1) / 16.
+ * Groups of two or more members with P >= min_blocks (>= 1) are kept, in the
+ * order of their first member; members in increasing index.
+ * Outputs (host, caller-owned): seq_prefix_blocks [num_seqs] (P of the
+ *   sequence's group, else 0); group_offsets [num_seqs + 1] (group k's members
+ *   are group_members[group_offsets[k] .. group_offsets[k+1])); group_members
+ *   [num_seqs]; group_blocks [num_seqs] (P per group); num_groups;
+ *   max_group_size (largest group, 0 if none).
+ * Errors: INVALID (negative sizes, min_blocks < 1, NULL arrays). */
+pkv_status paged_attn_prefix_plan(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t max_context_len, int32_t min_blocks,
+                                  int32_t* seq_prefix_blocks, int32_t* group_offsets,
+                                  int32_t* group_members, int32_t* group_blocks,
+                                  int32_t* num_groups, int32_t* max_group_size);
+
+/* Workspace bytes of paged_attn_decode_prefix: the balanced pass's slots
+ * (paged_attn_workspace_bytes(..., 0)), then two regions of
+ * num_seqs * num_q_heads * (head_dim + 4) fp32 (the prefix partials, and the
+ * members' suffix partials), each from a 256-byte boundary. 0 when an
+ * argument is out of range (num_seqs > 4096). */
+size_t paged_attn_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t head_dim);
+
+/* Decode step with shared-prefix reads: the same result as
+ * paged_attn_decode_append (new_k / new_v given) or paged_attn_decode
+ * (both NULL) in the balanced single pass, on a 16-bit cache. A prefix kernel
+ * reads the P shared leading blocks of each group once (all workgroups of a
+ * (group, kv head) on one XCD, so repeats come from its L2) and computes, for
+ * every member and query head, the partial (m, l, o) over those P*16 tokens on
+ * matrix cores, 16 query rows at a time; the balanced pass reads each member
+ * from block P on; the merge kernel joins the two with the log-sum-exp rule.
+ * Group arguments (device int32, as paged_attn_prefix_plan writes them):
+ *   seq_prefix_blocks [num_seqs], group_offsets [num_groups + 1],
+ *   group_members, group_blocks [num_groups]; max_group_size bounds every
+ *   group's size. num_groups == 0: no prefix kernel, the arrays are ignored.
+ * Preconditions (not checked, as they live in device memory): the rows of a
+ *   group's members hold the same ids in blocks [0, P); every member has
+ *   1 <= P <= (L_i - 1) / 16 and seq_prefix_blocks = P; every other sequence
+ *   has seq_prefix_blocks = 0; a sequence is in at most one group.
+ * workspace: device, 256-byte aligned, >= paged_attn_prefix_workspace_bytes;
+ *   no initial contents needed; calls that share it must be ordered on one
+ *   stream. Scale and dtypes: as paged_attn_decode (k_scale / v_scale are not
+ *   taken: no FP8).
+ * Errors: INVALID (an FP8 cache, num_seqs > 4096, group sizes out of range,
+ *   NULL group arrays with num_groups > 0, a NULL or small workspace, and every
+ *   error of paged_attn_decode_append), HIP. */
+pkv_status paged_attn_decode_prefix(const pkv_pool* pool, int32_t layer, const void* new_k,
+                                    const void* new_v, int32_t src_dtype, const void* q,
+                                    int32_t q_dtype, void* out, const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, float scale,
+                                    int32_t max_context_len, const int32_t* seq_prefix_blocks,
+                                    const int32_t* group_offsets, const int32_t* group_members,
+                                    const int32_t* group_blocks, int32_t num_groups,
+                                    int32_t max_group_size, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
 /* Merge the partitions a partitioned paged_attn_decode left in workspace
  * into out (device [num_seqs][num_q_heads][head_dim] of out_dtype F16 or BF16):
  *   M = max_p m_p, w_p = l_p exp(m_p - M), out = sum_p w_p o_p / sum_p w_p

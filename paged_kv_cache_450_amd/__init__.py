@@ -22,6 +22,8 @@ __all__ = [
     "kv_pool_free_list", "block_alloc", "block_free", "block_incref", "block_refcount",
     "kv_seq_fork", "kv_seq_extend", "kv_cache_append", "paged_attn_workspace_bytes",
     "paged_attn_decode", "paged_attn_reduce", "pkv_last_error", "library_path", "lib",
+    "PrefixPlan", "paged_attn_prefix_plan", "paged_attn_prefix_workspace_bytes",
+    "paged_attn_decode_prefix",
 ]
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_STATE, PKV_ERR_HIP = 0, -1, -2, -3, -4
@@ -94,6 +96,11 @@ def _load():
         "paged_attn_decode_append": (i32, [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, i32,
                                            i32, f32, vp, vp, i32, i32, vp, sz, vp]),
         "paged_attn_reduce": (i32, [vp, vp, i32, vp, i32, i32, i32, i32, i32, vp]),
+        "paged_attn_prefix_plan": (i32, [p_i32, i32, p_i32, i32, i32, i32, p_i32, p_i32, p_i32,
+                                         p_i32, p_i32, p_i32]),
+        "paged_attn_prefix_workspace_bytes": (sz, [i32, i32, i32]),
+        "paged_attn_decode_prefix": (i32, [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, i32,
+                                           i32, f32, i32, vp, vp, vp, vp, i32, i32, vp, sz, vp]),
         "pkv_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -461,3 +468,81 @@ def paged_attn_reduce(workspace, out, context_lens, max_context_len: int, partit
     _check(lib.paged_attn_reduce(_ptr(workspace), _ptr(out), _dtype_code(out), _ptr(context_lens),
                                  out.shape[0], out.shape[1], out.shape[2], max_context_len,
                                  partition_size, _stream(stream)))
+
+
+# ------------------------------------------------------- shared prefixes ----
+class PrefixPlan:
+    """Groups of sequences whose tables begin with the same blocks (host arrays,
+    as paged_attn_prefix_plan writes them)."""
+
+    def __init__(self, seq_prefix_blocks, group_offsets, group_members, group_blocks,
+                 num_groups: int, max_group_size: int):
+        self.seq_prefix_blocks = seq_prefix_blocks
+        self.group_offsets = group_offsets
+        self.group_members = group_members
+        self.group_blocks = group_blocks
+        self.num_groups = num_groups
+        self.max_group_size = max_group_size
+
+    def groups(self):
+        """[(members, blocks)] per group."""
+        o = self.group_offsets
+        return [(self.group_members[o[k]:o[k + 1]].tolist(), int(self.group_blocks[k]))
+                for k in range(self.num_groups)]
+
+
+def paged_attn_prefix_plan(block_tables, context_lens, max_context_len: int,
+                           min_blocks: int = 1) -> PrefixPlan:
+    """block_tables: host int32 [B, W]; context_lens: host int32 [B]."""
+    bt = _host_i32(block_tables)
+    if bt.ndim != 2:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]")
+    lens = _host_i32(context_lens).reshape(-1)
+    n = bt.shape[0]
+    if lens.size != n:
+        raise ValueError("context_lens does not match block_tables")
+    pre = np.zeros(n, dtype=np.int32)
+    offs = np.zeros(n + 1, dtype=np.int32)
+    mem = np.zeros(max(n, 1), dtype=np.int32)
+    blk = np.zeros(max(n, 1), dtype=np.int32)
+    ng, mg = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib.paged_attn_prefix_plan(_i32_ptr(bt), bt.shape[1], _i32_ptr(lens), n,
+                                      max_context_len, min_blocks, _i32_ptr(pre), _i32_ptr(offs),
+                                      _i32_ptr(mem), _i32_ptr(blk), ctypes.byref(ng),
+                                      ctypes.byref(mg)))
+    k = ng.value
+    return PrefixPlan(pre, offs[:k + 1].copy(), mem[:offs[k]].copy(), blk[:k].copy(), k, mg.value)
+
+
+def paged_attn_prefix_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int) -> int:
+    return int(lib.paged_attn_prefix_workspace_bytes(num_seqs, num_q_heads, head_dim))
+
+
+def paged_attn_decode_prefix(pool, layer: int, q, out, block_tables, context_lens, scale: float,
+                             max_context_len: int, seq_prefix_blocks, group_offsets,
+                             group_members, group_blocks, num_groups: int, max_group_size: int,
+                             workspace, new_k=None, new_v=None, stream=None) -> None:
+    """Decode (with new_k / new_v: the fused step) reading each group's shared
+    leading blocks once; the group arrays are device int32 tensors."""
+    torch = _torch()
+    _dev(q, "q"); _dev(out, "out"); _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32); _dev(workspace, "workspace")
+    _dev(new_k, "new_k"); _dev(new_v, "new_v")
+    for name, a in (("seq_prefix_blocks", seq_prefix_blocks), ("group_offsets", group_offsets),
+                    ("group_members", group_members), ("group_blocks", group_blocks)):
+        _dev(a, name, torch.int32)
+    if q.dim() != 3 or block_tables.dim() != 2:
+        raise ValueError("q must be [B, Hq, D] and block_tables [B, W]")
+    if out is None or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if new_k is not None and (new_v is None or new_k.shape != new_v.shape or new_k.dim() != 3 or
+                              new_k.shape[0] != q.shape[0] or new_k.shape[2] != q.shape[2]):
+        raise ValueError("new_k and new_v must be [B, Hkv, D] like q")
+    src = _dtype_code(new_k) if new_k is not None else _dtype_code(q)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.paged_attn_decode_prefix(
+        pool, layer, _ptr(new_k), _ptr(new_v), src, _ptr(q), _dtype_code(q), _ptr(out),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), q.shape[0], q.shape[1],
+        float(scale), max_context_len, _ptr(seq_prefix_blocks), _ptr(group_offsets),
+        _ptr(group_members), _ptr(group_blocks), num_groups, max_group_size, _ptr(workspace),
+        ws_bytes, _stream(stream)))

@@ -22,7 +22,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["pool.cpp", "append.hip", "decode.hip", "reduce.hip", "copy.hip", "swap.hip"]
+SOURCES = ["pool.cpp", "prefix_plan.cpp", "append.hip", "decode.hip", "reduce.hip", "copy.hip",
+           "swap.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of the device code.

@@ -46,6 +46,7 @@
 #include "decode_balanced.h"
 #include "decode_core.h"
 #include "decode_mfma.h"
+#include "decode_prefix.h"
 #include "decode_valu.h"
 #include "device.h"
 
@@ -156,22 +157,19 @@ size_t balanced_bytes(size_t group, size_t head_dim, size_t waves) {
     return waves * 2 * group * (head_dim + 4) * sizeof(float);
 }
 
-// The balance rests on every wave of the launch being resident at once: the
-// launch is as wide as the kernel instance's occupancy allows on this device,
-// capped at kBalancedWavesPerCu (the width the workspace is sized for).
-template <class M, int KV, int D, int NBUF>
-hipError_t launch_balanced(DecodeParams prm, int cus, hipStream_t st) {
+template <class M, int KV, int D, int NBUF, bool kPre>
+hipError_t launch_balanced_as(DecodeParams prm, int cus, hipStream_t st) {
     static int wgs_per_cu = -1;  // per kernel instance; the same on every gfx950 device
     if (wgs_per_cu < 0) {
         int nb = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &nb, reinterpret_cast<const void*>(&decode_balanced_kernel<M, KV, D, NBUF>), 256,
-                0) != hipSuccess)
+                &nb, reinterpret_cast<const void*>(&decode_balanced_kernel<M, KV, D, NBUF, kPre>),
+                256, 0) != hipSuccess)
             return hipGetLastError();
         wgs_per_cu = std::max(1, std::min(nb, kBalancedWavesPerCu / 4));
     }
     prm.num_waves = cus * wgs_per_cu * 4;
-    hipLaunchKernelGGL((decode_balanced_kernel<M, KV, D, NBUF>), dim3(prm.num_waves / 4),
+    hipLaunchKernelGGL((decode_balanced_kernel<M, KV, D, NBUF, kPre>), dim3(prm.num_waves / 4),
                        dim3(256), 0, st, prm);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -179,6 +177,15 @@ hipError_t launch_balanced(DecodeParams prm, int cus, hipStream_t st) {
                        dim3(static_cast<uint32_t>(prm.num_kv_heads), static_cast<uint32_t>(prm.num_seqs)),
                        dim3(256), 0, st, prm);
     return hipGetLastError();
+}
+
+// The balance rests on every wave of the launch being resident at once: the
+// launch is as wide as the kernel instance's occupancy allows on this device,
+// capped at kBalancedWavesPerCu (the width the workspace is sized for).
+template <class M, int KV, int D, int NBUF>
+hipError_t launch_balanced(const DecodeParams& prm, int cus, hipStream_t st) {
+    if (prm.pre_blocks != nullptr) return launch_balanced_as<M, KV, D, NBUF, true>(prm, cus, st);
+    return launch_balanced_as<M, KV, D, NBUF, false>(prm, cus, st);
 }
 
 // Ring depths keep two waves per SIMD (MFMA at D = 128 holds its O^T
@@ -199,6 +206,64 @@ hipError_t balanced_by_dim(int D, int G, const DecodeParams& prm, int cus, hipSt
     if (D == 64) return balanced_by_group<KV, 64>(G, prm, cus, st);
     return balanced_by_group<KV, 128>(G, prm, cus, st);
 }
+
+// The shared-prefix kernel: four waves per 16 query rows, the matrix-core
+// ring depths (three tiles at D = 128, four at D = 64).
+template <int KV, int D, int G>
+hipError_t launch_prefix(const DecodeParams& prm, hipStream_t st) {
+    constexpr int R = (D == 128) ? 3 : 4;
+    const uint32_t pairs = static_cast<uint32_t>(prm.num_groups) * prm.num_kv_heads;
+    const uint32_t wgs = (pairs + 7) / 8 * 8 * static_cast<uint32_t>(prm.pre_slots);
+    hipLaunchKernelGGL((prefix_kernel<KV, D, G, 4, R>), dim3(wgs), dim3(256), 0, st, prm);
+    return hipGetLastError();
+}
+
+template <int KV>
+hipError_t prefix_by_shape(int D, int G, const DecodeParams& prm, hipStream_t st) {
+    if (D == 64) {
+        switch (G) {
+            case 1: return launch_prefix<KV, 64, 1>(prm, st);
+            case 2: return launch_prefix<KV, 64, 2>(prm, st);
+            case 4: return launch_prefix<KV, 64, 4>(prm, st);
+            default: return launch_prefix<KV, 64, 8>(prm, st);
+        }
+    }
+    switch (G) {
+        case 1: return launch_prefix<KV, 128, 1>(prm, st);
+        case 2: return launch_prefix<KV, 128, 2>(prm, st);
+        case 4: return launch_prefix<KV, 128, 4>(prm, st);
+        default: return launch_prefix<KV, 128, 8>(prm, st);
+    }
+}
+
+// Workspace of the shared-prefix decode: the balanced pass's slots (sized for
+// any group, as paged_attn_workspace_bytes sizes them), then the prefix
+// partials, then the members' suffix partials, each from a 256-byte boundary.
+struct PrefixLayout {
+    size_t pre_off, suf_off, total;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+PrefixLayout prefix_layout(size_t num_seqs, size_t num_q_heads, size_t head_dim) {
+    const size_t waves = static_cast<size_t>(device_cu_count()) * kBalancedWavesPerCu;
+    const size_t part = round256(num_seqs * num_q_heads * (head_dim + 4) * sizeof(float));
+    PrefixLayout l;
+    l.pre_off = round256(balanced_bytes(std::min<size_t>(num_q_heads, 8), head_dim, waves));
+    l.suf_off = l.pre_off + part;
+    l.total = l.suf_off + part;
+    return l;
+}
+
+// The groups of a shared-prefix decode (paged_attn_decode_prefix).
+struct PrefixArgs {
+    const int32_t* seq_prefix_blocks;
+    const int32_t* group_offsets;
+    const int32_t* group_members;
+    const int32_t* group_blocks;
+    int32_t num_groups;
+    int32_t max_group_size;
+};
 
 }  // namespace
 
@@ -230,7 +295,8 @@ pkv_status decode_impl(const char* fn, const pkv_pool* pool, int32_t layer, cons
                        int32_t num_q_heads, float scale, const float* k_scale,
                        const float* v_scale, int32_t max_context_len, int32_t partition_size,
                        void* workspace, size_t workspace_bytes, const void* new_k,
-                       const void* new_v, int32_t window, hipStream_t stream) {
+                       const void* new_v, int32_t window, hipStream_t stream,
+                       const PrefixArgs* pfx = nullptr) {
     using pkv::fail;
     if (pool == nullptr) return fail(PKV_ERR_INVALID, "%s: pool is NULL", fn);
     const pkv_pool_desc& d = pool->desc;
@@ -320,7 +386,8 @@ pkv_status decode_impl(const char* fn, const pkv_pool* pool, int32_t layer, cons
             // Balanced single pass over the whole batch.
             const int cus = device_cu_count();
             const int waves = cus * kBalancedWavesPerCu;
-            const size_t need = balanced_bytes(G, d.head_dim, waves);
+            const PrefixLayout pl = prefix_layout(num_seqs, num_q_heads, d.head_dim);
+            const size_t need = pfx != nullptr ? pl.total : balanced_bytes(G, d.head_dim, waves);
             if (workspace_bytes < need)
                 return fail(PKV_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn,
                             workspace_bytes, need);
@@ -328,12 +395,32 @@ pkv_status decode_impl(const char* fn, const pkv_pool* pool, int32_t layer, cons
                 return fail(PKV_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
             prm.slots = static_cast<float*>(workspace);
             prm.num_seqs = num_seqs;
+            const bool with_pre = pfx != nullptr && pfx->num_groups > 0;
+            if (with_pre) {
+                uint8_t* ws = static_cast<uint8_t*>(workspace);
+                prm.pre_blocks = pfx->seq_prefix_blocks;
+                prm.pre = reinterpret_cast<float*>(ws + pl.pre_off);
+                prm.suf = reinterpret_cast<float*>(ws + pl.suf_off);
+                prm.group_offsets = pfx->group_offsets;
+                prm.group_members = pfx->group_members;
+                prm.group_blocks = pfx->group_blocks;
+                prm.num_groups = pfx->num_groups;
+                prm.pre_slots = (pfx->max_group_size * G + 15) / 16;
+            }
             if (new_k != nullptr) {
                 const pkv_status sa = append_first(
                     fn, pool, layer, new_k, new_v, q_dtype, block_tables, max_blocks_per_seq,
                     context_lens, num_seqs, max_context_len, k_scale, v_scale, stream);
                 if (sa != PKV_OK) return sa;
                 prm.new_k = prm.new_v = nullptr;
+            }
+            if (with_pre) {
+                const hipError_t ep = (d.kv_dtype == PKV_F16)
+                                          ? prefix_by_shape<PKV_F16>(d.head_dim, G, prm, stream)
+                                          : prefix_by_shape<PKV_BF16>(d.head_dim, G, prm, stream);
+                if (ep != hipSuccess)
+                    return fail(PKV_ERR_HIP, "%s: prefix launch failed: %s", fn,
+                                hipGetErrorString(ep));
             }
             const hipError_t eb = (d.kv_dtype == PKV_F16)
                                       ? balanced_by_dim<PKV_F16>(d.head_dim, G, prm, cus, stream)
@@ -342,6 +429,10 @@ pkv_status decode_impl(const char* fn, const pkv_pool* pool, int32_t layer, cons
                 return fail(PKV_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(eb));
             return PKV_OK;
         }
+        if (pfx != nullptr)
+            return fail(PKV_ERR_INVALID,
+                        "%s: the shared-prefix pass needs a 16-bit cache, a workspace and at "
+                        "most %d sequences", fn, kBalancedMaxSeqs);
         // The ordering keys hold the block count in 23 bits.
         const int64_t max_tokens =
             std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * 16);
@@ -432,4 +523,55 @@ extern "C" pkv_status paged_attn_decode_window(
                        context_lens, num_seqs, num_q_heads, scale, k_scale, v_scale,
                        max_context_len, partition_size, workspace, workspace_bytes, new_k, new_v,
                        window, stream);
+}
+
+extern "C" size_t paged_attn_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                    int32_t head_dim) {
+    if (num_seqs < 0 || num_seqs > kBalancedMaxSeqs || num_q_heads <= 0 || head_dim <= 0)
+        return 0;
+    return prefix_layout(num_seqs, num_q_heads, head_dim).total;
+}
+
+extern "C" pkv_status paged_attn_decode_prefix(
+    const pkv_pool* pool, int32_t layer, const void* new_k, const void* new_v, int32_t src_dtype,
+    const void* q, int32_t q_dtype, void* out, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, float scale, int32_t max_context_len, const int32_t* seq_prefix_blocks,
+    const int32_t* group_offsets, const int32_t* group_members, const int32_t* group_blocks,
+    int32_t num_groups, int32_t max_group_size, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+    using pkv::fail;
+    const char* fn = "paged_attn_decode_prefix";
+    if ((new_k == nullptr) != (new_v == nullptr))
+        return fail(PKV_ERR_INVALID, "%s: new_k and new_v must both be given or both be NULL", fn);
+    if (new_k != nullptr) {
+        if (src_dtype != q_dtype)
+            return fail(PKV_ERR_INVALID, "%s: the new tokens' dtype must equal the q dtype", fn);
+        if ((reinterpret_cast<uintptr_t>(new_k) | reinterpret_cast<uintptr_t>(new_v)) % 16 != 0)
+            return fail(PKV_ERR_INVALID, "%s: new_k and new_v must be 16-byte aligned", fn);
+    }
+    if (pool == nullptr) return fail(PKV_ERR_INVALID, "%s: pool is NULL", fn);
+    if (!pkv::is_16bit(pool->desc.kv_dtype))
+        return fail(PKV_ERR_INVALID, "%s: the shared-prefix pass needs a 16-bit cache", fn);
+    if (num_seqs < 0 || num_seqs > kBalancedMaxSeqs)
+        return fail(PKV_ERR_INVALID, "%s: num_seqs %d outside [0, %d]", fn, num_seqs,
+                    kBalancedMaxSeqs);
+    if (num_groups < 0 || num_groups > num_seqs)
+        return fail(PKV_ERR_INVALID, "%s: num_groups %d outside [0, num_seqs]", fn, num_groups);
+    if (num_groups > 0) {
+        if (max_group_size < 1 || max_group_size > num_seqs)
+            return fail(PKV_ERR_INVALID, "%s: max_group_size %d outside [1, num_seqs]", fn,
+                        max_group_size);
+        if (seq_prefix_blocks == nullptr || group_offsets == nullptr ||
+            group_members == nullptr || group_blocks == nullptr)
+            return fail(PKV_ERR_INVALID, "%s: NULL group arrays", fn);
+    }
+    if (workspace == nullptr && num_seqs > 0)
+        return fail(PKV_ERR_INVALID, "%s: workspace is NULL", fn);
+    const PrefixArgs pfx{seq_prefix_blocks, group_offsets, group_members, group_blocks,
+                         num_groups, max_group_size};
+    return decode_impl(fn, pool, layer, q, q_dtype, out, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, nullptr, nullptr,
+                       max_context_len, 0, workspace, workspace_bytes, new_k, new_v, 0, stream,
+                       &pfx);
 }

@@ -31,27 +31,31 @@ using namespace pkv::dev;
 // Issue-side walker over the tiles of the batch in (sequence, kv head, block)
 // order, holding the block ids of the current sequence's table row: the first
 // 128 blocks from the window's start stay in registers for the row's other
-// heads, later blocks rotate through a second pair of 64-id chunks. Without a
-// sliding window a sequence's tiles are its blocks 0 .. nblk-1; with one,
-// jlo .. nblk-1.
+// heads, later blocks rotate through a second pair of 64-id chunks. A
+// sequence's tiles are its blocks jlo .. nblk-1: jlo is 0, or a sliding
+// window's first block, or the first block after those a shared-prefix pass
+// covers.
 struct TileWalk {
     int s, g, j, nblk;   // current tile: sequence, kv head, block; blocks end at nblk
     int jlo, lo;         // first block read, first token attended (sliding window)
     int L;               // tokens of sequence s as read here
+    int has_pre;         // sequence s has a shared-prefix partial
     int64_t a_sg;        // global index of tile (s, g, jlo)
     int chunk;           // sequences 64*chunk .. +63 have their lengths in lens
     int lens;            // per lane: tokens of sequence 64*chunk + lane
+    int pres;            // per lane: its leading blocks covered by the prefix pass
     int rbase;           // jlo rounded down to 64: row0_* start there
     int row0_a, row0_b;  // ids of blocks rbase .. +63 and +64 .. +127 of row s (per lane)
     int ids_a, ids_b;    // ids of blocks base .. base+127 (per lane, two chunks)
     int base;
 };
 
-__device__ __forceinline__ void walk_set_seq(const DecodeParams& p, TileWalk& t, int L) {
+__device__ __forceinline__ void walk_set_seq(const DecodeParams& p, TileWalk& t, int L, int pre) {
     t.L = L;
     t.nblk = (L + 15) >> 4;
     t.lo = window_lo(p, L);
-    t.jlo = t.lo >> 4;
+    t.jlo = first_block(p, L, pre);
+    t.has_pre = pre > 0;
 }
 
 __device__ __forceinline__ int walk_row_ids(const DecodeParams& p, const TileWalk& t, int j0,
@@ -79,7 +83,8 @@ __device__ __forceinline__ int walk_id(const DecodeParams& p, TileWalk& t, int l
     return __builtin_amdgcn_readlane(t.ids_a, t.j - t.base);
 }
 
-// Step to the next tile. Returns true when it starts a new segment.
+// Step to the next tile. kPre: sequences may begin after shared-prefix blocks.
+template <bool kPre>
 __device__ __forceinline__ void walk_advance(const DecodeParams& p, TileWalk& t, int lane) {
     if (++t.j < t.nblk) return;
     t.j = t.jlo;
@@ -100,9 +105,11 @@ __device__ __forceinline__ void walk_advance(const DecodeParams& p, TileWalk& t,
             t.chunk = t.s >> 6;
             const int jj = t.chunk * 64 + lane;
             t.lens = jj < p.num_seqs ? seq_tokens(p, jj) : 0;
+            t.pres = kPre && jj < p.num_seqs ? pre_of(p, jj) : 0;
         }
-        walk_set_seq(p, t, __builtin_amdgcn_readlane(t.lens, t.s & 63));
-    } while (t.nblk == 0 && t.s + 1 < p.num_seqs);
+        walk_set_seq(p, t, __builtin_amdgcn_readlane(t.lens, t.s & 63),
+                     __builtin_amdgcn_readlane(t.pres, t.s & 63));
+    } while (t.jlo >= t.nblk && t.s + 1 < p.num_seqs);
     t.j = t.jlo;
     walk_enter_row(p, t, lane);
 }
@@ -110,7 +117,8 @@ __device__ __forceinline__ void walk_advance(const DecodeParams& p, TileWalk& t,
 // Ring-slot description of an issued tile (all wave-uniform).
 struct SlotInfo {
     int nvalid, nlo;  // attended tokens of the tile: [nlo, nvalid) (nvalid 0 past the range)
-    int flags;        // bit 0: first tile of a segment, bit 1: last tile of a segment
+    int flags;        // bit 0: first tile of a segment, bit 1: last tile of a segment,
+                      // bit 2: its sequence has a shared-prefix partial
     int s, g, ntiles; // its segment's sequence, kv head and tile count
     int64_t a_sg;     // global index of the segment's first tile
 };
@@ -291,7 +299,10 @@ struct MfmaMath {
     }
 };
 
-template <class M, int KV, int D, int NBUF>
+// kPre: a shared-prefix pass covered the leading blocks of some sequences
+// (pre_blocks); without it that bookkeeping is compiled out, so its registers
+// cost the other forms nothing.
+template <class M, int KV, int D, int NBUF, bool kPre = false>
 __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams p) {
     constexpr int G = M::kG;
     constexpr int SS = SlotGeoB<D>::kStride;
@@ -304,7 +315,8 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
     int64_t total = 0;
     for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
         const int jj = c0 + lane;
-        total += wave_sum(jj < p.num_seqs ? window_blocks(p, seq_tokens(p, jj)) : 0);
+        total += wave_sum(
+            jj < p.num_seqs ? pass_tiles(p, seq_tokens(p, jj), kPre ? pre_of(p, jj) : 0) : 0);
     }
     total *= p.num_kv_heads;
     // R non-empty ranges: with fewer tiles than waves the surplus waves idle,
@@ -323,7 +335,8 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
         for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {  // t0 < total: some chunk holds it
             const int jj = c0 + lane;
             const int len = jj < p.num_seqs ? seq_tokens(p, jj) : 0;
-            const int tiles = window_blocks(p, len) * p.num_kv_heads;
+            const int pre = kPre && jj < p.num_seqs ? pre_of(p, jj) : 0;
+            const int tiles = pass_tiles(p, len, pre) * p.num_kv_heads;
             const int incl = wave_incl_scan(tiles, lane);
             const uint64_t hit = __ballot(jj < p.num_seqs && carry + incl > t0);
             if (hit) {
@@ -331,7 +344,9 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
                 tw.s = c0 + ln;
                 tw.chunk = c0 >> 6;
                 tw.lens = len;
-                walk_set_seq(p, tw, __builtin_amdgcn_readlane(len, ln));
+                tw.pres = pre;
+                walk_set_seq(p, tw, __builtin_amdgcn_readlane(len, ln),
+                             __builtin_amdgcn_readlane(pre, ln));
                 const int nt = tw.nblk - tw.jlo;  // tiles per head
                 const int64_t a_s = carry + __builtin_amdgcn_readlane(incl - tiles, ln);
                 const int64_t off = t0 - a_s;
@@ -373,10 +388,10 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
             M::issue(tt, r, lane);
             return;
         }
-        if (kn > 0) walk_advance(p, tw, lane);
+        if (kn > 0) walk_advance<kPre>(p, tw, lane);
         const bool first = kn == 0 || tw.j == tw.jlo;
         const bool last = kn == n - 1 || tw.j == tw.nblk - 1;
-        info.flags = (first ? 1 : 0) | (last ? 2 : 0);
+        info.flags = (first ? 1 : 0) | (last ? 2 : 0) | (kPre && tw.has_pre ? 4 : 0);
         info.s = tw.s;
         info.g = tw.g;
         info.ntiles = tw.nblk - tw.jlo;
@@ -413,7 +428,12 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
                 // End of a segment: write the output, or the partial of a split context.
                 M::finish(st);
                 if (cur.a_sg >= t0 && cur.a_sg + cur.ntiles <= t1) {
-                    M::store_out(p, st, cur.s, cur.g, lane);
+                    if (kPre && (cur.flags & 4))  // the merge folds in the prefix partial
+                        M::store_partial(p.suf + static_cast<size_t>(cur.s * p.num_kv_heads + cur.g) *
+                                                     G * SS,
+                                         st, lane);
+                    else
+                        M::store_out(p, st, cur.s, cur.g, lane);
                 } else {  // split context: slot 0 if it began before this range, else 1
                     const int slot = (cur.a_sg <= t0) ? 0 : 1;
                     M::store_partial(p.slots + static_cast<size_t>(w * 2 + slot) * G * SS, st, lane);
@@ -429,9 +449,11 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
 // sequence). It recomputes the split of the batch into R ranges, and for a
 // context that was split merges the partials its waves left in their slots;
 // contexts written whole by one wave were stored by the streaming kernel and
-// are left alone. A thread owns 4 dims of one head and merges the partials
-// online, eight at a time: the loads of a group are all issued before any is
-// used, and the running (max, sum, output) is rescaled when a group raises the
+// are left alone. With a shared-prefix pass, a member's prefix partial joins
+// the merge, and so does its suffix partial when one wave read the whole
+// suffix. A thread owns 4 dims of one head and merges the partials online,
+// eight at a time: the loads of a group are all issued before any is used,
+// and the running (max, sum, output) is rescaled when a group raises the
 // maximum, so a context split over up to eight waves costs one round trip to
 // memory after the lengths.
 template <int KV, int D, int G>
@@ -442,32 +464,59 @@ __global__ __launch_bounds__(256) void balanced_merge_kernel(const DecodeParams 
     int64_t total = 0, before = 0;  // tiles per head of the batch, and of sequences < s
     for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
         const int jj = c0 + lane;
-        const int nb = jj < p.num_seqs ? window_blocks(p, seq_tokens(p, jj)) : 0;
+        const int nb = jj < p.num_seqs ? pass_tiles(p, seq_tokens(p, jj), pre_of(p, jj)) : 0;
         total += wave_sum(nb);
         before += wave_sum(jj < s ? nb : 0);
     }
-    const int nblk = window_blocks(p, seq_tokens(p, s));
+    const int pre = pre_of(p, s);
+    const bool has_pre = pre > 0;
+    const int nblk = pass_tiles(p, seq_tokens(p, s), pre);
     uint16_t* out = static_cast<uint16_t*>(p.out) +
                     (static_cast<size_t>(s) * p.num_q_heads + g * G) * D;
     const int t = threadIdx.x;
-    if (nblk == 0) {
+    if (nblk == 0 && !has_pre) {
         for (int idx = t; idx < G * D; idx += 256) out[idx] = 0;
         return;
     }
-    total *= p.num_kv_heads;
-    const int R = static_cast<int>(total < p.num_waves ? total : p.num_waves);
-    const int64_t a_sg = before * p.num_kv_heads + static_cast<int64_t>(g) * nblk;
-    const int wa = wave_of(a_sg, total, R);
-    const int wb = wave_of(a_sg + nblk - 1, total, R);
-    if (wa == wb) return;  // written whole by its wave
-    // Wave wa's piece began before its range: slot 1; waves after it: slot 0.
-    const int slot_a = (a_sg <= range_start(total, wa, R)) ? 0 : 1;
+    // Waves wa .. wb read pieces of this context (none when the prefix pass
+    // covered all of it); whole: one wave read it all and left its partial in suf.
+    int wa = 0, wb = -1, slot_a = 0;
+    bool whole = false;
+    if (nblk > 0) {
+        total *= p.num_kv_heads;
+        const int R = static_cast<int>(total < p.num_waves ? total : p.num_waves);
+        const int64_t a_sg = before * p.num_kv_heads + static_cast<int64_t>(g) * nblk;
+        wa = wave_of(a_sg, total, R);
+        wb = wave_of(a_sg + nblk - 1, total, R);
+        if (wa == wb) {
+            if (!has_pre) return;  // written whole by its wave
+            whole = true;
+        }
+        // Wave wa's piece began before its range: slot 1; waves after it: slot 0.
+        slot_a = (a_sg <= range_start(total, wa, R)) ? 0 : 1;
+    }
     for (int idx = t; idx < G * D / 4; idx += 256) {
         const int h = idx / (D / 4), d = (idx % (D / 4)) * 4;
         const float* base = p.slots + static_cast<size_t>(h) * SS;
         float run_m = -INFINITY, run_l = 0.0f;
         float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        for (int v0 = wa; v0 <= wb; v0 += kGroup) {
+        // Fold one partial (o normalised, m in log2 units, l).
+        auto fold = [&](const float* hs) {
+            const float4 ov = *reinterpret_cast<const float4*>(hs + d);
+            const float mv = hs[D], lv = hs[D + 1];
+            const float mx = fmaxf(run_m, mv);
+            const float ms = (mx == -INFINITY) ? 0.0f : mx;
+            const float a = fast_exp2(run_m - ms);
+            const float wv = lv * fast_exp2(mv - ms);
+            run_l = run_l * a + wv;
+            acc = make_float4(fmaf(wv, ov.x, acc.x * a), fmaf(wv, ov.y, acc.y * a),
+                              fmaf(wv, ov.z, acc.z * a), fmaf(wv, ov.w, acc.w * a));
+            run_m = mx;
+        };
+        const size_t row = (static_cast<size_t>(s) * p.num_q_heads + g * G + h) * SS;
+        if (has_pre) fold(p.pre + row);
+        if (whole) fold(p.suf + row);
+        for (int v0 = wa; !whole && v0 <= wb; v0 += kGroup) {
             float mv[kGroup], lv[kGroup];
             float4 ov[kGroup];
 #pragma unroll

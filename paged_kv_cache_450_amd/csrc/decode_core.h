@@ -45,6 +45,18 @@ struct DecodeParams {
     const uint8_t* new_k;
     const uint8_t* new_v;
     int32_t window;           // > 0: attend over the last `window` tokens only
+    // Shared-prefix decode (pre_blocks NULL: none). The prefix kernel reads the
+    // leading blocks a group of sequences shares once for all its members and
+    // leaves their partials in `pre`; the balanced pass starts each member
+    // after them, and the merge folds the two together.
+    const int32_t* pre_blocks;     // [B] leading blocks covered by the prefix kernel (0: none)
+    float* pre;                    // [B][Hq][D + 4] prefix partials: o / l, m (log2), l
+    float* suf;                    // [B][Hq][D + 4] partials of members' contexts whole in one wave
+    const int32_t* group_offsets;  // [num_groups + 1] into group_members
+    const int32_t* group_members;  // sequence indices, group by group
+    const int32_t* group_blocks;   // [num_groups] shared leading blocks of each group
+    int32_t num_groups;
+    int32_t pre_slots;             // prefix workgroups per (group, kv head)
 };
 
 // First token a sequence of L tokens attends over (sliding window).
@@ -55,6 +67,22 @@ __device__ __forceinline__ int window_lo(const DecodeParams& p, int L) {
 // Blocks a decode reads of a sequence of L tokens: [window_lo / 16, ceil(L / 16)).
 __device__ __forceinline__ int window_blocks(const DecodeParams& p, int L) {
     return ((L + 15) >> 4) - (window_lo(p, L) >> 4);
+}
+
+// Leading blocks of sequence j that the shared-prefix kernel covers (0 without one).
+__device__ __forceinline__ int pre_of(const DecodeParams& p, int j) {
+    return p.pre_blocks != nullptr ? max(p.pre_blocks[j], 0) : 0;
+}
+
+// First block the balanced pass reads of a sequence of L tokens whose first
+// `pre` blocks the shared-prefix kernel covers (sliding window: its first block).
+__device__ __forceinline__ int first_block(const DecodeParams& p, int L, int pre) {
+    return max(window_lo(p, L) >> 4, min(pre, (L + 15) >> 4));
+}
+
+// Tiles per kv head the balanced pass reads of that sequence.
+__device__ __forceinline__ int pass_tiles(const DecodeParams& p, int L, int pre) {
+    return ((L + 15) >> 4) - first_block(p, L, pre);
 }
 
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
@@ -76,6 +104,12 @@ constexpr int kStreamPolicy = 2;
 __device__ __forceinline__ uint4 rsrc_load16(__amdgpu_buffer_rsrc_t r, int voff) {
     return __builtin_bit_cast(uint4,
                               __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kStreamPolicy));
+}
+
+// The same load with the default policy, for bytes that other workgroups on
+// the same XCD are about to read too: the lines stay in its L2.
+__device__ __forceinline__ uint4 rsrc_load16_kept(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
 // Longest-first order of the sequences of a single-pass decode: returns the

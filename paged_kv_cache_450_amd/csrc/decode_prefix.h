@@ -1,0 +1,169 @@
+// Shared-prefix pass: the leading blocks a group of sequences shares, read once
+// for all the group's members, on matrix cores.
+#pragma once
+
+#include "decode_core.h"
+#include "decode_mfma.h"
+
+namespace {
+
+using namespace pkv::dev;
+
+// ---------------------------------------------------------------------------
+// Sequences that share a prompt map the same physical blocks ([P2]
+// "PagedAttention：...": shared blocks, reference counts), so those blocks hold
+// the same K/V for every member. A decode that reads them per member moves
+// them from HBM once per member; here they are read once per group.
+//
+// The matrix-core product has 16 query columns. One workgroup serves 16 query
+// rows of one kv head g: 16 / G members of a group times their G heads
+// (G = 1: sixteen members, G = 8: two). Its NW waves deal the group's shared
+// blocks round robin, stream them through a ring of tiles exactly as the
+// matrix-core decode does (decode_mfma.h), and merge through LDS into one
+// partial (o / l, m in log2 units, l) per member and query head, written to
+// pre[s][qh]. The balanced pass then reads each member from the first block
+// after the shared ones, and its merge kernel folds the prefix partial in with
+// the log-sum-exp rule (exact in real arithmetic).
+//
+// All workgroups of one (group, kv head) read the same tiles, so they are
+// placed on one XCD: workgroups are dealt to the 8 XCDs round robin by linear
+// index, and the index is laid out so that all those of a (group, kv head)
+// pair share their index mod 8, and the tiles are loaded with the default
+// cache policy (not the streaming one of the other decode kernels). The first
+// to ask for a tile brings it into that XCD's L2 and the others find it there.
+template <int KV, int D, int G, int NW, int NBUF>
+__global__ __launch_bounds__(NW * 64) void prefix_kernel(const DecodeParams p) {
+    using Gm = MfmaGeo<D>;
+    constexpr int NK = Gm::kNk, NV = Gm::kNv, ND = Gm::kNd, TB = Gm::kTileBytes;
+    constexpr int MPS = 16 / G;  // members per workgroup
+    constexpr int SS = D + 4;
+    static_assert(G >= 1 && G <= 16 && 16 % G == 0, "16 query rows per workgroup");
+
+    // Linear index = ((pair / 8) * slots + slot) * 8 + pair % 8, pair = group * Hkv + g.
+    const int bid = blockIdx.x;
+    const int rest = bid >> 3;
+    const int slot = rest % p.pre_slots;
+    const int pair = (rest / p.pre_slots) * 8 + (bid & 7);
+    if (pair >= p.num_groups * p.num_kv_heads) return;
+    const int gr = pair / p.num_kv_heads, g = pair % p.num_kv_heads;
+    const int m0 = p.group_offsets[gr];
+    const int msz = p.group_offsets[gr + 1] - m0;
+    if (msz <= 0 || slot * MPS >= msz) return;
+    // Shared blocks, read through the first member's table row.
+    const int P = min(max(p.group_blocks[gr], 0), p.max_blocks);
+    const int s0 = p.group_members[m0];
+
+    const int lane = threadIdx.x & 63;
+    const int w = (NW == 1) ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hl = lane & 15;
+    const int kg = lane >> 4;
+
+    // Q^T operand: row hl is head hl % G of member slot*MPS + hl / G (zeros
+    // past the group's end; those lanes read the last member's row and
+    // discard it).
+    __shared__ __attribute__((aligned(16))) uint8_t q_all[NW][NK * 1024];
+    const QLds<D> qr{q_all[w]};
+    {
+        const int mi = slot * MPS + hl / G;
+        const int s = p.group_members[m0 + min(mi, msz - 1)];
+        const int hq = g * G + hl % G;
+        const uint16_t* qrow =
+            static_cast<const uint16_t*>(p.q) + (static_cast<size_t>(s) * p.num_q_heads + hq) * D;
+        uint4 qv[NK];
+#pragma unroll
+        for (int c = 0; c < NK; ++c) qv[c] = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * kg);
+#pragma unroll
+        for (int c = 0; c < NK; ++c)
+            *reinterpret_cast<uint4*>(q_all[w] + c * 1024 + lane * 16) =
+                mi < msz ? qv[c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    // This wave's tiles: blocks w, w + NW, ... below P.
+    const int n = P > w ? (P - w + NW - 1) / NW : 0;
+    BlockIds<NW> ids;
+    ids.init(p.block_tables + static_cast<size_t>(s0) * p.max_blocks + w, n, lane);
+
+    const float sscale = p.scale_log2;
+    f32x4_t o[ND];
+#pragma unroll
+    for (int j = 0; j < ND; ++j) o[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m = -INFINITY, lsum = 0.0f;
+
+    __shared__ __attribute__((aligned(16))) uint8_t stage_all[NW][Gm::kStage];
+    uint8_t* stage = stage_all[w];
+
+    const uint8_t* kpl = p.k_plane + static_cast<size_t>(g) * TB;
+    const uint8_t* vpl = p.v_plane + static_cast<size_t>(g) * TB;
+    const size_t bstride = static_cast<size_t>(p.num_kv_heads) * TB;
+    const int koff = hl * Gm::kRowBytes + 16 * kg;
+    const int voff = lane * 16;
+
+    MfmaTile<D> t[NBUF];
+    int nv[NBUF];
+    auto issue = [&](MfmaTile<D>& tt, int& nvalid, int kn) {
+        // Shared blocks are full: every token of a tile is attended.
+        const TileRef r =
+            tile_ref(p, kpl, vpl, bstride, TB, ids.next(kn), (w + kn * NW) * 16, P * 16, 0);
+        nvalid = r.nvalid;
+        // Default cache policy: the other workgroups of this (group, kv head),
+        // on the same XCD, read the same tiles from its L2.
+#pragma unroll
+        for (int c = 0; c < NK; ++c) tt.k[c] = rsrc_load16_kept(r.k, koff + 64 * c);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) tt.v[i] = rsrc_load16_kept(r.v, voff + 1024 * i);
+    };
+
+#pragma unroll
+    for (int x = 0; x < NBUF; ++x) issue(t[x], nv[x], x);
+    for (int k0 = 0; k0 < n; k0 += NBUF) {
+#pragma unroll
+        for (int x = 0; x < NBUF; ++x) {
+            if (nv[x] == 16)
+                mfma_consume<KV, D, false>(t[x], 16, 0, qr, o, m, lsum, sscale, stage, lane);
+            else if (nv[x] > 0)  // an id outside the pool: no tokens
+                mfma_consume<KV, D, true>(t[x], nv[x], 0, qr, o, m, lsum, sscale, stage, lane);
+            issue(t[x], nv[x], k0 + x + NBUF);
+        }
+    }
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+
+    // Merge the NW waves' partials of the 16 rows and store them per member.
+    __shared__ float lds_o[NW][16][D];
+    __shared__ float lds_m[NW][16];
+    __shared__ float lds_l[NW][16];
+#pragma unroll
+    for (int j = 0; j < ND; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lds_o[w][hl][16 * j + 4 * kg + r] = o[j][r];
+    if (kg == 0) {
+        lds_m[w][hl] = m;
+        lds_l[w][hl] = lsum;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 16 * D; idx += NW * 64) {
+        const int r = idx / D, d = idx % D;
+        const int mi = slot * MPS + r / G;
+        if (mi >= msz) continue;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int x = 0; x < NW; ++x) mx = fmaxf(mx, lds_m[x][r]);
+        const float ms = (mx == -INFINITY) ? 0.0f : mx;
+        float l = 0.0f, acc = 0.0f;
+#pragma unroll
+        for (int x = 0; x < NW; ++x) {
+            const float a = fast_exp2(lds_m[x][r] - ms);
+            l = fmaf(lds_l[x][r], a, l);
+            acc = fmaf(lds_o[x][r][d], a, acc);
+        }
+        const int s = p.group_members[m0 + mi];
+        float* dst = p.pre + (static_cast<size_t>(s) * p.num_q_heads + g * G + r % G) * SS;
+        dst[d] = l > 0.0f ? acc / l : 0.0f;
+        if (d == 0) {
+            dst[D] = mx;
+            dst[D + 1] = l;
+        }
+    }
+}
+
+}  // namespace

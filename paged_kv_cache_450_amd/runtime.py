@@ -24,8 +24,9 @@ from . import (BLOCK_SIZE, PKV_BF16, PKV_ERR_OOM, PKV_F16, PKV_FP8_E4M3, PkvErro
                kv_pool_free_list, kv_pool_num_free, kv_prefix_acquire, kv_prefix_register,
                kv_seq_extend, kv_seq_extend_cow, kv_seq_fork, kv_seq_trim, kv_swap_in, kv_swap_out,
                kv_swap_slot_bytes,
-               paged_attn_decode, paged_attn_decode_append, paged_attn_decode_window,
-               paged_attn_reduce,
+               paged_attn_decode, paged_attn_decode_append, paged_attn_decode_prefix,
+               paged_attn_decode_window, paged_attn_prefix_plan,
+               paged_attn_prefix_workspace_bytes, paged_attn_reduce,
                paged_attn_workspace_bytes)
 
 DTYPE_CODES = {"f16": PKV_F16, "bf16": PKV_BF16, "e4m3": PKV_FP8_E4M3}
@@ -124,11 +125,17 @@ class DecodeBatch:
     fused form that also stores each sequence's new token. A single pass (partition_size 0) is
     balanced across the GPU unless balanced=False. window > 0: every sequence
     attends over its last `window` tokens only (paged_attn_decode_window).
+    shared_prefix=True (balanced single pass on a 16-bit cache): sequences whose
+    tables begin with the same blocks are grouped on the host
+    (paged_attn_prefix_plan, runs of at least min_prefix_blocks), and each
+    group's shared blocks are read once per step (paged_attn_decode_prefix); a
+    window set later takes the windowed call instead.
     """
 
     def __init__(self, cache: PagedKVCache, tables: np.ndarray, lens, num_q_heads: int,
                  q_dtype, partition_size: int = 0, scale=None, k_scale=None, v_scale=None,
-                 max_context_len=None, device="cuda", balanced: bool = True, window: int = 0):
+                 max_context_len=None, device="cuda", balanced: bool = True, window: int = 0,
+                 shared_prefix: bool = False, min_prefix_blocks: int = 1):
         self.cache = cache
         self.window = window
         lens = np.asarray(lens, dtype=np.int32)
@@ -151,12 +158,35 @@ class DecodeBatch:
         # split contexts' partials); without one: one workgroup per
         # (sequence, kv head).
         self.balanced = partition_size == 0 and balanced and ws > 0
+        self.plan = None
+        if shared_prefix:
+            if not self.balanced or window > 0 or cache.desc.kv_dtype == PKV_FP8_E4M3:
+                raise ValueError("shared_prefix needs the balanced single pass on a 16-bit "
+                                 "cache, without a window")
+            self.plan = paged_attn_prefix_plan(tables, lens, self.max_context_len,
+                                               min_prefix_blocks)
+            ws = paged_attn_prefix_workspace_bytes(self.num_seqs, num_q_heads, self.head_dim)
+
+            def dev(a):
+                return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+            self.plan_dev = (dev(self.plan.seq_prefix_blocks), dev(self.plan.group_offsets),
+                             dev(self.plan.group_members), dev(self.plan.group_blocks))
         if partition_size > 0 or self.balanced:
             self.workspace = torch.empty(max(ws, 16) // 4, dtype=torch.float32, device=device)
         else:
             self.workspace = None
 
+    def _decode_prefix(self, layer: int, q, new_k, new_v, stream):
+        pre, offs, mem, blk = self.plan_dev
+        paged_attn_decode_prefix(self.cache.handle, layer, q, self.out, self.tables, self.lens,
+                                 self.scale, self.max_context_len, pre, offs, mem, blk,
+                                 self.plan.num_groups, self.plan.max_group_size, self.workspace,
+                                 new_k, new_v, stream)
+
     def decode(self, layer: int, q, stream=None):
+        if self.plan is not None and self.window == 0:
+            self._decode_prefix(layer, q, None, None, stream)
+            return
         if self.window > 0:
             paged_attn_decode_window(self.cache.handle, layer, q,
                                      None if self.partition_size else self.out, self.tables,
@@ -174,6 +204,9 @@ class DecodeBatch:
         want = (self.num_seqs, self.cache.desc.num_kv_heads, self.head_dim)
         if tuple(new_k.shape) != want or tuple(new_v.shape) != want:
             raise ValueError(f"new_k and new_v must be {want}")
+        if self.plan is not None and self.window == 0:
+            self._decode_prefix(layer, q, new_k, new_v, stream)
+            return
         if self.window > 0:
             paged_attn_decode_window(self.cache.handle, layer, q,
                                      None if self.partition_size else self.out, self.tables,

@@ -35,12 +35,14 @@ assert _BS == BS
 
 
 def build_product(cfg, seed=0, device="cuda", partition_size=None, fill_byte=POISON,
-                  run_step=True, placement_seed=None, balanced=None, fused=True):
+                  run_step=True, placement_seed=None, balanced=None, fused=True,
+                  shared_prefix=None):
     """Product side: pool, bookkeeping, prefill appends, then (run_step) one
     decode step per layer whose outputs are kept in side.outputs. fused: the
-    step is paged_attn_decode_append (else kv_cache_append + paged_attn_decode)."""
+    step is paged_attn_decode_append (else kv_cache_append + paged_attn_decode);
+    shared_prefix (default: the workload's): paged_attn_decode_prefix."""
     side = Workload(cfg, seed, device, partition_size, fill_byte, placement_seed,
-                    balanced=balanced, fused=fused)
+                    balanced=balanced, fused=fused, shared_prefix=shared_prefix)
     if run_step:
         side.outputs = [step(side, layer).clone() for layer in range(cfg.layers)]
     return side

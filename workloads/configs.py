@@ -19,6 +19,7 @@ class Config:
     share_prefix_tokens: int = 0        # > 0: even-indexed sequences share this many tokens
     partition_size: int = 0             # default split-K partition (0: one pass)
     balanced: bool = True               # single pass: balanced over waves (else per sequence)
+    shared_prefix: bool = False         # read blocks shared by several sequences once per step
 
     @property
     def group(self) -> int:
