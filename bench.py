@@ -49,19 +49,22 @@ KERNEL_SOURCES = {
     "balanced": tuple(_CSRC + f for f in ("decode.hip", "decode_core.h", "decode_valu.h",
                                            "decode_mfma.h", "decode_balanced.h", "device.h",
                                            "common.h")),
+    "prefix": tuple(_CSRC + f for f in ("decode.hip", "decode_core.h", "decode_valu.h",
+                                         "decode_mfma.h", "decode_balanced.h", "decode_prefix.h",
+                                         "device.h", "common.h")),
 }
 MEASURED_TRAFFIC = {  # workload -> counters of its decode kernel
-    "llama13b_layer": {  # FETCH 367,297.2 KiB x 1.99992 + WRITE 960.0 KiB
-        "kernel": "valu", "bytes": 753_177_003,
-        "sources_sha256": "0afcdca6b4860c46430002feddd0a62efb828977ab6bf094007028e63c7aa37d",
+    "llama13b_layer": {  # FETCH 367,298.7 KiB x 1.99988 + WRITE 960.0 KiB
+        "kernel": "valu", "bytes": 753_166_446,
+        "sources_sha256": "226c38afb4b297c88ae0c5e7e2c0154acefe60e2e4f6ead7b50f567b0073cf35",
         "summary": "profiles/decode_kernel_llama13b_layer.md"},
-    "longctx_fp8": {  # FETCH 715,694.3 KiB x 1.99998 + WRITE 5,754.6 KiB
-        "kernel": "valu", "bytes": 1_471_616_465,
-        "sources_sha256": "0afcdca6b4860c46430002feddd0a62efb828977ab6bf094007028e63c7aa37d",
+    "longctx_fp8": {  # FETCH 715,694.3 KiB x 1.99998 + WRITE 5,755.6 KiB
+        "kernel": "valu", "bytes": 1_471_617_489,
+        "sources_sha256": "226c38afb4b297c88ae0c5e7e2c0154acefe60e2e4f6ead7b50f567b0073cf35",
         "summary": "profiles/decode_kernel_longctx_fp8.md"},
-    "gqa_prefix": {  # streaming kernel: FETCH 409,090.2 KiB x 1.99995 + WRITE 12,219.7 KiB
-        "kernel": "balanced", "bytes": 850_307_011,
-        "sources_sha256": "c8a6905b28a7535238e1265a87ecbeba8d48d7aaae72797d8ac243c687df74d5",
+    "gqa_prefix": {  # streaming kernel: FETCH 408,603.3 KiB x 1.99994 + WRITE 12,217.8 KiB
+        "kernel": "balanced", "bytes": 849_306_964,
+        "sources_sha256": "f6f542117187db5453401ba0f1de80fc21160838df3dc1c2be1b467334bc72f4",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
 }
 

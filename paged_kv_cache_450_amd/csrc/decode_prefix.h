@@ -166,4 +166,33 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const DecodeParams p) {
     }
 }
 
+// The shared-prefix kernel: four waves per 16 query rows, the matrix-core
+// ring depths (three tiles at D = 128, four at D = 64).
+template <int KV, int D, int G>
+hipError_t launch_prefix(const DecodeParams& prm, hipStream_t st) {
+    constexpr int R = (D == 128) ? 3 : 4;
+    const uint32_t pairs = static_cast<uint32_t>(prm.num_groups) * prm.num_kv_heads;
+    const uint32_t wgs = (pairs + 7) / 8 * 8 * static_cast<uint32_t>(prm.pre_slots);
+    hipLaunchKernelGGL((prefix_kernel<KV, D, G, 4, R>), dim3(wgs), dim3(256), 0, st, prm);
+    return hipGetLastError();
+}
+
+template <int KV>
+hipError_t prefix_by_shape(int D, int G, const DecodeParams& prm, hipStream_t st) {
+    if (D == 64) {
+        switch (G) {
+            case 1: return launch_prefix<KV, 64, 1>(prm, st);
+            case 2: return launch_prefix<KV, 64, 2>(prm, st);
+            case 4: return launch_prefix<KV, 64, 4>(prm, st);
+            default: return launch_prefix<KV, 64, 8>(prm, st);
+        }
+    }
+    switch (G) {
+        case 1: return launch_prefix<KV, 128, 1>(prm, st);
+        case 2: return launch_prefix<KV, 128, 2>(prm, st);
+        case 4: return launch_prefix<KV, 128, 4>(prm, st);
+        default: return launch_prefix<KV, 128, 8>(prm, st);
+    }
+}
+
 }  // namespace
