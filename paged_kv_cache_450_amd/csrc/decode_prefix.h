@@ -58,24 +58,21 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const DecodeParams p) {
     const int hl = lane & 15;
     const int kg = lane >> 4;
 
-    // Q^T operand: row hl is head hl % G of member slot*MPS + hl / G (zeros
-    // past the group's end; those lanes read the last member's row and
-    // discard it).
-    __shared__ __attribute__((aligned(16))) uint8_t q_all[NW][NK * 1024];
-    const QLds<D> qr{q_all[w]};
-    {
+    // Q^T operand, one copy for the workgroup: row hl is head hl % G of member
+    // slot*MPS + hl / G (zeros past the group's end; those lanes read the last
+    // member's row and discard it). Wave c < NK writes its 32-dim chunk c.
+    static_assert(NW >= NK, "one wave per Q chunk");
+    __shared__ __attribute__((aligned(16))) uint8_t q_lds[NK * 1024];
+    const QLds<D> qr{q_lds};
+    if (w < NK) {
         const int mi = slot * MPS + hl / G;
         const int s = p.group_members[m0 + min(mi, msz - 1)];
         const int hq = g * G + hl % G;
         const uint16_t* qrow =
             static_cast<const uint16_t*>(p.q) + (static_cast<size_t>(s) * p.num_q_heads + hq) * D;
-        uint4 qv[NK];
-#pragma unroll
-        for (int c = 0; c < NK; ++c) qv[c] = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * kg);
-#pragma unroll
-        for (int c = 0; c < NK; ++c)
-            *reinterpret_cast<uint4*>(q_all[w] + c * 1024 + lane * 16) =
-                mi < msz ? qv[c] : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 qv = *reinterpret_cast<const uint4*>(qrow + 32 * w + 8 * kg);
+        *reinterpret_cast<uint4*>(q_lds + w * 1024 + lane * 16) =
+            mi < msz ? qv : make_uint4(0u, 0u, 0u, 0u);
     }
 
     // This wave's tiles: blocks w, w + NW, ... below P.
@@ -89,8 +86,12 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const DecodeParams p) {
     for (int j = 0; j < ND; ++j) o[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     float m = -INFINITY, lsum = 0.0f;
 
-    __shared__ __attribute__((aligned(16))) uint8_t stage_all[NW][Gm::kStage];
-    uint8_t* stage = stage_all[w];
+    // The waves' V staging tiles during the stream; afterwards the same bytes
+    // hold the waves' partials for the merge.
+    constexpr int kMergeBytes = NW * 16 * (D + 2) * 4;
+    constexpr int kLdsBytes = NW * Gm::kStage > kMergeBytes ? NW * Gm::kStage : kMergeBytes;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kLdsBytes];
+    uint8_t* stage = lds_raw + w * Gm::kStage;
 
     const uint8_t* kpl = p.k_plane + static_cast<size_t>(g) * TB;
     const uint8_t* vpl = p.v_plane + static_cast<size_t>(g) * TB;
@@ -115,6 +116,7 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const DecodeParams p) {
 
 #pragma unroll
     for (int x = 0; x < NBUF; ++x) issue(t[x], nv[x], x);
+    __syncthreads();  // Q is in LDS
     for (int k0 = 0; k0 < n; k0 += NBUF) {
 #pragma unroll
         for (int x = 0; x < NBUF; ++x) {
@@ -129,9 +131,10 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const DecodeParams p) {
     lsum += __shfl_xor(lsum, 32);
 
     // Merge the NW waves' partials of the 16 rows and store them per member.
-    __shared__ float lds_o[NW][16][D];
-    __shared__ float lds_m[NW][16];
-    __shared__ float lds_l[NW][16];
+    __syncthreads();  // every wave is done with its staging tile
+    float (*lds_o)[16][D] = reinterpret_cast<float (*)[16][D]>(lds_raw);
+    float (*lds_m)[16] = reinterpret_cast<float (*)[16]>(lds_raw + NW * 16 * D * 4);
+    float (*lds_l)[16] = reinterpret_cast<float (*)[16]>(lds_raw + NW * 16 * (D + 1) * 4);
 #pragma unroll
     for (int j = 0; j < ND; ++j)
 #pragma unroll
@@ -166,14 +169,16 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const DecodeParams p) {
     }
 }
 
-// The shared-prefix kernel: four waves per 16 query rows, the matrix-core
-// ring depths (three tiles at D = 128, four at D = 64).
+// The shared-prefix kernel: four waves per 16 query rows (eight measured no
+// faster), the matrix-core ring depths (three tiles at D = 128, four at
+// D = 64).
 template <int KV, int D, int G>
 hipError_t launch_prefix(const DecodeParams& prm, hipStream_t st) {
     constexpr int R = (D == 128) ? 3 : 4;
+    constexpr int NW = 4;
     const uint32_t pairs = static_cast<uint32_t>(prm.num_groups) * prm.num_kv_heads;
     const uint32_t wgs = (pairs + 7) / 8 * 8 * static_cast<uint32_t>(prm.pre_slots);
-    hipLaunchKernelGGL((prefix_kernel<KV, D, G, 4, R>), dim3(wgs), dim3(256), 0, st, prm);
+    hipLaunchKernelGGL((prefix_kernel<KV, D, G, NW, R>), dim3(wgs), dim3(NW * 64), 0, st, prm);
     return hipGetLastError();
 }
 

@@ -129,13 +129,22 @@ class DecodeBatch:
     tables begin with the same blocks are grouped on the host
     (paged_attn_prefix_plan, runs of at least min_prefix_blocks), and each
     group's shared blocks are read once per step (paged_attn_decode_prefix); a
-    window set later takes the windowed call instead.
+    window set later takes the windowed call instead. shared_prefix="auto" does
+    so only when the plan saves at least PREFIX_AUTO_BYTES of repeated reads per
+    layer: the prefix kernel costs about 10 us per call whatever it reads, and
+    the plain pass's repeated reads of a shared block mostly hit the 256 MB
+    last-level cache, so they cost less than their bytes suggest.
     """
+
+    # Repeated K/V reads per layer the prefix pass must save before "auto" takes
+    # it. Measured on MI355X (64 sharers, 64 / 8 heads x 128, bf16): 132 MB
+    # saved (512 shared tokens) cost 3% per call, 264 MB (1024) gained 6%.
+    PREFIX_AUTO_BYTES = 200_000_000
 
     def __init__(self, cache: PagedKVCache, tables: np.ndarray, lens, num_q_heads: int,
                  q_dtype, partition_size: int = 0, scale=None, k_scale=None, v_scale=None,
                  max_context_len=None, device="cuda", balanced: bool = True, window: int = 0,
-                 shared_prefix: bool = False, min_prefix_blocks: int = 1):
+                 shared_prefix=False, min_prefix_blocks: int = 1):
         self.cache = cache
         self.window = window
         lens = np.asarray(lens, dtype=np.int32)
@@ -165,6 +174,9 @@ class DecodeBatch:
                                  "cache, without a window")
             self.plan = paged_attn_prefix_plan(tables, lens, self.max_context_len,
                                                min_prefix_blocks)
+            if shared_prefix == "auto" and self.repeated_bytes() < self.PREFIX_AUTO_BYTES:
+                self.plan = None
+        if self.plan is not None:
             ws = paged_attn_prefix_workspace_bytes(self.num_seqs, num_q_heads, self.head_dim)
 
             def dev(a):
@@ -175,6 +187,17 @@ class DecodeBatch:
             self.workspace = torch.empty(max(ws, 16) // 4, dtype=torch.float32, device=device)
         else:
             self.workspace = None
+
+    def repeated_bytes(self) -> int:
+        """K/V bytes per layer that the plain pass reads more than once and the
+        prefix pass reads once: (members - 1) x shared blocks per group."""
+        if self.plan is None:
+            return 0
+        d = self.cache.desc
+        esz = 1 if d.kv_dtype == PKV_FP8_E4M3 else 2
+        per_block = 2 * d.num_kv_heads * BLOCK_SIZE * d.head_dim * esz
+        sizes = np.diff(self.plan.group_offsets)
+        return int(((sizes - 1) * self.plan.group_blocks).sum()) * per_block
 
     def _decode_prefix(self, layer: int, q, new_k, new_v, stream):
         pre, offs, mem, blk = self.plan_dev
