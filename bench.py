@@ -33,6 +33,8 @@ import os
 import sys
 import time
 
+from dataclasses import replace
+
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
@@ -53,7 +55,7 @@ KERNEL_SOURCES = {
                                          "decode_mfma.h", "decode_balanced.h", "decode_prefix.h",
                                          "device.h", "common.h")),
 }
-MEASURED_TRAFFIC = {  # workload -> counters of its decode kernel
+MEASURED_TRAFFIC = {  # traffic_key -> counters of the decode call's streaming kernel
     "llama13b_layer": {  # FETCH 367,298.7 KiB x 1.99988 + WRITE 960.0 KiB
         "kernel": "valu", "bytes": 753_166_446,
         "sources_sha256": "226c38afb4b297c88ae0c5e7e2c0154acefe60e2e4f6ead7b50f567b0073cf35",
@@ -66,6 +68,18 @@ MEASURED_TRAFFIC = {  # workload -> counters of its decode kernel
         "kernel": "balanced", "bytes": 849_306_964,
         "sources_sha256": "f6f542117187db5453401ba0f1de80fc21160838df3dc1c2be1b467334bc72f4",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
+    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 358,277.6 KiB x 1.99989 + WRITE 12,412.7 KiB
+        "kernel": "prefix", "bytes": 746_422_283,
+        "sources_sha256": "b95bd360f2d9dd76040cfd3a1dbf9746de4c3c7ae8714d597f46523ae4a443b3",
+        "summary": "profiles/prefix_kernel_gqa_prefix.md"},
+    "gqa_prefix/shared_prefix/prompt2048": {  # streaming kernel: FETCH 262,202.6 KiB x 1.99992 + WRITE 12,448.4 KiB
+        "kernel": "prefix", "bytes": 549_716_322,
+        "sources_sha256": "b95bd360f2d9dd76040cfd3a1dbf9746de4c3c7ae8714d597f46523ae4a443b3",
+        "summary": "profiles/prefix_kernel_gqa_prefix.md"},
+    "gqa_prefix/prompt2048": {  # streaming kernel: FETCH 471,871.4 KiB x 1.99992 + WRITE 12,327.2 KiB
+        "kernel": "balanced", "bytes": 978_977_434,
+        "sources_sha256": "f6f542117187db5453401ba0f1de80fc21160838df3dc1c2be1b467334bc72f4",
+        "summary": "profiles/prefix_kernel_gqa_prefix.md"},
 }
 
 
@@ -77,6 +91,21 @@ def sources_sha256(kernel: str) -> str:
         with open(os.path.join(root, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def traffic_key(cfg, w, args) -> str:
+    """The measured-traffic entry that matches this run: the workload in its
+    default form, or with the options that change what the call launches."""
+    key = cfg.name
+    if args.unfused:
+        key += "/unfused"
+    if args.partition_size is not None and args.partition_size != cfg.partition_size:
+        key += f"/ps{args.partition_size}"
+    if w.batch.plan is not None:
+        key += "/shared_prefix"
+    if args.prefix_tokens:
+        key += f"/prompt{args.prefix_tokens}"
+    return key
 
 
 def measured_traffic(workload: str):
@@ -618,6 +647,9 @@ def main(argv=None):
     ap.add_argument("--unfused", action="store_true",
                     help="run a step as kv_cache_append + paged_attn_decode instead of the "
                          "fused paged_attn_decode_append")
+    ap.add_argument("--prefix-tokens", type=int, default=0, metavar="N",
+                    help="lengthen the shared prompt of a workload with one (gqa_prefix) to N "
+                         "tokens; its sharers' contexts grow to at least N + 1")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="read blocks that several sequences share once per step "
                          "(paged_attn_decode_prefix) instead of once per sequence")
@@ -643,6 +675,11 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     cfg = W.CONFIGS[args.workload]
+    if args.prefix_tokens > 0:
+        if not cfg.share_prefix_tokens:
+            print(f"--prefix-tokens: workload {cfg.name} has no shared prompt", file=sys.stderr)
+            return 2
+        cfg = replace(cfg, share_prefix_tokens=args.prefix_tokens)
     torch.cuda.set_device(0)
     fused = not args.unfused
     first = Workload(cfg, args.seed, "cuda", args.partition_size,
@@ -756,6 +793,7 @@ def main(argv=None):
             "kv_dtype": cfg.kv_dtype, "q_dtype": cfg.q_dtype,
             "context_lens": list(cfg.lengths),
             "partition_size": first.partition_size,
+            "shared_prompt_tokens": cfg.share_prefix_tokens,
             "shared_prefix": ({"groups": first.batch.plan.num_groups,
                                "members": int(first.batch.plan.group_offsets[-1]),
                                "blocks": first.batch.plan.group_blocks.tolist()}
@@ -783,7 +821,7 @@ def main(argv=None):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(decode_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(cfg.name),
+            "traffic": measured_traffic(traffic_key(cfg, first, args)),
             "algorithmic_bytes": int(per_layer_unique),
         },
     }
