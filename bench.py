@@ -467,7 +467,7 @@ def swap_rate(cfg, blocks: int, iters: int, stream) -> dict:
 
 
 def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False, swap_slots=0,
-                 pool_blocks=0, max_gen=128, window=0) -> dict:
+                 pool_blocks=0, max_gen=128, window=0, shared_prefix=False) -> dict:
     """The continuous-batching loop (ContinuousBatcher) over a seeded request
     stream shaped like the workload: prompts of up to its longest context, 1 to
     max_gen generated tokens, a third of the requests with 2-3 samples, 4 arrivals
@@ -477,8 +477,9 @@ def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False, swap_slo
     cache; swap_slots: preempt into a swap space of that many pinned host slots
     (else by recomputation); window > 0: a sliding window of that many tokens
     (blocks before it released every iteration); pool_blocks > 0: a pool of that many blocks
-    instead (a tight pool forces preemption). Inputs are drawn before the timed region, which
-    holds the bookkeeping (host) and the GPU work of every iteration."""
+    instead (a tight pool forces preemption); shared_prefix (True or "auto"): the balanced
+    pass with the shared-prefix pass, planned every iteration. Inputs are drawn before the
+    timed region, which holds the bookkeeping (host) and the GPU work of every iteration."""
     import torch
 
     import workloads as W
@@ -504,8 +505,13 @@ def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False, swap_slo
     k_scale = v_scale = None
     if cfg.kv_dtype == "e4m3":
         k_scale, v_scale = W.fp8_scales([kp, ks]), W.fp8_scales([vp, vs])
-    # the workload's single-pass form: balanced (with a workspace) or per sequence
-    wsb = P_workspace_bytes(cfg) if cfg.balanced else 0
+    # the workload's single-pass form: balanced (with a workspace) or per sequence;
+    # the shared-prefix pass needs the balanced one and a workspace for the batch
+    if shared_prefix:
+        import paged_kv_cache_450_amd as P
+        wsb = P.paged_attn_prefix_workspace_bytes(cap, cfg.q_heads, cfg.head_dim)
+    else:
+        wsb = P_workspace_bytes(cfg) if cfg.balanced else 0
     workspace = torch.empty(wsb // 4, dtype=torch.float32, device="cuda") if wsb else None
 
     def prompt_kv(spec, layer):
@@ -532,7 +538,8 @@ def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False, swap_slo
         plan = loop.plan()
         host_s += time.perf_counter() - h0
         loop.execute(plan, prompt_kv, step_inputs, cfg.q_heads, k_scale=k_scale,
-                     v_scale=v_scale, workspace=workspace, stream=stream)
+                     v_scale=v_scale, workspace=workspace, stream=stream,
+                     shared_prefix=shared_prefix)
         tokens += len(plan.batch)
         prefill += sum(int(a[2].size) for a in plan.admitted)
         reused += sum(a[1] // BS for a in plan.admitted)
@@ -557,6 +564,7 @@ def serving_rate(cfg, iters: int, stream, groups=(0, 0), caching=False, swap_slo
             "blocks_released_by_window": released,
             "swapped_out": swapped_out, "blocks_swapped": swapped_blocks, "pool_blocks": nb,
             "prefix_caching": caching, "prefix_groups": list(groups),
+            "shared_prefix": shared_prefix, "shared_prefix_groups_run": loop.prefix_groups_run,
             "prefill_tokens": prefill, "cached_blocks_reused": reused,
             "requests_admitted": 4 * iters - len(pending) - len(loop.waiting)}
 
@@ -639,6 +647,9 @@ def main(argv=None):
                     help="run the serving loop on a pool of N blocks")
     ap.add_argument("--serve-gen", type=int, default=128, metavar="N",
                     help="longest generation of the serving stream's requests")
+    ap.add_argument("--serve-shared-prefix", choices=["on", "auto"], default=None,
+                    help="run the serving loop's decode with the shared-prefix pass (always, "
+                         "or when it saves enough repeated reads)")
     ap.add_argument("--serve-window", type=int, default=0, metavar="W",
                     help="run the serving loop with a sliding window of W tokens")
     ap.add_argument("--window", default=None, metavar="W[,W...]",
@@ -831,9 +842,10 @@ def main(argv=None):
                             for x in args.window.split(",")]
     if args.serve > 0:
         groups = tuple(int(x) for x in args.serve_prefix.split(",")) if args.serve_prefix else (0, 0)
+        shared = {None: False, "on": True, "auto": "auto"}[args.serve_shared_prefix]
         result["serving"] = serving_rate(cfg, args.serve, stream, groups, args.serve_caching,
                                          args.serve_swap, args.serve_blocks, args.serve_gen,
-                                         args.serve_window)
+                                         args.serve_window, shared)
     if args.swap > 0:
         result["swap"] = swap_rate(cfg, args.swap, args.steps, stream)
     if args.block_copy > 0:

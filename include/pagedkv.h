@@ -475,7 +475,10 @@ size_t paged_attn_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * Preconditions (not checked, as they live in device memory): the rows of a
  *   group's members hold the same ids in blocks [0, P); every member has
  *   1 <= P <= (L_i - 1) / 16 and seq_prefix_blocks = P; every other sequence
- *   has seq_prefix_blocks = 0; a sequence is in at most one group.
+ *   has seq_prefix_blocks = 0; a sequence is in at most one group, so
+ *   group_offsets[num_groups] <= num_seqs. A plan that breaks them gives wrong
+ *   outputs, not stray accesses: the kernel skips groups whose offsets leave
+ *   [0, num_seqs] and members outside [0, num_seqs).
  * workspace: device, 256-byte aligned, >= paged_attn_prefix_workspace_bytes;
  *   no initial contents needed; calls that share it must be ordered on one
  *   stream. Scale and dtypes: as paged_attn_decode (k_scale / v_scale are not

@@ -48,10 +48,13 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const DecodeParams p) {
     const int gr = pair / p.num_kv_heads, g = pair % p.num_kv_heads;
     const int m0 = p.group_offsets[gr];
     const int msz = p.group_offsets[gr + 1] - m0;
-    if (msz <= 0 || slot * MPS >= msz) return;
-    // Shared blocks, read through the first member's table row.
+    // A plan lists each sequence at most once: members stay inside the batch.
+    if (m0 < 0 || msz <= 0 || m0 + msz > p.num_seqs || slot * MPS >= msz) return;
+    // Shared blocks, read through the first member's table row; a member index
+    // outside the batch is skipped (its rows get zeros and no store).
     const int P = min(max(p.group_blocks[gr], 0), p.max_blocks);
     const int s0 = p.group_members[m0];
+    if (static_cast<uint32_t>(s0) >= static_cast<uint32_t>(p.num_seqs)) return;
 
     const int lane = threadIdx.x & 63;
     const int w = (NW == 1) ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -66,13 +69,15 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const DecodeParams p) {
     const QLds<D> qr{q_lds};
     if (w < NK) {
         const int mi = slot * MPS + hl / G;
-        const int s = p.group_members[m0 + min(mi, msz - 1)];
+        int s = p.group_members[m0 + min(mi, msz - 1)];
+        const bool live = mi < msz && static_cast<uint32_t>(s) < static_cast<uint32_t>(p.num_seqs);
+        if (!live) s = s0;
         const int hq = g * G + hl % G;
         const uint16_t* qrow =
             static_cast<const uint16_t*>(p.q) + (static_cast<size_t>(s) * p.num_q_heads + hq) * D;
         const uint4 qv = *reinterpret_cast<const uint4*>(qrow + 32 * w + 8 * kg);
         *reinterpret_cast<uint4*>(q_lds + w * 1024 + lane * 16) =
-            mi < msz ? qv : make_uint4(0u, 0u, 0u, 0u);
+            live ? qv : make_uint4(0u, 0u, 0u, 0u);
     }
 
     // This wave's tiles: blocks w, w + NW, ... below P.
@@ -160,6 +165,7 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const DecodeParams p) {
             acc = fmaf(lds_o[x][r][d], a, acc);
         }
         const int s = p.group_members[m0 + mi];
+        if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(p.num_seqs)) continue;
         float* dst = p.pre + (static_cast<size_t>(s) * p.num_q_heads + g * G + r % G) * SS;
         dst[d] = l > 0.0f ? acc / l : 0.0f;
         if (d == 0) {

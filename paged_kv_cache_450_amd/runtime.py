@@ -117,6 +117,50 @@ class PagedKVCache:
         kv_cache_append(self.handle, layer, k, v, slots, k_scale, v_scale, stream)
 
 
+# Repeated K/V reads per layer a shared-prefix plan must save before
+# shared_prefix="auto" takes paged_attn_decode_prefix. Measured on MI355X (64
+# sharers, 64 / 8 heads x 128, bf16): 132 MB saved (512 shared tokens) cost 3%
+# per call, 264 MB (1024) gained 6%. The prefix kernel costs about 10 us per
+# call whatever it reads, and the plain pass's repeated reads of a shared block
+# mostly hit the 256 MB last-level cache, so they cost less than their bytes.
+PREFIX_AUTO_BYTES = 200_000_000
+
+
+def prefix_repeated_bytes(plan, desc) -> int:
+    """K/V bytes per layer that the plain pass reads more than once and the
+    prefix pass reads once: (members - 1) x shared blocks, summed over groups."""
+    if plan is None or plan.num_groups == 0:
+        return 0
+    esz = 1 if desc.kv_dtype == PKV_FP8_E4M3 else 2
+    per_block = 2 * desc.num_kv_heads * BLOCK_SIZE * desc.head_dim * esz
+    sizes = np.diff(plan.group_offsets)
+    return int(((sizes - 1) * plan.group_blocks).sum()) * per_block
+
+
+def plan_shared_prefix(tables, lens, max_context_len: int, desc, mode, min_blocks: int = 1):
+    """The host plan for paged_attn_decode_prefix, or None when there is
+    nothing to share or mode is "auto" and the plan saves too little."""
+    plan = paged_attn_prefix_plan(tables, lens, max_context_len, min_blocks)
+    if plan.num_groups == 0:
+        return plan if mode is True else None
+    if mode == "auto" and prefix_repeated_bytes(plan, desc) < PREFIX_AUTO_BYTES:
+        return None
+    return plan
+
+
+def plan_to_device(plan, device):
+    """The plan's four arrays in one host-to-device copy (a copy from pageable
+    memory holds the host until it is done), returned as views."""
+    parts = [np.asarray(a, dtype=np.int32).reshape(-1) for a in
+             (plan.seq_prefix_blocks, plan.group_offsets, plan.group_members, plan.group_blocks)]
+    buf = torch.from_numpy(np.concatenate(parts)).to(device)
+    views, at = [], 0
+    for a in parts:
+        views.append(buf[at:at + a.size])
+        at += a.size
+    return tuple(views)
+
+
 class DecodeBatch:
     """Device-side state of one batch: tables, lengths, workspace and output.
 
@@ -131,15 +175,10 @@ class DecodeBatch:
     group's shared blocks are read once per step (paged_attn_decode_prefix); a
     window set later takes the windowed call instead. shared_prefix="auto" does
     so only when the plan saves at least PREFIX_AUTO_BYTES of repeated reads per
-    layer: the prefix kernel costs about 10 us per call whatever it reads, and
-    the plain pass's repeated reads of a shared block mostly hit the 256 MB
-    last-level cache, so they cost less than their bytes suggest.
+    layer.
     """
 
-    # Repeated K/V reads per layer the prefix pass must save before "auto" takes
-    # it. Measured on MI355X (64 sharers, 64 / 8 heads x 128, bf16): 132 MB
-    # saved (512 shared tokens) cost 3% per call, 264 MB (1024) gained 6%.
-    PREFIX_AUTO_BYTES = 200_000_000
+    PREFIX_AUTO_BYTES = PREFIX_AUTO_BYTES
 
     def __init__(self, cache: PagedKVCache, tables: np.ndarray, lens, num_q_heads: int,
                  q_dtype, partition_size: int = 0, scale=None, k_scale=None, v_scale=None,
@@ -172,32 +211,20 @@ class DecodeBatch:
             if not self.balanced or window > 0 or cache.desc.kv_dtype == PKV_FP8_E4M3:
                 raise ValueError("shared_prefix needs the balanced single pass on a 16-bit "
                                  "cache, without a window")
-            self.plan = paged_attn_prefix_plan(tables, lens, self.max_context_len,
-                                               min_prefix_blocks)
-            if shared_prefix == "auto" and self.repeated_bytes() < self.PREFIX_AUTO_BYTES:
-                self.plan = None
+            self.plan = plan_shared_prefix(tables, lens, self.max_context_len, cache.desc,
+                                           shared_prefix, min_prefix_blocks)
         if self.plan is not None:
             ws = paged_attn_prefix_workspace_bytes(self.num_seqs, num_q_heads, self.head_dim)
-
-            def dev(a):
-                return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
-            self.plan_dev = (dev(self.plan.seq_prefix_blocks), dev(self.plan.group_offsets),
-                             dev(self.plan.group_members), dev(self.plan.group_blocks))
+            self.plan_dev = plan_to_device(self.plan, device)
         if partition_size > 0 or self.balanced:
             self.workspace = torch.empty(max(ws, 16) // 4, dtype=torch.float32, device=device)
         else:
             self.workspace = None
 
     def repeated_bytes(self) -> int:
-        """K/V bytes per layer that the plain pass reads more than once and the
-        prefix pass reads once: (members - 1) x shared blocks per group."""
-        if self.plan is None:
-            return 0
-        d = self.cache.desc
-        esz = 1 if d.kv_dtype == PKV_FP8_E4M3 else 2
-        per_block = 2 * d.num_kv_heads * BLOCK_SIZE * d.head_dim * esz
-        sizes = np.diff(self.plan.group_offsets)
-        return int(((sizes - 1) * self.plan.group_blocks).sum()) * per_block
+        """K/V bytes per layer the plan's prefix pass reads once instead of once
+        per member (0 without a plan)."""
+        return prefix_repeated_bytes(self.plan, self.cache.desc)
 
     def _decode_prefix(self, layer: int, q, new_k, new_v, stream):
         pre, offs, mem, blk = self.plan_dev
@@ -403,6 +430,7 @@ class ContinuousBatcher:
         self.waiting = deque()
         self.running = []
         self.iteration = 0
+        self.prefix_groups_run = 0  # groups read once by paged_attn_decode_prefix, summed
         self._specs = {}
 
     def submit(self, spec) -> None:
@@ -512,11 +540,16 @@ class ContinuousBatcher:
         self.waiting.appendleft(spec)
 
     def execute(self, plan: IterationPlan, prompt_kv, step_inputs, num_q_heads: int,
-                scale=None, k_scale=None, v_scale=None, workspace=None, stream=None):
+                scale=None, k_scale=None, v_scale=None, workspace=None, stream=None,
+                shared_prefix=False):
         """The iteration's GPU work. prompt_kv(spec, layer) -> (k, v): the rows
         of a whole prompt (those after the cached blocks are written);
         step_inputs(layer, batch_size) -> (q, k_new, v_new). Returns the decode
-        outputs, one [B, Hq, D] tensor per layer."""
+        outputs, one [B, Hq, D] tensor per layer. shared_prefix (True or
+        "auto", with a workspace of paged_attn_prefix_workspace_bytes for the
+        batch, no window, a 16-bit cache): the iteration's sequences that begin
+        with the same blocks (forked samples, prompts from the prefix cache)
+        read them once per layer through paged_attn_decode_prefix."""
         h = self.cache.handle
         desc = self.cache.desc
         if plan.swap_in_ids:
@@ -540,6 +573,13 @@ class ContinuousBatcher:
         lens = torch.from_numpy(plan.lens).to(dev)
         sc = (1.0 / math.sqrt(desc.head_dim)) if scale is None else scale
         max_ctx = int(plan.lens.max())
+        pre = None
+        if (shared_prefix and workspace is not None and self.window == 0
+                and desc.kv_dtype != PKV_FP8_E4M3):
+            pp = plan_shared_prefix(plan.tables, plan.lens, max_ctx, desc, shared_prefix)
+            if pp is not None and pp.num_groups > 0:
+                pre = (pp, plan_to_device(pp, dev))
+                self.prefix_groups_run += pp.num_groups
         for layer in range(desc.num_layers):
             q, kn, vn = step_inputs(layer, len(plan.batch))
             out = torch.empty((len(plan.batch), num_q_heads, desc.head_dim), dtype=q.dtype,
@@ -547,6 +587,11 @@ class ContinuousBatcher:
             if self.window > 0:
                 paged_attn_decode_window(h, layer, q, out, tables, lens, sc, max_ctx, self.window,
                                          0, workspace, k_scale, v_scale, kn, vn, stream)
+            elif pre is not None:
+                pp, (spb, offs, mem, blk) = pre
+                paged_attn_decode_prefix(h, layer, q, out, tables, lens, sc, max_ctx, spb, offs,
+                                         mem, blk, pp.num_groups, pp.max_group_size, workspace,
+                                         kn, vn, stream)
             else:
                 paged_attn_decode_append(h, layer, kn, vn, q, out, tables, lens, sc, max_ctx, 0,
                                          workspace, k_scale, v_scale, stream)

@@ -51,8 +51,23 @@ def _gpu(require_gpu):
     ("f16", 2, 2, 64, 14, 40, True, 32, 17)])
 def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching, swap_slots,
                                   window):
+    run_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching, swap_slots, window)
+
+
+# The loop with the shared-prefix pass on its balanced iterations: forked
+# samples share every full prompt block, and with prefix caching requests of
+# one group share a 48-token system prompt.
+@pytest.mark.parametrize("dt,hq,hkv,dim,num_blocks,max_gen,caching", [
+    ("bf16", 8, 2, 128, 40, 12, True), ("f16", 2, 2, 64, 20, 12, True),
+    ("f16", 4, 4, 128, 48, 12, False)])
+def test_continuous_batching_loop_shared_prefix(dt, hq, hkv, dim, num_blocks, max_gen, caching):
+    run_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching, 0, 0, shared_prefix=True)
+
+
+def run_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching, swap_slots, window,
+             shared_prefix=False):
     name = f"batching_{dt}_{hq}_{hkv}_{dim}_{num_blocks}_{caching}"
-    say(f"{name} swap_slots={swap_slots} window={window}")
+    say(f"{name} swap_slots={swap_slots} window={window} shared_prefix={shared_prefix}")
     layers, max_prompt = 2, 40
     width = -(-(max_prompt + 48 + max_gen) // 16)
     groups = (3, 48) if caching else (0, 0)
@@ -70,7 +85,8 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching
         oswap = np.full((swap_slots, layers, 2, hkv, 16, dim), np.iinfo(p6.dtype).max,
                         dtype=p6.dtype)
     scale = float(np.float32(1.0 / np.sqrt(dim)))
-    wsb = P.paged_attn_workspace_bytes(1, hq, dim, 1, 0)
+    wsb = (P.paged_attn_prefix_workspace_bytes(128, hq, dim) if shared_prefix
+           else P.paged_attn_workspace_bytes(1, hq, dim, 1, 0))
     workspace = torch.empty(wsb // 4, dtype=torch.float32, device="cuda")
     pending = list(trace)
     steps = preempted = copies = reused = swapped = trimmed = 0
@@ -102,8 +118,10 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching
                     W.step_rows(name, 0, it, layer, "k", n, hkv, dim, dt, "cuda"),
                     W.step_rows(name, 0, it, layer, "v", n, hkv, dim, dt, "cuda"))
 
+        assert len(p.batch) <= 128
         outs = prod.execute(p, prompt_kv, step_inputs, hq, scale,
-                            workspace=workspace if it % 2 else None)
+                            workspace=workspace if it % 2 else None,
+                            shared_prefix=shared_prefix)
         if orc.swap_in:
             opool.swap_in(p6, oswap, *zip(*orc.swap_in))
         if orc.swap_out:
@@ -146,6 +164,9 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching
         assert swapped > 0 or window
     if window:
         assert trimmed > 0
+    if shared_prefix:
+        assert prod.prefix_groups_run > 0
     say(f"{name}: {steps} steps, {copies} copies, {preempted} preemptions, {swapped} swaps, "
-        f"{reused} cached blocks, {trimmed} blocks released by the window")
+        f"{reused} cached blocks, {trimmed} blocks released by the window, "
+        f"{prod.prefix_groups_run} prefix groups")
     cache.close()
