@@ -68,13 +68,13 @@ MEASURED_TRAFFIC = {  # traffic_key -> counters of the decode call's streaming k
         "kernel": "balanced", "bytes": 849_306_964,
         "sources_sha256": "f6f542117187db5453401ba0f1de80fc21160838df3dc1c2be1b467334bc72f4",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
-    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 358,277.6 KiB x 1.99989 + WRITE 12,412.7 KiB
-        "kernel": "prefix", "bytes": 746_422_283,
-        "sources_sha256": "b95bd360f2d9dd76040cfd3a1dbf9746de4c3c7ae8714d597f46523ae4a443b3",
+    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 358,250.3 KiB x 1.99989 + WRITE 12,411.3 KiB
+        "kernel": "prefix", "bytes": 746_364_330,
+        "sources_sha256": "967297d42bdca39e10093f788069efd27b6317b2b32ea38666aa6d7c25bede53",
         "summary": "profiles/prefix_kernel_gqa_prefix.md"},
-    "gqa_prefix/shared_prefix/prompt2048": {  # streaming kernel: FETCH 262,202.6 KiB x 1.99992 + WRITE 12,448.4 KiB
-        "kernel": "prefix", "bytes": 549_716_322,
-        "sources_sha256": "b95bd360f2d9dd76040cfd3a1dbf9746de4c3c7ae8714d597f46523ae4a443b3",
+    "gqa_prefix/shared_prefix/prompt2048": {  # streaming kernel: FETCH 262,194.7 KiB x 1.99994 + WRITE 12,449.0 KiB
+        "kernel": "prefix", "bytes": 549_707_159,
+        "sources_sha256": "967297d42bdca39e10093f788069efd27b6317b2b32ea38666aa6d7c25bede53",
         "summary": "profiles/prefix_kernel_gqa_prefix.md"},
     "gqa_prefix/prompt2048": {  # streaming kernel: FETCH 471,871.4 KiB x 1.99992 + WRITE 12,327.2 KiB
         "kernel": "balanced", "bytes": 978_977_434,
