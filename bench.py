@@ -156,9 +156,10 @@ class Workload:
         balanced = cfg.balanced if balanced is None else balanced
         # shared_prefix: the balanced single pass on a 16-bit cache reads the
         # blocks its sequences share once (paged_attn_decode_prefix).
+        # (True, or "auto": only when it saves enough repeated reads)
         shared = cfg.shared_prefix if shared_prefix is None else shared_prefix
-        shared = bool(shared and balanced and self.partition_size == 0 and
-                      cfg.kv_dtype != "e4m3")
+        if not (balanced and self.partition_size == 0 and cfg.kv_dtype != "e4m3"):
+            shared = False
         self.batch = DecodeBatch(self.cache, self.tables, lens, cfg.q_heads, qdt,
                                  self.partition_size, device=device, balanced=balanced,
                                  shared_prefix=shared)

@@ -170,3 +170,18 @@ def test_full_size_workload_sampled():
     o = H.oracle_bookkeeping(cfg, 0)
     seqs = sorted(set(H.sample_sequences(cfg, side, 8)) | {0, 2, 3, 126})
     check_layers(cfg, side, o, seqs, range(cfg.layers), whole_pool=False)
+
+
+@pytest.mark.parametrize("prompt,expect_pass", [(512, False), (2048, True)])
+def test_auto_picks_the_pass_and_matches(prompt, expect_pass):
+    """shared_prefix="auto" on the full-size GQA batch: the 512-token shared
+    prompt saves too little and runs the plain pass, a 2048-token one runs the
+    prefix pass; either way sampled outputs match the oracle."""
+    cfg = replace(W.CONFIGS["gqa_prefix"], share_prefix_tokens=prompt)
+    say(f"prefix auto prompt={prompt}")
+    side = H.build_product(cfg, seed=0, fused=True, shared_prefix="auto")
+    torch.cuda.synchronize()
+    assert (side.batch.plan is not None) == expect_pass
+    o = H.oracle_bookkeeping(cfg, 0)
+    seqs = sorted(set(H.sample_sequences(cfg, side, 6)) | {0, 2, 3})
+    check_layers(cfg, side, o, seqs, range(cfg.layers), whole_pool=False)
