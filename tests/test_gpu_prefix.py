@@ -145,6 +145,27 @@ def test_groups_of_every_shape(hq, hkv, dim, dt, groups, singles):
     H.assert_close(H.out_f64(plain.out, dt), ref, dt, "plain balanced pass")
 
 
+def test_many_groups_in_a_large_batch():
+    """600 sequences: 60 groups of 2 to 17 members with shared runs of 1 to 40
+    blocks, and the rest sharing nothing; decode only, against the oracle."""
+    rng = np.random.default_rng(42)
+    groups = [(int(rng.integers(2, 18)), int(rng.integers(1, 41)),
+               [int(x) for x in rng.integers(1, 300, size=3)]) for _ in range(60)]
+    members = sum(g[0] for g in groups)
+    singles = [int(x) for x in rng.integers(1, 900, size=600 - members)]
+    say(f"prefix many groups: {members} members, {len(singles)} singles")
+    cache, tables, lens, expect = hand_built(groups, singles, 4, 64, "f16", 11)
+    q = W.normal((lens.size, 8, 64), "f16", 12, "cuda")
+    batch = DecodeBatch(cache, tables, lens, 8, q.dtype, shared_prefix=True)
+    assert batch.plan.groups() == expect
+    batch.decode(0, q)
+    torch.cuda.synchronize()
+    p6 = opool.view_pool(cache.buf.cpu().numpy(), 1, cache.num_blocks, 16, 4, 64, "f16")
+    scale = float(np.float32(1.0 / math.sqrt(64)))
+    ref = oattn.paged_decode(p6, 0, H.q_f64(q, "f16"), tables, lens, scale, "f16")
+    H.assert_close(H.out_f64(batch.out, "f16"), ref, "f16", "prefix pass, 600 sequences")
+
+
 def test_no_shared_blocks_is_the_plain_pass_bitwise():
     """A batch that shares nothing plans no group: no prefix kernel runs and the
     call gives the plain balanced pass's bits."""
