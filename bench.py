@@ -57,28 +57,28 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {  # traffic_key -> counters of the decode call's streaming kernel
     "llama13b_layer": {  # FETCH 367,298.7 KiB x 1.99988 + WRITE 960.0 KiB
-        "kernel": "valu", "bytes": 753_166_446,
-        "sources_sha256": "226c38afb4b297c88ae0c5e7e2c0154acefe60e2e4f6ead7b50f567b0073cf35",
+        "kernel": "valu", "bytes": 753_164_689,
+        "sources_sha256": "4c433fb86e79da107b4a2f1ffba567c5e9fef8ba727ce55b46766fe30d3f66b0",
         "summary": "profiles/decode_kernel_llama13b_layer.md"},
-    "longctx_fp8": {  # FETCH 715,694.3 KiB x 1.99998 + WRITE 5,755.6 KiB
-        "kernel": "valu", "bytes": 1_471_617_489,
-        "sources_sha256": "226c38afb4b297c88ae0c5e7e2c0154acefe60e2e4f6ead7b50f567b0073cf35",
+    "longctx_fp8": {  # FETCH 715,694.3 KiB x 1.99998 + WRITE 5,755.4 KiB
+        "kernel": "valu", "bytes": 1_471_617_403,
+        "sources_sha256": "4c433fb86e79da107b4a2f1ffba567c5e9fef8ba727ce55b46766fe30d3f66b0",
         "summary": "profiles/decode_kernel_longctx_fp8.md"},
-    "gqa_prefix": {  # streaming kernel: FETCH 408,603.3 KiB x 1.99994 + WRITE 12,217.8 KiB
-        "kernel": "balanced", "bytes": 849_306_964,
-        "sources_sha256": "f6f542117187db5453401ba0f1de80fc21160838df3dc1c2be1b467334bc72f4",
+    "gqa_prefix": {  # streaming kernel: FETCH 408,477.0 KiB x 1.99995 + WRITE 12,218.6 KiB
+        "kernel": "balanced", "bytes": 849_050_127,
+        "sources_sha256": "fb0e407c583d53f647f6619c9aa5a38c64868751379ae4f5af3d03d891d53849",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
-    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 358,250.3 KiB x 1.99989 + WRITE 12,411.3 KiB
-        "kernel": "prefix", "bytes": 746_364_330,
-        "sources_sha256": "967297d42bdca39e10093f788069efd27b6317b2b32ea38666aa6d7c25bede53",
+    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 358,168.5 KiB x 1.99992 + WRITE 12,411.7 KiB
+        "kernel": "prefix", "bytes": 746_210_382,
+        "sources_sha256": "f4832d46105557260663887df860ec1b3c60d21968b7f24404317a3d33fb87d9",
         "summary": "profiles/prefix_kernel_gqa_prefix.md"},
-    "gqa_prefix/shared_prefix/prompt2048": {  # streaming kernel: FETCH 262,194.7 KiB x 1.99994 + WRITE 12,449.0 KiB
-        "kernel": "prefix", "bytes": 549_707_159,
-        "sources_sha256": "967297d42bdca39e10093f788069efd27b6317b2b32ea38666aa6d7c25bede53",
+    "gqa_prefix/shared_prefix/prompt2048": {  # streaming kernel: FETCH 262,192.4 KiB x 1.99995 + WRITE 12,448.4 KiB
+        "kernel": "prefix", "bytes": 549_702_398,
+        "sources_sha256": "f4832d46105557260663887df860ec1b3c60d21968b7f24404317a3d33fb87d9",
         "summary": "profiles/prefix_kernel_gqa_prefix.md"},
-    "gqa_prefix/prompt2048": {  # streaming kernel: FETCH 471,871.4 KiB x 1.99992 + WRITE 12,327.2 KiB
-        "kernel": "balanced", "bytes": 978_977_434,
-        "sources_sha256": "f6f542117187db5453401ba0f1de80fc21160838df3dc1c2be1b467334bc72f4",
+    "gqa_prefix/prompt2048": {  # streaming kernel: FETCH 471,493.9 KiB x 1.99992 + WRITE 12,326.9 KiB
+        "kernel": "balanced", "bytes": 978_203_484,
+        "sources_sha256": "fb0e407c583d53f647f6619c9aa5a38c64868751379ae4f5af3d03d891d53849",
         "summary": "profiles/prefix_kernel_gqa_prefix.md"},
 }
 

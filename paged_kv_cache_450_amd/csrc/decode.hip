@@ -8,7 +8,7 @@
 // [P3] "突破大模型推理瓶颈：...", section 2.4: accumulate in FP32.
 //
 // gfx950 design (decode is HBM-bound: about 1 flop per KV byte for MHA).
-// Three kernels share one contract and one set of helpers:
+// The kernels share one contract and one set of helpers:
 //  * decode_valu.h: vector-ALU math, one workgroup of NW wave64s per (kv
 //    head, sequence, partition): one query head per kv head on 16-bit caches,
 //    and every FP8 cache;
@@ -16,7 +16,10 @@
 //    for grouped query heads on 16-bit caches;
 //  * decode_balanced.h: the balanced single pass (equal tile ranges, one per
 //    resident wave) with either math, and the kernel that merges contexts
-//    split between waves.
+//    split between waves;
+//  * decode_prefix.h: the shared-prefix kernel, which reads the leading
+//    blocks a group of sequences shares once for all of them ahead of the
+//    balanced pass (paged_attn_decode_prefix).
 // Common to all (decode_core.h):
 //  * a (block, kv head) tile of 16 tokens x D is contiguous, and tiles are
 //    read with raw buffer loads whose descriptor is built per tile from the

@@ -27,6 +27,11 @@ using namespace pkv::dev;
 // the log-sum-exp rule (the kernel boundary makes the partials visible; a
 // merge inside the streaming kernel would need device-wide cache maintenance
 // per split, which costs more than the launch).
+//
+// After a shared-prefix pass (decode_prefix.h), a group member's tiles start
+// at the first block after the shared run, a member's context written whole
+// by one wave goes to its own partial slot instead of the output, and the
+// merge folds the prefix partial in as one more piece.
 
 // Issue-side walker over the tiles of the batch in (sequence, kv head, block)
 // order, holding the block ids of the current sequence's table row: the first
