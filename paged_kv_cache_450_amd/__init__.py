@@ -62,7 +62,10 @@ def _load():
             "(there is no fallback path)")
     L = ctypes.CDLL(_LIB_PATH)
     i32, i64, sz, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
-    p_i32, p_i64 = ctypes.POINTER(i32), ctypes.POINTER(i64)
+    # Host arrays go in as plain addresses (numpy's data pointer as an int):
+    # building a typed ctypes pointer per argument costs more than the
+    # bookkeeping call itself.
+    p_i32 = p_i64 = p_u64 = vp
     p_desc = ctypes.POINTER(PoolDesc)
     sig = {
         "kv_pool_bytes": (sz, [p_desc]),
@@ -82,8 +85,8 @@ def _load():
         "kv_swap_slot_bytes": (sz, [vp]),
         "kv_swap_out": (i32, [vp, p_i32, p_i32, i32, vp, sz, vp]),
         "kv_swap_in": (i32, [vp, p_i32, p_i32, i32, vp, sz, vp]),
-        "kv_prefix_register": (i32, [vp, ctypes.POINTER(ctypes.c_uint64), p_i32, i32, p_i32]),
-        "kv_prefix_acquire": (i32, [vp, ctypes.POINTER(ctypes.c_uint64), i32, p_i32, p_i32]),
+        "kv_prefix_register": (i32, [vp, p_u64, p_i32, i32, p_i32]),
+        "kv_prefix_acquire": (i32, [vp, p_u64, i32, p_i32, p_i32]),
         "kv_pool_num_cached": (i32, [vp]),
         "kv_seq_trim": (i32, [vp, i32, p_i32, i32, p_i32, i32, p_i32]),
         "paged_attn_decode_window": (i32, [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, i32,
@@ -122,8 +125,9 @@ def _check(status: int) -> None:
         raise PkvError(status, pkv_last_error())
 
 
-def _i32_ptr(a: np.ndarray):
-    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+def _i32_ptr(a: np.ndarray) -> int:
+    """Address of a host int32 array's data, as the C calls take it."""
+    return a.ctypes.data
 
 
 def _host_i32(a, writable=False) -> np.ndarray:
@@ -179,8 +183,8 @@ def kv_pool_cached_list(pool) -> np.ndarray:
     return out
 
 
-def _u64_ptr(a: np.ndarray):
-    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
+def _u64_ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
 
 
 def kv_prefix_register(pool, keys, ids) -> int:
@@ -241,7 +245,7 @@ def kv_seq_extend(pool, block_tables: np.ndarray, cur_lens, new_lens) -> np.ndar
     total = int(new.astype(np.int64).sum() - cur.astype(np.int64).sum())
     slots = np.empty(max(total, 0), dtype=np.int64)
     _check(lib.kv_seq_extend(pool, bt.shape[0], _i32_ptr(bt), bt.shape[1], _i32_ptr(cur),
-                             _i32_ptr(new), slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+                             _i32_ptr(new), slots.ctypes.data))
     return slots
 
 
@@ -262,7 +266,7 @@ def kv_seq_extend_cow(pool, block_tables: np.ndarray, cur_lens, new_lens):
     n = ctypes.c_int32(0)
     _check(lib.kv_seq_extend_cow(pool, bt.shape[0], _i32_ptr(bt), bt.shape[1], _i32_ptr(cur),
                                  _i32_ptr(new),
-                                 slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                 slots.ctypes.data,
                                  _i32_ptr(src), _i32_ptr(dst), ctypes.byref(n)))
     return slots, src[:n.value].copy(), dst[:n.value].copy()
 

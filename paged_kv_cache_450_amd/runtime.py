@@ -508,8 +508,11 @@ class ContinuousBatcher:
         if p.batch:
             if self.window > 0:
                 p.trimmed = kv_seq_trim(h, tables, cur + 1, self.window)
+            # Each row becomes a view of this iteration's table (no copy): the
+            # next iteration stacks the rows into a new array, so this one is
+            # never written again once the plan is returned.
             for k, s in enumerate(p.batch):
-                s.row[:] = tables[k]
+                s.row = tables[k]
                 s.length += 1
                 s.generated += 1
             p.tables, p.lens, p.slots = tables, cur + 1, slots
