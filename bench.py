@@ -68,13 +68,13 @@ MEASURED_TRAFFIC = {  # traffic_key -> counters of the decode call's streaming k
         "kernel": "balanced", "bytes": 849_050_127,
         "sources_sha256": "fb0e407c583d53f647f6619c9aa5a38c64868751379ae4f5af3d03d891d53849",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
-    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 358,168.5 KiB x 1.99992 + WRITE 12,411.7 KiB
-        "kernel": "prefix", "bytes": 746_210_382,
-        "sources_sha256": "f4832d46105557260663887df860ec1b3c60d21968b7f24404317a3d33fb87d9",
+    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 358,265.8 KiB x 1.99989 + WRITE 12,411.6 KiB
+        "kernel": "prefix", "bytes": 746_396_022,
+        "sources_sha256": "fd635a157ed1a8cea7607948a27cebaaa807559ce56cf220e33ab9b9d5556dc5",
         "summary": "profiles/prefix_kernel_gqa_prefix.md"},
-    "gqa_prefix/shared_prefix/prompt2048": {  # streaming kernel: FETCH 262,192.4 KiB x 1.99995 + WRITE 12,448.4 KiB
-        "kernel": "prefix", "bytes": 549_702_398,
-        "sources_sha256": "f4832d46105557260663887df860ec1b3c60d21968b7f24404317a3d33fb87d9",
+    "gqa_prefix/shared_prefix/prompt2048": {  # streaming kernel: FETCH 262,190.6 KiB x 1.99992 + WRITE 12,448.0 KiB
+        "kernel": "prefix", "bytes": 549_690_992,
+        "sources_sha256": "fd635a157ed1a8cea7607948a27cebaaa807559ce56cf220e33ab9b9d5556dc5",
         "summary": "profiles/prefix_kernel_gqa_prefix.md"},
     "gqa_prefix/prompt2048": {  # streaming kernel: FETCH 471,493.9 KiB x 1.99992 + WRITE 12,326.9 KiB
         "kernel": "balanced", "bytes": 978_203_484,

@@ -175,13 +175,14 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(const DecodeParams p) {
     }
 }
 
-// The shared-prefix kernel: four waves per 16 query rows (eight measured no
-// faster), the matrix-core ring depths (three tiles at D = 128, four at
-// D = 64).
+// The shared-prefix kernel: eight waves per 16 query rows (the shared run is
+// streamed by the waves in turn, so more waves mean fewer ring rounds each:
+// 5% faster than four on 256 shared blocks), the matrix-core ring depths
+// (three tiles at D = 128, four at D = 64).
 template <int KV, int D, int G>
 hipError_t launch_prefix(const DecodeParams& prm, hipStream_t st) {
     constexpr int R = (D == 128) ? 3 : 4;
-    constexpr int NW = 4;
+    constexpr int NW = 8;
     const uint32_t pairs = static_cast<uint32_t>(prm.num_groups) * prm.num_kv_heads;
     const uint32_t wgs = (pairs + 7) / 8 * 8 * static_cast<uint32_t>(prm.pre_slots);
     hipLaunchKernelGGL((prefix_kernel<KV, D, G, NW, R>), dim3(wgs), dim3(NW * 64), 0, st, prm);
