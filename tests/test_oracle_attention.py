@@ -275,3 +275,103 @@ def test_planted_merge_mistake_fails_identity():
         return (w[:, :, None] * o).sum(axis=0) / w.sum(axis=0)[:, None]
     with pytest.raises(AssertionError):
         check_split_merge(attention.partials, bad_merge)
+
+
+# ----------------------------------------------- FP8 (E4M3) KV cache pins ----
+# [P2] "vLLM 也不是银弹：真实部署中的坑", third pitfall: an FP8 KV cache. Each kv
+# head has its own K scale and V scale, and a stored code means
+# decode(code) * scale. The brute force below dequantises through torch's
+# float8_e4m3fn conversion (a library routine, not the oracle's table) and
+# attends with Python floats. The scales differ per head and between K and V
+# by large factors, so applying a scale to the wrong operand or head moves
+# every output far outside the tolerance.
+FP8_K_SCALE = np.array([0.01, 0.37, 0.055], dtype=np.float32)
+FP8_V_SCALE = np.array([0.25, 4.0, 0.8], dtype=np.float32)
+
+
+def e4m3_codes(rng, shape):
+    """Random finite E4M3 codes (never the NaN codes 0x7F / 0xFF)."""
+    c = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    return np.where((c & 0x7F) == 0x7F, c ^ 0x01, c).astype(np.uint8)
+
+
+def build_paged_e4m3(rng, lengths, hkv, dim, num_blocks):
+    """As build_paged, for a uint8 E4M3 pool; unused slots hold NaN codes."""
+    pool6 = np.full((1, 2, num_blocks, hkv, BS, dim), 0x7F, dtype=np.uint8)
+    ids = rng.permutation(num_blocks)
+    maxb = max(-(-l // BS) for l in lengths)
+    tables = np.full((len(lengths), maxb + 1), -1, dtype=np.int32)
+    ks, vs, pos = [], [], 0
+    for i, length in enumerate(lengths):
+        k = e4m3_codes(rng, (length, hkv, dim))
+        v = e4m3_codes(rng, (length, hkv, dim))
+        ks.append(k)
+        vs.append(v)
+        for j in range(-(-length // BS)):
+            b = int(ids[pos]); pos += 1
+            tables[i, j] = b
+            lo, hi = j * BS, min((j + 1) * BS, length)
+            pool6[0, 0, b, :, : hi - lo, :] = k[lo:hi].transpose(1, 0, 2)
+            pool6[0, 1, b, :, : hi - lo, :] = v[lo:hi].transpose(1, 0, 2)
+    return pool6, tables, ks, vs
+
+
+def torch_dequant(codes, scales):
+    """[L, Hkv, D] codes -> nested Python floats, code value x its head's scale."""
+    vals = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return (vals * scales.astype(np.float64)[None, :, None]).tolist()
+
+
+def check_fp8_against_brute_force(decode_fn, seed=21):
+    rng = np.random.default_rng(seed)
+    for hq, hkv, dim, lengths in [(3, 3, 8, [1, 9, 16, 35]),
+                                  (6, 3, 4, [17, 40]),
+                                  (2, 2, 16, [50])]:
+        ksc, vsc = FP8_K_SCALE[:hkv], FP8_V_SCALE[:hkv]
+        pool6, tables, ks, vs = build_paged_e4m3(rng, lengths, hkv, dim, num_blocks=24)
+        q = rng.standard_normal((len(lengths), hq, dim))
+        scale = 1.0 / math.sqrt(dim)
+        got = decode_fn(pool6, 0, q, tables, np.array(lengths), scale, "e4m3",
+                        k_scale=ksc, v_scale=vsc)
+        for i, length in enumerate(lengths):
+            ref = brute_attention(q[i].tolist(), torch_dequant(ks[i], ksc),
+                                  torch_dequant(vs[i], vsc), scale, hq // hkv)
+            assert np.allclose(got[i], np.array(ref), rtol=1e-12, atol=1e-12), (hq, hkv, length)
+
+
+def test_fp8_paged_decode_matches_brute_force():
+    check_fp8_against_brute_force(attention.paged_decode)
+
+
+def test_fp8_single_token_gives_scaled_value_exactly():
+    """L = 1: the output is the stored V code times that head's V scale."""
+    rng = np.random.default_rng(22)
+    pool6, tables, ks, vs = build_paged_e4m3(rng, [1], 3, 8, 4)
+    q = rng.standard_normal((1, 3, 8))
+    out = attention.paged_decode(pool6, 0, q, tables, np.array([1]), 0.3, "e4m3",
+                                 k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
+    ref = np.array(torch_dequant(vs[0], FP8_V_SCALE))[0]
+    assert np.array_equal(out[0], ref)
+
+
+def _fp8_mutant(kind):
+    """paged_decode with one planted mistake in the FP8 scale handling."""
+    def decode(pool6, layer, q, tables, lens, scale, kv_dtype, k_scale=None, v_scale=None):
+        if kind == "swap_scales":
+            k_scale, v_scale = v_scale, k_scale
+        elif kind == "k_scale_for_both":
+            v_scale = k_scale
+        elif kind == "reversed_heads":
+            k_scale, v_scale = k_scale[::-1].copy(), v_scale[::-1].copy()
+        elif kind == "v_unscaled":
+            v_scale = np.ones_like(v_scale)
+        return attention.paged_decode(pool6, layer, q, tables, lens, scale, kv_dtype,
+                                      k_scale=k_scale, v_scale=v_scale)
+    return decode
+
+
+@pytest.mark.parametrize("kind", ["swap_scales", "k_scale_for_both", "reversed_heads",
+                                  "v_unscaled"])
+def test_planted_fp8_scale_mistakes_fail_brute_force(kind):
+    with pytest.raises(AssertionError):
+        check_fp8_against_brute_force(_fp8_mutant(kind))
