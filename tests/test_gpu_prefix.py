@@ -121,8 +121,9 @@ def hand_built(groups, singles, hkv, dim, dt, seed):
     (16, 2, 128, "bf16", [(5, 3, [1, 33]), (2, 40, [1, 200]), (3, 1, [9])], [1, 700]),
     (8, 2, 64, "f16", [(7, 64, [1, 17, 500]), (4, 6, [2])], [64, 65, 1000]),
     (8, 4, 64, "bf16", [(2, 1, [1])], []),
-    # a shared run of 300 blocks: each wave's block ids rotate past their first 64
-    (16, 2, 128, "bf16", [(3, 300, [1, 50, 17])], [40]),
+    # a shared run of 600 blocks dealt to the prefix kernel's eight waves: 75
+    # tiles each, so every wave's block ids rotate past their first 64
+    (16, 2, 128, "bf16", [(3, 600, [1, 50, 17])], [40]),
 ])
 def test_groups_of_every_shape(hq, hkv, dim, dt, groups, singles):
     """Hand-built batches with several groups of different sizes and shared
