@@ -497,6 +497,44 @@ pkv_status paged_attn_decode_prefix(const pkv_pool* pool, int32_t layer, const v
                                     int32_t max_group_size, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of the library's static device scratch, one copy per GPU, that
+ * paged_attn_decode_append_noalloc uses as its workspace. */
+#define PKV_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* paged_attn_decode_append without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. The workspace is a static device
+ * array of the library (PKV_STATIC_SCRATCH_BYTES, 32 MiB; each GPU the call
+ * runs on holds its own copy until the process ends). Nothing is allocated:
+ * the array's device address is looked up once per device (with that device
+ * current) on the first call there.
+ * Differences from paged_attn_decode_append:
+ *  - out is always written: with partition_size > 0 the call runs
+ *    paged_attn_reduce on the partials itself, on the same stream;
+ *  - partition_size == 0 on a 16-bit cache with up to 4096 sequences takes
+ *    the balanced single pass (as paged_attn_decode_append with a workspace);
+ *    FP8 caches and larger batches take the per-sequence pass, which needs no
+ *    workspace.
+ * The scratch needs no initial contents. The current device must be the
+ * device of stream and of every buffer. Every call on one GPU shares that
+ * GPU's array, so calls that may overlap on one GPU (other streams, other
+ * threads) race on it: order them on one stream.
+ * Every other argument and the output are those of paged_attn_decode_append.
+ * Errors: INVALID (a batch whose workspace would exceed
+ *   PKV_STATIC_SCRATCH_BYTES, NULL out, and every error of
+ *   paged_attn_decode_append and paged_attn_reduce), HIP (also when the
+ *   scratch's device address cannot be had). */
+pkv_status paged_attn_decode_append_noalloc(const pkv_pool* pool, int32_t layer,
+                                            const void* new_k, const void* new_v,
+                                            int32_t src_dtype, const void* q, int32_t q_dtype,
+                                            void* out, const int32_t* block_tables,
+                                            int32_t max_blocks_per_seq,
+                                            const int32_t* context_lens, int32_t num_seqs,
+                                            int32_t num_q_heads, float scale,
+                                            const float* k_scale, const float* v_scale,
+                                            int32_t max_context_len, int32_t partition_size,
+                                            hipStream_t stream);
+
 /* Merge the partitions a partitioned paged_attn_decode left in workspace
  * into out (device [num_seqs][num_q_heads][head_dim] of out_dtype F16 or BF16):
  *   M = max_p m_p, w_p = l_p exp(m_p - M), out = sum_p w_p o_p / sum_p w_p

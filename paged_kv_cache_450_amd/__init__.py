@@ -23,12 +23,13 @@ __all__ = [
     "kv_seq_fork", "kv_seq_extend", "kv_cache_append", "paged_attn_workspace_bytes",
     "paged_attn_decode", "paged_attn_reduce", "pkv_last_error", "library_path", "lib",
     "PrefixPlan", "paged_attn_prefix_plan", "paged_attn_prefix_workspace_bytes",
-    "paged_attn_decode_prefix",
+    "paged_attn_decode_prefix", "paged_attn_decode_append_noalloc", "STATIC_SCRATCH_BYTES",
 ]
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_STATE, PKV_ERR_HIP = 0, -1, -2, -3, -4
 PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 BLOCK_SIZE = 16
+STATIC_SCRATCH_BYTES = 32 << 20  # PKV_STATIC_SCRATCH_BYTES
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
@@ -98,6 +99,8 @@ def _load():
                                     i32, i32, vp, sz, vp]),
         "paged_attn_decode_append": (i32, [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, i32,
                                            i32, f32, vp, vp, i32, i32, vp, sz, vp]),
+        "paged_attn_decode_append_noalloc": (i32, [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32,
+                                                   vp, i32, i32, f32, vp, vp, i32, i32, vp]),
         "paged_attn_reduce": (i32, [vp, vp, i32, vp, i32, i32, i32, i32, i32, vp]),
         "paged_attn_prefix_plan": (i32, [p_i32, i32, p_i32, i32, i32, i32, p_i32, p_i32, p_i32,
                                          p_i32, p_i32, p_i32]),
@@ -438,6 +441,32 @@ def paged_attn_decode_append(pool, layer: int, new_k, new_v, q, out, block_table
         _ptr(out), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), q.shape[0],
         q.shape[1], float(scale), _ptr(k_scale), _ptr(v_scale), max_context_len, partition_size,
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def paged_attn_decode_append_noalloc(pool, layer: int, new_k, new_v, q, out, block_tables,
+                                     context_lens, scale: float, max_context_len: int,
+                                     partition_size: int = 0, k_scale=None, v_scale=None,
+                                     stream=None) -> None:
+    """paged_attn_decode_append with the library's static scratch as its
+    workspace (nothing allocated by the caller); out is always written (split-K
+    runs its reduce in the same call)."""
+    torch = _torch()
+    _dev(new_k, "new_k"); _dev(new_v, "new_v")
+    _dev(q, "q"); _dev(out, "out"); _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    _dev(k_scale, "k_scale", torch.float32); _dev(v_scale, "v_scale", torch.float32)
+    if q.dim() != 3 or block_tables.dim() != 2:
+        raise ValueError("q must be [B, Hq, D] and block_tables [B, W]")
+    if new_k.shape != new_v.shape or new_k.dtype != new_v.dtype or new_k.dim() != 3 or \
+            new_k.shape[0] != q.shape[0] or new_k.shape[2] != q.shape[2]:
+        raise ValueError("new_k and new_v must be [B, Hkv, D] like q")
+    if out is None or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    _check(lib.paged_attn_decode_append_noalloc(
+        pool, layer, _ptr(new_k), _ptr(new_v), _dtype_code(new_k), _ptr(q), _dtype_code(q),
+        _ptr(out), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), q.shape[0],
+        q.shape[1], float(scale), _ptr(k_scale), _ptr(v_scale), max_context_len, partition_size,
+        _stream(stream)))
 
 
 def paged_attn_decode_window(pool, layer: int, q, out, block_tables, context_lens, scale: float,

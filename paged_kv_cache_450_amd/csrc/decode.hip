@@ -44,6 +44,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "common.h"
 #include "decode_balanced.h"
@@ -548,4 +549,93 @@ extern "C" pkv_status paged_attn_decode_prefix(
                        context_lens, num_seqs, num_q_heads, scale, nullptr, nullptr,
                        max_context_len, 0, workspace, workspace_bytes, new_k, new_v, 0, stream,
                        &pfx);
+}
+
+// ---------------------------------------------------------------------------
+// The decode step for callers that cannot allocate device memory (code under
+// graph capture, tight serving loops, harnesses that forbid allocation): the
+// workspace is a static device array of the library, one per GPU, instead of
+// a caller buffer.
+namespace {
+
+constexpr size_t kScratchBytes = PKV_STATIC_SCRATCH_BYTES;  // per GPU
+
+// Host code never passes this name to a kernel or a copy: it stands for the
+// array on the host side only. Its device address on each GPU comes from
+// hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];  // device address of `scratch` on each GPU (NULL: not looked up)
+
+// Device address of the scratch array on the current device, looked up once
+// per device with that device current.
+pkv_status scratch_address(const char* fn, void** out) {
+    using pkv::fail;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(PKV_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PKV_ERR_INVALID, "%s: device %d beyond the %d the library tracks", fn, dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(PKV_ERR_HIP, "%s: no device address for the scratch array: %s", fn,
+                        hipGetErrorString(e));
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" pkv_status paged_attn_decode_append_noalloc(
+    const pkv_pool* pool, int32_t layer, const void* new_k, const void* new_v, int32_t src_dtype,
+    const void* q, int32_t q_dtype, void* out, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, float scale, const float* k_scale, const float* v_scale,
+    int32_t max_context_len, int32_t partition_size, hipStream_t stream) {
+    using pkv::fail;
+    const char* fn = "paged_attn_decode_append_noalloc";
+    if (pool == nullptr) return fail(PKV_ERR_INVALID, "%s: pool is NULL", fn);
+    const pkv_pool_desc& d = pool->desc;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_q_heads % d.num_kv_heads != 0 ||
+        max_context_len < 0 || partition_size < 0)
+        return fail(PKV_ERR_INVALID, "%s: bad sizes", fn);
+    if (num_seqs == 0) return PKV_OK;
+    if (out == nullptr) return fail(PKV_ERR_INVALID, "%s: out is NULL", fn);
+    // The scratch this call needs: the split-K partials, or the balanced
+    // pass's split-context partials (16-bit caches, up to 4096 sequences);
+    // the per-sequence pass (FP8 caches, larger batches) needs none.
+    size_t need = 0;
+    if (partition_size > 0) {
+        need = paged_attn_workspace_bytes(num_seqs, num_q_heads, d.head_dim, max_context_len,
+                                          partition_size);
+    } else if (pkv::is_16bit(d.kv_dtype) && num_seqs <= kBalancedMaxSeqs) {
+        const size_t waves = static_cast<size_t>(device_cu_count()) * kBalancedWavesPerCu;
+        need = balanced_bytes(static_cast<size_t>(num_q_heads / d.num_kv_heads), d.head_dim,
+                              waves);
+    }
+    if (need > kScratchBytes)
+        return fail(PKV_ERR_INVALID,
+                    "%s: this batch needs %zu bytes of workspace; the static scratch holds %zu "
+                    "(use paged_attn_decode_append with a workspace)", fn, need, kScratchBytes);
+    void* ws = nullptr;
+    if (need > 0) {
+        const pkv_status st = scratch_address(fn, &ws);
+        if (st != PKV_OK) return st;
+    }
+    const pkv_status st = paged_attn_decode_append(
+        pool, layer, new_k, new_v, src_dtype, q, q_dtype, partition_size > 0 ? nullptr : out,
+        block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads, scale, k_scale,
+        v_scale, max_context_len, partition_size, ws, need > 0 ? kScratchBytes : 0, stream);
+    if (st != PKV_OK || partition_size == 0) return st;
+    return paged_attn_reduce(ws, out, q_dtype, context_lens, num_seqs, num_q_heads, d.head_dim,
+                             max_context_len, partition_size, stream);
 }
