@@ -24,6 +24,10 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["pool.cpp", "prefix_plan.cpp", "append.hip", "decode.hip", "reduce.hip", "copy.hip",
            "swap.hip"]
+# The gather-rate probe (a measuring instrument for bench.py, not the decode
+# path) goes into a library of its own.
+PROBE_SOURCES = ["probe.hip"]
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libpkvprobe.so")
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of the device code.
@@ -53,19 +57,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str, verbose: bool) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"linking {LIB_NAME} failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError(f"linking {os.path.basename(path)} failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the shared libraries (the decode library
+    and the probe library); returns the decode library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB_PATH, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 
