@@ -93,17 +93,21 @@ def sources_sha256(kernel: str) -> str:
     return h.hexdigest()
 
 
-def traffic_key(cfg, w, args) -> str:
-    """The measured-traffic entry that matches this run: the workload in its
-    default form, or with the options that change what the call launches."""
+def traffic_key(cfg, w, args=None) -> str:
+    """The measured-traffic entry that matches this run: the workload, with
+    the options that change what the call launches (args None: the
+    workload's default options)."""
     key = cfg.name
-    if args.unfused:
+    if args is not None and args.unfused:
         key += "/unfused"
-    if args.partition_size is not None and args.partition_size != cfg.partition_size:
+    if (args is not None and args.partition_size is not None
+            and args.partition_size != cfg.partition_size):
         key += f"/ps{args.partition_size}"
     if w.batch.plan is not None:
         key += "/shared_prefix"
-    if args.prefix_tokens:
+    if w.batch.l2_blocks is not None:
+        key += "/shared_prefix_l2"
+    if args is not None and args.prefix_tokens:
         key += f"/prompt{args.prefix_tokens}"
     return key
 
@@ -301,23 +305,54 @@ class OracleBookkeeping:
         return np.concatenate([[0], np.cumsum(counts)])
 
 
-def cpu_baseline(w: Workload, budget_s: float):
+def _oracle_worker(job):
+    """One worker of cpu_baseline's parallel leg, in a spawned process of its
+    own (one BLAS thread): maps the oracle's host pool read-only from a file
+    and runs the oracle's decode over its share of the sequences, whole passes
+    until its budget is spent. Returns its start and end on the system-wide
+    monotonic clock, the KV bytes it decoded and the sequences it did."""
+    from oracle import attention as oattn
+
+    path, shape, dtype, rows, lens, qs, scale, kv_dtype, ks, vs, esz, budget = job
+    p6 = np.memmap(path, dtype=dtype, mode="r", shape=shape)
+    t_start = time.monotonic()
+    elapsed, done, seqs = 0.0, 0, 0
+    while elapsed < budget:
+        for row, n, q in zip(rows, lens, qs):
+            t0 = time.perf_counter()
+            oattn.paged_decode(p6, 0, q, row[None], np.array([n]), scale, kv_dtype, ks, vs)
+            elapsed += time.perf_counter() - t0
+            done += int(n) * shape[3] * shape[5] * 2 * esz
+            seqs += 1
+            if elapsed >= budget:
+                break
+    t_end = time.monotonic()
+    del p6
+    return t_start, t_end, done, seqs
+
+
+def cpu_baseline(w: Workload, budget_s: float, workers=None):
     """The fp64 oracle, as it is, on a bounded sample of the same workload:
     whole sequences, in order, until about budget_s of CPU work. Only the
     oracle's decode (gather through the table, softmax, PV) is timed; its
     host pool is built by the oracle's own append, with the oracle's own
-    bookkeeping, from host copies of the seeded inputs."""
+    bookkeeping, from host copies of the seeded inputs.
+
+    Two legs: `value` runs the sequences over `workers` spawned processes at
+    once (one BLAS thread each; the oracle's per-head loop uses one core per
+    process), as many as the host's cores allow up to 16, and reports the
+    aggregate rate over the wall time from the first worker's start to the
+    last one's end; `single_thread` runs them in this process with BLAS
+    limited to one thread."""
+    import multiprocessing as mp
+    import tempfile
+
     import torch
 
     from oracle import attention as oattn
     from oracle import pool as opool
 
     cfg = w.cfg
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
     ob = OracleBookkeeping(cfg, w.seed)
     offs = ob.token_offsets()
 
@@ -326,52 +361,90 @@ def cpu_baseline(w: Workload, budget_s: float):
 
     nb = ob.model.num_blocks
     per_layer = opool.pool_bytes(1, nb, BS, cfg.kv_heads, cfg.head_dim, cfg.kv_dtype)
-    buf = np.zeros(per_layer, dtype=np.uint8)
-    p6 = opool.view_pool(buf, 1, nb, BS, cfg.kv_heads, cfg.head_dim, cfg.kv_dtype)
-    ks = vs = None
-    if cfg.kv_dtype == "e4m3":
-        ks, vs = w.k_scale[0].cpu().numpy(), w.v_scale[0].cpu().numpy()
-    scale = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))
-    esz = opool.ESIZE[cfg.kv_dtype]
-    # Host pool: the oracle's own append of every private sequence's tokens.
-    todo = []
-    for i in range(cfg.batch):
-        if ob.start[i] > 0:
-            continue  # a prefix sharer; its prefix owner's tokens are not in this host pool
-        lo, hi = int(offs[i]), int(offs[i + 1])
-        opool.append(p6, 0, raw(w.k_cached[0][lo:hi]), raw(w.v_cached[0][lo:hi]), cfg.src_dtype,
-                     cfg.kv_dtype, ob.slots_cached[lo:hi], ks, vs)
-        opool.append(p6, 0, raw(w.k_new[0][i:i + 1]), raw(w.v_new[0][i:i + 1]), cfg.src_dtype,
-                     cfg.kv_dtype, ob.slots_new[i:i + 1], ks, vs)
-        todo.append((i, opool.raw_to_f64(raw(w.q[0][i:i + 1]), cfg.q_dtype)))
-    def run(budget):
-        """Whole passes over those sequences until about budget s of oracle decode."""
-        elapsed, done_bytes, seqs, passes = 0.0, 0, 0, 0
-        while elapsed < budget and todo:
-            for i, q in todo:
-                t0 = time.perf_counter()
-                oattn.paged_decode(p6, 0, q, ob.tables[i:i + 1], ob.lens[i:i + 1], scale,
-                                   cfg.kv_dtype, ks, vs)
-                elapsed += time.perf_counter() - t0
-                done_bytes += int(ob.lens[i]) * cfg.kv_heads * cfg.head_dim * 2 * esz
-                seqs += 1
-                if elapsed >= budget:
-                    break
-            passes += 1
-        return {"value": round(done_bytes / elapsed / 1e9, 4),
-                "seqs_per_s": round(seqs / elapsed, 3),
-                "sample": f"{seqs} sequence decodes ({passes} passes over the {len(todo)} "
-                          f"sequences of {cfg.name} layer 0; {done_bytes / 1e6:.1f} MB of KV), "
-                          f"fp64 numpy decode only, {elapsed:.1f} s"}
-
-    every = run(budget_s)
-    single = None
+    shm_dir = "/dev/shm" if os.path.isdir("/dev/shm") else None
+    tmp = tempfile.NamedTemporaryFile(prefix="pkv_oracle_pool_", dir=shm_dir, delete=False)
+    tmp.close()
     try:
-        from threadpoolctl import threadpool_limits
-        with threadpool_limits(limits=1):
-            single = run(budget_s / 2)
-    except ImportError:
-        pass
+        buf = np.memmap(tmp.name, dtype=np.uint8, mode="w+", shape=(per_layer,))
+        p6 = opool.view_pool(buf, 1, nb, BS, cfg.kv_heads, cfg.head_dim, cfg.kv_dtype)
+        ks = vs = None
+        if cfg.kv_dtype == "e4m3":
+            ks, vs = w.k_scale[0].cpu().numpy(), w.v_scale[0].cpu().numpy()
+        scale = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))
+        esz = opool.ESIZE[cfg.kv_dtype]
+        # Host pool: the oracle's own append of every private sequence's tokens.
+        todo = []
+        for i in range(cfg.batch):
+            if ob.start[i] > 0:
+                continue  # a prefix sharer; its prefix owner's tokens are not in this host pool
+            lo, hi = int(offs[i]), int(offs[i + 1])
+            opool.append(p6, 0, raw(w.k_cached[0][lo:hi]), raw(w.v_cached[0][lo:hi]),
+                         cfg.src_dtype, cfg.kv_dtype, ob.slots_cached[lo:hi], ks, vs)
+            opool.append(p6, 0, raw(w.k_new[0][i:i + 1]), raw(w.v_new[0][i:i + 1]), cfg.src_dtype,
+                         cfg.kv_dtype, ob.slots_new[i:i + 1], ks, vs)
+            todo.append((i, opool.raw_to_f64(raw(w.q[0][i:i + 1]), cfg.q_dtype)))
+        buf.flush()
+
+        def what(seqs, passes, done, secs):
+            return (f"{seqs} sequence decodes ({passes} over the {len(todo)} sequences of "
+                    f"{cfg.name} layer 0; {done / 1e6:.1f} MB of KV), fp64 numpy decode only, "
+                    f"{secs:.1f} s")
+
+        # Parallel leg: sequences dealt round robin to the workers.
+        n_work = workers or max(1, min(16, os.cpu_count() or 1, len(todo)))
+        jobs = []
+        for k in range(n_work):
+            mine = todo[k::n_work]
+            jobs.append((tmp.name, p6.shape, p6.dtype, [ob.tables[i] for i, _ in mine],
+                         [int(ob.lens[i]) for i, _ in mine], [q for _, q in mine], scale,
+                         cfg.kv_dtype, ks, vs, esz, budget_s))
+        saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                                 "MKL_NUM_THREADS")}
+        os.environ.update({k: "1" for k in saved})
+        try:
+            with mp.get_context("spawn").Pool(n_work) as pool:
+                res = pool.map(_oracle_worker, jobs, chunksize=1)
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+        wall = max(r[1] for r in res) - min(r[0] for r in res)
+        done = sum(r[2] for r in res)
+        seqs = sum(r[3] for r in res)
+        par = {"value": round(done / wall / 1e9, 4), "seqs_per_s": round(seqs / wall, 3),
+               "sample": what(seqs, "whole passes of each worker", done, wall)
+               + f" of wall time on {n_work} worker processes"}
+
+        def run(budget):
+            """Whole passes over those sequences until about budget s of oracle decode."""
+            elapsed, done_bytes, nseq, passes = 0.0, 0, 0, 0
+            while elapsed < budget and todo:
+                for i, q in todo:
+                    t0 = time.perf_counter()
+                    oattn.paged_decode(p6, 0, q, ob.tables[i:i + 1], ob.lens[i:i + 1], scale,
+                                       cfg.kv_dtype, ks, vs)
+                    elapsed += time.perf_counter() - t0
+                    done_bytes += int(ob.lens[i]) * cfg.kv_heads * cfg.head_dim * 2 * esz
+                    nseq += 1
+                    if elapsed >= budget:
+                        break
+                passes += 1
+            return {"value": round(done_bytes / elapsed / 1e9, 4),
+                    "seqs_per_s": round(nseq / elapsed, 3),
+                    "sample": what(nseq, f"{passes} passes", done_bytes, elapsed)}
+
+        single = None
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                single = run(budget_s / 2)
+        except ImportError:
+            pass
+        del p6, buf
+    finally:
+        os.unlink(tmp.name)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -379,8 +452,8 @@ def cpu_baseline(w: Workload, budget_s: float):
                          "")
     except OSError:
         pass
-    out = {"value": every["value"], "unit": "GB/s", "cores": threads, "kind": "oracle",
-           "sample": every["sample"], "seqs_per_s": every["seqs_per_s"],
+    out = {"value": par["value"], "unit": "GB/s", "cores": n_work, "kind": "oracle",
+           "sample": par["sample"], "seqs_per_s": par["seqs_per_s"],
            "cpu_count": os.cpu_count(), "cpu_model": model}
     if single is not None:
         out["single_thread"] = {"value": single["value"], "unit": "GB/s", "cores": 1,
@@ -612,9 +685,172 @@ def window_rate(ws, window: int, steps: int, stream, fused: bool, full_us: float
             "full_context_us_per_layer": round(full_us, 3)}
 
 
+# The other workloads the default run reports beside the 13B layer:
+# (name, warm-up steps, timed steps).
+OTHER_CONFIGS = (("tiny", 20, 200), ("7b_32layer", 2, 5), ("gqa_prefix", 10, 100),
+                 ("longctx_fp8", 10, 50))
+
+
+def config_summary(name: str, seed: int, warmup: int, steps: int, stream) -> dict:
+    """One workload in its default form, measured as the main line measures
+    the 13B layer: `steps` whole steps back to back over replicas of >= 2 GB in
+    total (wall clock, synchronized on both sides), then the decode call alone
+    (per layer, as the step makes it; the split-K reduce separately), each
+    launched `steps` x layers times back to back between one HIP event pair.
+    The roofline figure is the decode call's unique KV bytes over its time."""
+    import torch
+
+    import workloads as W
+
+    cfg = W.CONFIGS[name]
+    t_build = time.perf_counter()
+    first = Workload(cfg, seed, "cuda", keep_cached_inputs=False)
+    reps = max(1, min(8, math.ceil(2e9 / max(first.cache.nbytes, 1))))
+    ws = [first] + [Workload(cfg, seed + r, "cuda", keep_cached_inputs=False)
+                    for r in range(1, reps)]
+    t_build = time.perf_counter() - t_build
+    kv = sum(w.kv_bytes() for w in ws) / reps
+    uniq = sum(w.kv_unique_bytes() for w in ws) / reps
+    nl = cfg.layers
+    for i in range(warmup):
+        ws[i % reps].step(stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ws[i % reps].step(stream=stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+
+    def per_launch_us(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(steps):
+            for layer in range(nl):
+                fn(ws[i % reps], layer)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (steps * nl) * 1e3
+
+    decode_us = per_launch_us(lambda w, l: w.decode_append(l, stream))
+    reduce_us = (per_launch_us(lambda w, l: w.reduce(stream)) if first.partition_size > 0
+                 else 0.0)
+    per_layer_unique = uniq / nl
+    rate = per_layer_unique / (decode_us * 1e-6) / 1e9
+    out = {
+        "layers": nl, "batch": cfg.batch, "q_heads": cfg.q_heads, "kv_heads": cfg.kv_heads,
+        "head_dim": cfg.head_dim, "kv_dtype": cfg.kv_dtype, "context_lens": list(cfg.lengths),
+        "partition_size": first.partition_size,
+        "single_pass": ("balanced" if first.batch.balanced else "per-sequence")
+        if first.partition_size == 0 else None,
+        "replicas": reps, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(wall * 1e3, 5),
+        "GB/s": round(kv / wall / 1e9, 2), "pct_hbm_peak": round(100 * kv / wall / 1e9 /
+                                                                 HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(cfg.batch / wall, 1),
+        "kv_bytes_per_step": int(kv), "kv_unique_bytes_per_step": int(uniq),
+        "decode_call_us_per_layer": round(decode_us, 3), "reduce_us": round(reduce_us, 3),
+        "roofline": {"bound": "hbm", "kernel": decode_kernel_name(cfg, first),
+                     "achieved": round(rate, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(rate / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(traffic_key(cfg, first)),
+                     "algorithmic_bytes": int(per_layer_unique)},
+        "setup_s": round(t_build, 1),
+    }
+    if cfg.batch <= 8 and kv < 1e7:
+        out["latency_us_per_step"] = round(wall * 1e6, 2)
+    for w in ws:
+        w.cache.close()
+    del ws, first
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def gather_probe(stream, iters: int = 20) -> dict:
+    """The decode's memory access pattern alone (libpkvprobe.so): waves
+    streaming random 4 KiB K tiles and the matching V tiles from two 1 GiB
+    planes, 16-byte non-temporal loads, no arithmetic. The rate the
+    scattered tiles reach is the decode kernels' practical ceiling on this
+    GPU. Staged through a ring of three tiles in registers (the decode's form)
+    or a ring of two or three tiles in LDS filled by direct buffer-to-LDS
+    loads, at several waves per workgroup; each form launched `iters` times
+    back to back between one HIP event pair. Two sizes: 5120 waves x 51 tiles
+    (2.14 GB per launch) and 5120 x 18 (755 MB, the 13B layer's size)."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_450_amd",
+                        "libpkvprobe.so")
+    lib = ctypes.CDLL(path)
+    fn = lib.pkv_probe_gather
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    fn.restype = ctypes.c_int
+    fn.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    num_tiles = 1 << 18  # 1 GiB per plane
+    kp = torch.full((num_tiles * 4096,), 1, dtype=torch.uint8, device="cuda")
+    vpl = torch.full((num_tiles * 4096,), 2, dtype=torch.uint8, device="cuda")
+    num_waves = 5120
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(num_tiles).astype(np.int32)
+
+    def run_ids(run: int, per_wave: int) -> np.ndarray:
+        """Tile k of consecutive waves 0..run-1 of each group of `run` waves
+        are `run` adjacent tiles (a block's adjacent kv heads in the pool):
+        the group's concurrent loads form one run of run x 4 KiB."""
+        groups = num_waves // run
+        starts = rng.permutation(num_tiles // run)[: groups * per_wave].astype(np.int64) * run
+        ids = starts.reshape(groups, per_wave)[:, None, :] + np.arange(run)[None, :, None]
+        return ids.reshape(num_waves, per_wave).astype(np.int32)
+
+    layouts = {"random": perm[: num_waves * 51].copy(), "runs of 4": run_ids(4, 51).ravel(),
+               "runs of 40": run_ids(40, 51).ravel()}
+    sink = torch.zeros(num_waves * 64, dtype=torch.int32, device="cuda")
+    st = stream.cuda_stream
+    out = []
+    for layout, per_wave, forms in (
+            ("random", 51, ((0, 4), (0, 1), (1, 1), (1, 2), (1, 4), (2, 1), (2, 2))),
+            ("random", 18, ((0, 4), (1, 1), (1, 4), (2, 1))),
+            ("runs of 4", 51, ((0, 4), (1, 4))), ("runs of 40", 51, ((0, 4), (1, 4)))):
+        host = layouts[layout]
+        if per_wave != 51:
+            host = host[: num_waves * per_wave]
+        ids = torch.from_numpy(np.ascontiguousarray(host)).cuda()
+        for mode, wpg in forms:
+            def launch():
+                rc = fn(kp.data_ptr(), vpl.data_ptr(), ids.data_ptr(), num_waves, per_wave,
+                        num_tiles, mode, wpg, sink.data_ptr(), st)
+                if rc != 0:
+                    raise RuntimeError(f"pkv_probe_gather: hip error {rc}")
+            for _ in range(3):
+                launch()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(iters):
+                launch()
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / iters * 1e3
+            nbytes = num_waves * per_wave * 8192
+            out.append({"staging": ["registers, 3 tiles", "LDS, 2 tiles", "LDS, 3 tiles"][mode],
+                        "tile_layout": layout,
+                        "waves_per_workgroup": wpg, "tiles_per_wave": per_wave,
+                        "bytes_per_launch": nbytes, "us": round(us, 2),
+                        "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    del kp, vpl, ids, sink
+    torch.cuda.empty_cache()
+    return {"forms": out}
+
+
 def P_workspace_bytes(cfg) -> int:
     import paged_kv_cache_450_amd as P
     return P.paged_attn_workspace_bytes(1, cfg.q_heads, cfg.head_dim, 1, 0)
+
+
+# --shared-prefix choices -> DecodeBatch(shared_prefix=...)
+SHARED_FORMS = {None: None, "kernel": True, "l2": "l2", "auto": "auto"}
 
 
 # ------------------------------------------------------------------ main ----
@@ -662,10 +898,17 @@ def main(argv=None):
     ap.add_argument("--prefix-tokens", type=int, default=0, metavar="N",
                     help="lengthen the shared prompt of a workload with one (gqa_prefix) to N "
                          "tokens; its sharers' contexts grow to at least N + 1")
-    ap.add_argument("--shared-prefix", action="store_true",
-                    help="read blocks that several sequences share once per step "
-                         "(paged_attn_decode_prefix) instead of once per sequence")
+    ap.add_argument("--shared-prefix", nargs="?", const="kernel", default=None,
+                    choices=["kernel", "l2", "auto"],
+                    help="read blocks that several sequences share once per step with the prefix "
+                         "kernel (paged_attn_decode_prefix; the default when given alone), or "
+                         "through the L2 in the balanced pass (l2: paged_attn_decode_prefix_l2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gather-probe", action="store_true",
+                    help="also measure the rate of the decode's access pattern alone (random "
+                         "4 KiB K and V tiles) with register and LDS staging")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the other workloads the default 13B run also reports")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain elementwise copy of this many MiB before warm-up: a "
@@ -696,12 +939,12 @@ def main(argv=None):
     fused = not args.unfused
     first = Workload(cfg, args.seed, "cuda", args.partition_size,
                      keep_cached_inputs=False if args.no_cpu_baseline else "first", fused=fused,
-                     shared_prefix=True if args.shared_prefix else None)
+                     shared_prefix=SHARED_FORMS[args.shared_prefix])
     pool_bytes = first.cache.nbytes
     reps = args.replicas or max(1, min(8, math.ceil(2e9 / max(pool_bytes, 1))))
     ws = [first] + [Workload(cfg, args.seed + r, "cuda", args.partition_size,
                              keep_cached_inputs=False, fused=fused,
-                             shared_prefix=True if args.shared_prefix else None)
+                             shared_prefix=SHARED_FORMS[args.shared_prefix])
                     for r in range(1, reps)]
     kv_bytes = [w.kv_bytes() for w in ws]
     kv_unique = [w.kv_unique_bytes() for w in ws]
@@ -851,6 +1094,19 @@ def main(argv=None):
         result["swap"] = swap_rate(cfg, args.swap, args.steps, stream)
     if args.block_copy > 0:
         result["block_copy"] = block_copy_rate(cfg, args.block_copy, args.steps, stream)
+    if args.gather_probe:
+        result["gather_probe"] = gather_probe(stream)
+    if args.workload == "llama13b_layer" and not args.no_other_configs:
+        # The other workloads, each in its default form (their replicas are
+        # built after the 13B ones are released).
+        keep = first if not args.no_cpu_baseline else None
+        for w in ws:
+            if w is not keep:
+                w.cache.close()
+        ws = None
+        torch.cuda.empty_cache()
+        result["other_configs"] = {name: config_summary(name, args.seed, wu, st, stream)
+                                   for name, wu, st in OTHER_CONFIGS}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -313,6 +313,10 @@ pkv_status kv_cache_append(const pkv_pool* pool, int32_t layer, const void* k, c
                            const float* k_scale, const float* v_scale, hipStream_t stream);
 
 /* Bytes of workspace paged_attn_decode needs.
+ * Source: none on the pages. Cutting a long context into partitions whose
+ * partials are merged afterwards (split-K) is this library's long-context
+ * form, chosen for one GPU's many compute units; the pages only name the
+ * long-context pressure ([P2] third pitfall).
  * partition_size > 0: per (sequence, query head, partition) an fp32 max, an
  *   fp32 sum and head_dim fp32 outputs, with ceil(max_context_len /
  *   partition_size) partitions per sequence, laid out as described below
@@ -497,6 +501,34 @@ pkv_status paged_attn_decode_prefix(const pkv_pool* pool, int32_t layer, const v
                                     int32_t max_group_size, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream);
 
+/* Decode step with shared-prefix reads through the L2: the same result as
+ * paged_attn_decode_append (new_k / new_v given) or paged_attn_decode (both
+ * NULL) in the balanced single pass on a 16-bit cache ([P2]
+ * "PagedAttention：...": sequences that share a prompt map the same physical
+ * blocks). The balanced pass reads every sequence's whole context as usual,
+ * but the first seq_prefix_blocks[i] blocks of sequence i, which other
+ * sequences of the batch share, are loaded with the caching policy (all other
+ * KV loads stream through the caches), so the sharers' repeated reads of a
+ * block can be served by the L2 instead of HBM. No extra kernel and no extra
+ * partials: the lighter form for short shared prompts, where the prefix
+ * kernel of paged_attn_decode_prefix costs more than it saves.
+ * seq_prefix_blocks: device int32 [num_seqs], as paged_attn_prefix_plan
+ *   writes it (0 for a sequence that shares nothing); only a load policy
+ *   depends on it, so any values give the same output. NULL: the plain
+ *   balanced pass.
+ * workspace: as paged_attn_decode's balanced pass (at least
+ *   paged_attn_workspace_bytes(..., 0) bytes, 256-byte aligned).
+ * Errors: INVALID (an FP8 cache, num_seqs > 4096, a NULL workspace, and every
+ *   error of paged_attn_decode_append), HIP. */
+pkv_status paged_attn_decode_prefix_l2(const pkv_pool* pool, int32_t layer, const void* new_k,
+                                       const void* new_v, int32_t src_dtype, const void* q,
+                                       int32_t q_dtype, void* out, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                       int32_t num_seqs, int32_t num_q_heads, float scale,
+                                       int32_t max_context_len, const int32_t* seq_prefix_blocks,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
 /* Bytes of the library's static device scratch, one copy per GPU, that
  * paged_attn_decode_append_noalloc uses as its workspace. */
 #define PKV_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
@@ -536,7 +568,9 @@ pkv_status paged_attn_decode_append_noalloc(const pkv_pool* pool, int32_t layer,
                                             hipStream_t stream);
 
 /* Merge the partitions a partitioned paged_attn_decode left in workspace
- * into out (device [num_seqs][num_q_heads][head_dim] of out_dtype F16 or BF16):
+ * into out (device [num_seqs][num_q_heads][head_dim] of out_dtype F16 or BF16).
+ * Source: none on the pages; the exact log-sum-exp merge of this library's
+ * split-K form (see paged_attn_workspace_bytes):
  *   M = max_p m_p, w_p = l_p exp(m_p - M), out = sum_p w_p o_p / sum_p w_p
  * over p < ceil(L_i / partition_size) (L_i clamped to max_context_len);
  * a sequence with no tokens gets zeros.

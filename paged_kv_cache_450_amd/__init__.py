@@ -23,7 +23,8 @@ __all__ = [
     "kv_seq_fork", "kv_seq_extend", "kv_cache_append", "paged_attn_workspace_bytes",
     "paged_attn_decode", "paged_attn_reduce", "pkv_last_error", "library_path", "lib",
     "PrefixPlan", "paged_attn_prefix_plan", "paged_attn_prefix_workspace_bytes",
-    "paged_attn_decode_prefix", "paged_attn_decode_append_noalloc", "STATIC_SCRATCH_BYTES",
+    "paged_attn_decode_prefix", "paged_attn_decode_prefix_l2", "paged_attn_decode_append_noalloc",
+    "STATIC_SCRATCH_BYTES",
 ]
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_STATE, PKV_ERR_HIP = 0, -1, -2, -3, -4
@@ -99,6 +100,8 @@ def _load():
                                     i32, i32, vp, sz, vp]),
         "paged_attn_decode_append": (i32, [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, i32,
                                            i32, f32, vp, vp, i32, i32, vp, sz, vp]),
+        "paged_attn_decode_prefix_l2": (i32, [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp,
+                                              i32, i32, f32, i32, vp, vp, sz, vp]),
         "paged_attn_decode_append_noalloc": (i32, [vp, i32, vp, vp, i32, vp, i32, vp, vp, i32,
                                                    vp, i32, i32, f32, vp, vp, i32, i32, vp]),
         "paged_attn_reduce": (i32, [vp, vp, i32, vp, i32, i32, i32, i32, i32, vp]),
@@ -549,6 +552,33 @@ def paged_attn_prefix_plan(block_tables, context_lens, max_context_len: int,
 
 def paged_attn_prefix_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int) -> int:
     return int(lib.paged_attn_prefix_workspace_bytes(num_seqs, num_q_heads, head_dim))
+
+
+def paged_attn_decode_prefix_l2(pool, layer: int, q, out, block_tables, context_lens,
+                                scale: float, max_context_len: int, seq_prefix_blocks, workspace,
+                                new_k=None, new_v=None, stream=None) -> None:
+    """Decode (with new_k / new_v: the fused step) in the balanced pass,
+    loading each sequence's shared leading blocks (seq_prefix_blocks, a device
+    int32 tensor, or None) with the caching policy so that repeats can hit L2."""
+    torch = _torch()
+    _dev(q, "q"); _dev(out, "out"); _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32); _dev(workspace, "workspace")
+    _dev(new_k, "new_k"); _dev(new_v, "new_v")
+    _dev(seq_prefix_blocks, "seq_prefix_blocks", torch.int32)
+    if q.dim() != 3 or block_tables.dim() != 2:
+        raise ValueError("q must be [B, Hq, D] and block_tables [B, W]")
+    if out is None or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if new_k is not None and (new_v is None or new_k.shape != new_v.shape or new_k.dim() != 3 or
+                              new_k.shape[0] != q.shape[0] or new_k.shape[2] != q.shape[2]):
+        raise ValueError("new_k and new_v must be [B, Hkv, D] like q")
+    src = _dtype_code(new_k) if new_k is not None else _dtype_code(q)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.paged_attn_decode_prefix_l2(
+        pool, layer, _ptr(new_k), _ptr(new_v), src, _ptr(q), _dtype_code(q), _ptr(out),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), q.shape[0], q.shape[1],
+        float(scale), max_context_len, _ptr(seq_prefix_blocks), _ptr(workspace), ws_bytes,
+        _stream(stream)))
 
 
 def paged_attn_decode_prefix(pool, layer: int, q, out, block_tables, context_lens, scale: float,

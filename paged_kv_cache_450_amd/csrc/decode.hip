@@ -161,20 +161,22 @@ size_t balanced_bytes(size_t group, size_t head_dim, size_t waves) {
     return waves * 2 * group * (head_dim + 4) * sizeof(float);
 }
 
-template <class M, int KV, int D, int NBUF, bool kPre>
+template <class M, int KV, int D, int NBUF, bool kPre, bool kKeep>
 hipError_t launch_balanced_as(DecodeParams prm, int cus, hipStream_t st) {
     static int wgs_per_cu = -1;  // per kernel instance; the same on every gfx950 device
     if (wgs_per_cu < 0) {
         int nb = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &nb, reinterpret_cast<const void*>(&decode_balanced_kernel<M, KV, D, NBUF, kPre>),
+                &nb,
+                reinterpret_cast<const void*>(
+                    &decode_balanced_kernel<M, KV, D, NBUF, kPre, kKeep>),
                 256, 0) != hipSuccess)
             return hipGetLastError();
         wgs_per_cu = std::max(1, std::min(nb, kBalancedWavesPerCu / 4));
     }
     prm.num_waves = cus * wgs_per_cu * 4;
-    hipLaunchKernelGGL((decode_balanced_kernel<M, KV, D, NBUF, kPre>), dim3(prm.num_waves / 4),
-                       dim3(256), 0, st, prm);
+    hipLaunchKernelGGL((decode_balanced_kernel<M, KV, D, NBUF, kPre, kKeep>),
+                       dim3(prm.num_waves / 4), dim3(256), 0, st, prm);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((balanced_merge_kernel<KV, D, M::kG>),
@@ -188,8 +190,11 @@ hipError_t launch_balanced_as(DecodeParams prm, int cus, hipStream_t st) {
 // capped at kBalancedWavesPerCu (the width the workspace is sized for).
 template <class M, int KV, int D, int NBUF>
 hipError_t launch_balanced(const DecodeParams& prm, int cus, hipStream_t st) {
-    if (prm.pre_blocks != nullptr) return launch_balanced_as<M, KV, D, NBUF, true>(prm, cus, st);
-    return launch_balanced_as<M, KV, D, NBUF, false>(prm, cus, st);
+    if (prm.pre_blocks != nullptr)
+        return launch_balanced_as<M, KV, D, NBUF, true, false>(prm, cus, st);
+    if (prm.keep_blocks != nullptr)
+        return launch_balanced_as<M, KV, D, NBUF, false, true>(prm, cus, st);
+    return launch_balanced_as<M, KV, D, NBUF, false, false>(prm, cus, st);
 }
 
 // Ring depths keep two waves per SIMD (MFMA at D = 128 holds its O^T
@@ -230,7 +235,9 @@ PrefixLayout prefix_layout(size_t num_seqs, size_t num_q_heads, size_t head_dim)
     return l;
 }
 
-// The groups of a shared-prefix decode (paged_attn_decode_prefix).
+// The groups of a shared-prefix decode (paged_attn_decode_prefix), or, with
+// via_l2, only each sequence's shared leading blocks
+// (paged_attn_decode_prefix_l2).
 struct PrefixArgs {
     const int32_t* seq_prefix_blocks;
     const int32_t* group_offsets;
@@ -238,6 +245,7 @@ struct PrefixArgs {
     const int32_t* group_blocks;
     int32_t num_groups;
     int32_t max_group_size;
+    bool via_l2;
 };
 
 }  // namespace
@@ -362,7 +370,8 @@ pkv_status decode_impl(const char* fn, const pkv_pool* pool, int32_t layer, cons
             const int cus = device_cu_count();
             const int waves = cus * kBalancedWavesPerCu;
             const PrefixLayout pl = prefix_layout(num_seqs, num_q_heads, d.head_dim);
-            const size_t need = pfx != nullptr ? pl.total : balanced_bytes(G, d.head_dim, waves);
+            const bool kernel_pass = pfx != nullptr && !pfx->via_l2;
+            const size_t need = kernel_pass ? pl.total : balanced_bytes(G, d.head_dim, waves);
             if (workspace_bytes < need)
                 return fail(PKV_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn,
                             workspace_bytes, need);
@@ -370,7 +379,8 @@ pkv_status decode_impl(const char* fn, const pkv_pool* pool, int32_t layer, cons
                 return fail(PKV_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
             prm.slots = static_cast<float*>(workspace);
             prm.num_seqs = num_seqs;
-            const bool with_pre = pfx != nullptr && pfx->num_groups > 0;
+            const bool with_pre = kernel_pass && pfx->num_groups > 0;
+            if (pfx != nullptr && pfx->via_l2) prm.keep_blocks = pfx->seq_prefix_blocks;
             if (with_pre) {
                 uint8_t* ws = static_cast<uint8_t*>(workspace);
                 prm.pre_blocks = pfx->seq_prefix_blocks;
@@ -544,11 +554,42 @@ extern "C" pkv_status paged_attn_decode_prefix(
     if (workspace == nullptr && num_seqs > 0)
         return fail(PKV_ERR_INVALID, "%s: workspace is NULL", fn);
     const PrefixArgs pfx{seq_prefix_blocks, group_offsets, group_members, group_blocks,
-                         num_groups, max_group_size};
+                         num_groups, max_group_size, false};
     return decode_impl(fn, pool, layer, q, q_dtype, out, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_q_heads, scale, nullptr, nullptr,
                        max_context_len, 0, workspace, workspace_bytes, new_k, new_v, 0, stream,
                        &pfx);
+}
+
+extern "C" pkv_status paged_attn_decode_prefix_l2(
+    const pkv_pool* pool, int32_t layer, const void* new_k, const void* new_v, int32_t src_dtype,
+    const void* q, int32_t q_dtype, void* out, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, float scale, int32_t max_context_len, const int32_t* seq_prefix_blocks,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    using pkv::fail;
+    const char* fn = "paged_attn_decode_prefix_l2";
+    if ((new_k == nullptr) != (new_v == nullptr))
+        return fail(PKV_ERR_INVALID, "%s: new_k and new_v must both be given or both be NULL", fn);
+    if (new_k != nullptr) {
+        if (src_dtype != q_dtype)
+            return fail(PKV_ERR_INVALID, "%s: the new tokens' dtype must equal the q dtype", fn);
+        if ((reinterpret_cast<uintptr_t>(new_k) | reinterpret_cast<uintptr_t>(new_v)) % 16 != 0)
+            return fail(PKV_ERR_INVALID, "%s: new_k and new_v must be 16-byte aligned", fn);
+    }
+    if (pool == nullptr) return fail(PKV_ERR_INVALID, "%s: pool is NULL", fn);
+    if (!pkv::is_16bit(pool->desc.kv_dtype))
+        return fail(PKV_ERR_INVALID, "%s: needs a 16-bit cache", fn);
+    if (num_seqs < 0 || num_seqs > kBalancedMaxSeqs)
+        return fail(PKV_ERR_INVALID, "%s: num_seqs %d outside [0, %d]", fn, num_seqs,
+                    kBalancedMaxSeqs);
+    if (workspace == nullptr && num_seqs > 0)
+        return fail(PKV_ERR_INVALID, "%s: workspace is NULL", fn);
+    const PrefixArgs pfx{seq_prefix_blocks, nullptr, nullptr, nullptr, 0, 0, true};
+    return decode_impl(fn, pool, layer, q, q_dtype, out, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_q_heads, scale, nullptr, nullptr,
+                       max_context_len, 0, workspace, workspace_bytes, new_k, new_v, 0, stream,
+                       seq_prefix_blocks != nullptr ? &pfx : nullptr);
 }
 
 // ---------------------------------------------------------------------------

@@ -49,6 +49,8 @@ struct TileWalk {
     int chunk;           // sequences 64*chunk .. +63 have their lengths in lens
     int lens;            // per lane: tokens of sequence 64*chunk + lane
     int pres;            // per lane: its leading blocks covered by the prefix pass
+    int keeps;           // per lane: its leading shared blocks read through the L2
+    int keep;            // sequence s: blocks below this are read with the caching policy
     int rbase;           // jlo rounded down to 64: row0_* start there
     int row0_a, row0_b;  // ids of blocks rbase .. +63 and +64 .. +127 of row s (per lane)
     int ids_a, ids_b;    // ids of blocks base .. base+127 (per lane, two chunks)
@@ -88,8 +90,9 @@ __device__ __forceinline__ int walk_id(const DecodeParams& p, TileWalk& t, int l
     return __builtin_amdgcn_readlane(t.ids_a, t.j - t.base);
 }
 
-// Step to the next tile. kPre: sequences may begin after shared-prefix blocks.
-template <bool kPre>
+// Step to the next tile. kPre: sequences may begin after shared-prefix blocks;
+// kKeep: sequences have leading shared blocks read through the L2.
+template <bool kPre, bool kKeep>
 __device__ __forceinline__ void walk_advance(const DecodeParams& p, TileWalk& t, int lane) {
     if (++t.j < t.nblk) return;
     t.j = t.jlo;
@@ -111,9 +114,11 @@ __device__ __forceinline__ void walk_advance(const DecodeParams& p, TileWalk& t,
             const int jj = t.chunk * 64 + lane;
             t.lens = jj < p.num_seqs ? seq_tokens(p, jj) : 0;
             t.pres = kPre && jj < p.num_seqs ? pre_of(p, jj) : 0;
+            if constexpr (kKeep) t.keeps = jj < p.num_seqs ? keep_of(p, jj) : 0;
         }
         walk_set_seq(p, t, __builtin_amdgcn_readlane(t.lens, t.s & 63),
                      __builtin_amdgcn_readlane(t.pres, t.s & 63));
+        if constexpr (kKeep) t.keep = __builtin_amdgcn_readlane(t.keeps, t.s & 63);
     } while (t.jlo >= t.nblk && t.s + 1 < p.num_seqs);
     t.j = t.jlo;
     walk_enter_row(p, t, lane);
@@ -152,7 +157,16 @@ struct ValuMath {
         load_q<KV, KV, D>(q, qrow, lane % kLpt);
     }
     __device__ static void fetch_q_lds(const DecodeParams&, State&, int, int, int) {}
-    __device__ static void issue(TileT& t, const TileRef& r, int lane) {
+    // kept: the tile is shared with other sequences of the batch; load it with
+    // the caching policy so that their reads of it can hit the L2.
+    __device__ static void issue(TileT& t, const TileRef& r, int lane, bool kept = false) {
+        if (kept) {
+#pragma unroll
+            for (int i = 0; i < kNld; ++i) t.k[i] = rsrc_load16_kept(r.k, lane * 16 + i * 1024);
+#pragma unroll
+            for (int i = 0; i < kNld; ++i) t.v[i] = rsrc_load16_kept(r.v, lane * 16 + i * 1024);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < kNld; ++i) t.k[i] = rsrc_load16(r.k, lane * 16 + i * 1024);
 #pragma unroll
@@ -253,8 +267,15 @@ struct MfmaMath {
             *reinterpret_cast<uint4*>(x.qlds + c * 1024 + lane * 16) =
                 hl < G ? v[c] : make_uint4(0u, 0u, 0u, 0u);
     }
-    __device__ static void issue(TileT& t, const TileRef& r, int lane) {
+    __device__ static void issue(TileT& t, const TileRef& r, int lane, bool kept = false) {
         const int koff = (lane & 15) * Gm::kRowBytes + 16 * (lane >> 4);
+        if (kept) {  // shared with other sequences: the caching policy (see ValuMath)
+#pragma unroll
+            for (int c = 0; c < kNk; ++c) t.k[c] = rsrc_load16_kept(r.k, koff + 64 * c);
+#pragma unroll
+            for (int i = 0; i < kNv; ++i) t.v[i] = rsrc_load16_kept(r.v, lane * 16 + 1024 * i);
+            return;
+        }
 #pragma unroll
         for (int c = 0; c < kNk; ++c) t.k[c] = rsrc_load16(r.k, koff + 64 * c);
 #pragma unroll
@@ -307,8 +328,11 @@ struct MfmaMath {
 // kPre: a shared-prefix pass covered the leading blocks of some sequences
 // (pre_blocks); without it that bookkeeping is compiled out, so its registers
 // cost the other forms nothing.
-template <class M, int KV, int D, int NBUF, bool kPre = false>
-__global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams p) {
+// kKeep: some sequences begin with blocks that others of the batch share
+// (keep_blocks); those are loaded with the caching policy.
+template <class M, int KV, int D, int NBUF, bool kPre = false, bool kKeep = false>
+__global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodeParams p) {
+    static_assert(!(kPre && kKeep), "one shared-prefix form at a time");
     constexpr int G = M::kG;
     constexpr int SS = SlotGeoB<D>::kStride;
     const int lane = threadIdx.x & 63;
@@ -352,6 +376,10 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
                 tw.pres = pre;
                 walk_set_seq(p, tw, __builtin_amdgcn_readlane(len, ln),
                              __builtin_amdgcn_readlane(pre, ln));
+                if constexpr (kKeep) {
+                    tw.keeps = jj < p.num_seqs ? keep_of(p, jj) : 0;
+                    tw.keep = __builtin_amdgcn_readlane(tw.keeps, ln);
+                }
                 const int nt = tw.nblk - tw.jlo;  // tiles per head
                 const int64_t a_s = carry + __builtin_amdgcn_readlane(incl - tiles, ln);
                 const int64_t off = t0 - a_s;
@@ -393,7 +421,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
             M::issue(tt, r, lane);
             return;
         }
-        if (kn > 0) walk_advance<kPre>(p, tw, lane);
+        if (kn > 0) walk_advance<kPre, kKeep>(p, tw, lane);
         const bool first = kn == 0 || tw.j == tw.jlo;
         const bool last = kn == n - 1 || tw.j == tw.nblk - 1;
         info.flags = (first ? 1 : 0) | (last ? 2 : 0) | (kPre && tw.has_pre ? 4 : 0);
@@ -410,7 +438,7 @@ __global__ __launch_bounds__(256) void decode_balanced_kernel(const DecodeParams
                                    tw.L, tw.lo);
         info.nvalid = r.nvalid;
         info.nlo = r.nlo;
-        M::issue(tt, r, lane);
+        M::issue(tt, r, lane, kKeep && tw.j < tw.keep);
     };
 
 #pragma unroll

@@ -57,7 +57,17 @@ struct DecodeParams {
     const int32_t* group_blocks;   // [num_groups] shared leading blocks of each group
     int32_t num_groups;
     int32_t pre_slots;             // prefix workgroups per (group, kv head)
+    // Shared leading blocks read through the L2 (keep_blocks NULL: none): the
+    // balanced pass reads the first keep_blocks[s] blocks of sequence s, which
+    // other sequences of the batch share, with the caching load policy, so
+    // that the sharers' repeated reads can hit the L2 instead of HBM.
+    const int32_t* keep_blocks;    // [B]
 };
+
+// Leading blocks of sequence j to read with the caching policy (0 without a hint).
+__device__ __forceinline__ int keep_of(const DecodeParams& p, int j) {
+    return p.keep_blocks != nullptr ? max(p.keep_blocks[j], 0) : 0;
+}
 
 // First token a sequence of L tokens attends over (sliding window).
 __device__ __forceinline__ int window_lo(const DecodeParams& p, int L) {

@@ -25,7 +25,7 @@ from . import (BLOCK_SIZE, PKV_BF16, PKV_ERR_OOM, PKV_F16, PKV_FP8_E4M3, PkvErro
                kv_seq_extend, kv_seq_extend_cow, kv_seq_fork, kv_seq_trim, kv_swap_in, kv_swap_out,
                kv_swap_slot_bytes,
                paged_attn_decode, paged_attn_decode_append, paged_attn_decode_prefix,
-               paged_attn_decode_window, paged_attn_prefix_plan,
+               paged_attn_decode_prefix_l2, paged_attn_decode_window, paged_attn_prefix_plan,
                paged_attn_prefix_workspace_bytes, paged_attn_reduce,
                paged_attn_workspace_bytes)
 
@@ -118,12 +118,15 @@ class PagedKVCache:
 
 
 # Repeated K/V reads per layer a shared-prefix plan must save before
-# shared_prefix="auto" takes paged_attn_decode_prefix. Measured on MI355X (64
-# sharers, 64 / 8 heads x 128, bf16): 132 MB saved (512 shared tokens) cost 3%
-# per call, 264 MB (1024) gained 6%. The prefix kernel costs about 10 us per
-# call whatever it reads, and the plain pass's repeated reads of a shared block
-# mostly hit the 256 MB last-level cache, so they cost less than their bytes.
-PREFIX_AUTO_BYTES = 200_000_000
+# shared_prefix="auto" takes the prefix kernel (paged_attn_decode_prefix);
+# below it, the shared blocks are read through the L2 by the balanced pass
+# (paged_attn_decode_prefix_l2). Measured on MI355X (64 sharers, 64 / 8 heads
+# x 128, bf16, per call): 132 MB repeated (512 shared tokens): plain pass
+# 157.0 us, L2 form 150.0 us, prefix kernel 160.9 us; 264 MB (1024): 163.6,
+# 153.7, 153.4 us; 528 MB (2048): L2 form 162.9, prefix kernel 143.8 us. The
+# prefix kernel costs about 10 us per call whatever it reads; the L2 form costs
+# nothing extra but its repeats still cross the fabric when they miss the L2.
+PREFIX_AUTO_BYTES = 250_000_000
 
 
 def prefix_repeated_bytes(plan, desc) -> int:
@@ -140,12 +143,25 @@ def prefix_repeated_bytes(plan, desc) -> int:
 def plan_shared_prefix(tables, lens, max_context_len: int, desc, mode, min_blocks: int = 1):
     """The host plan for paged_attn_decode_prefix, or None when there is
     nothing to share or mode is "auto" and the plan saves too little."""
+    plan, form = shared_prefix_form(tables, lens, max_context_len, desc, mode, min_blocks)
+    return plan if form == "kernel" or (mode is True and plan is not None) else None
+
+
+def shared_prefix_form(tables, lens, max_context_len: int, desc, mode, min_blocks: int = 1):
+    """(plan, form) for a batch: form "kernel" (paged_attn_decode_prefix),
+    "l2" (paged_attn_decode_prefix_l2: the plan's seq_prefix_blocks only) or
+    None (nothing shared: the plain pass). mode True: the prefix kernel
+    whenever groups exist; "l2": the L2 form whenever they do; "auto": the
+    prefix kernel when it saves at least PREFIX_AUTO_BYTES of repeated reads
+    per layer, else the L2 form."""
     plan = paged_attn_prefix_plan(tables, lens, max_context_len, min_blocks)
     if plan.num_groups == 0:
-        return plan if mode is True else None
-    if mode == "auto" and prefix_repeated_bytes(plan, desc) < PREFIX_AUTO_BYTES:
-        return None
-    return plan
+        return plan, None
+    if mode is True:
+        return plan, "kernel"
+    if mode == "l2":
+        return plan, "l2"
+    return plan, ("kernel" if prefix_repeated_bytes(plan, desc) >= PREFIX_AUTO_BYTES else "l2")
 
 
 def plan_to_device(plan, device):
@@ -207,12 +223,21 @@ class DecodeBatch:
         # (sequence, kv head).
         self.balanced = partition_size == 0 and balanced and ws > 0
         self.plan = None
+        # shared_prefix="l2": the shared leading blocks are read by the
+        # balanced pass itself, through the L2 (paged_attn_decode_prefix_l2);
+        # l2_blocks holds each sequence's count on the device.
+        self.l2_blocks = None
         if shared_prefix:
             if not self.balanced or window > 0 or cache.desc.kv_dtype == PKV_FP8_E4M3:
                 raise ValueError("shared_prefix needs the balanced single pass on a 16-bit "
                                  "cache, without a window")
-            self.plan = plan_shared_prefix(tables, lens, self.max_context_len, cache.desc,
-                                           shared_prefix, min_prefix_blocks)
+            pl, form = shared_prefix_form(tables, lens, self.max_context_len, cache.desc,
+                                          shared_prefix, min_prefix_blocks)
+            if form == "l2":
+                self.l2_blocks = torch.from_numpy(
+                    np.ascontiguousarray(pl.seq_prefix_blocks, dtype=np.int32)).to(device)
+            elif form == "kernel" or shared_prefix is True:
+                self.plan = pl
         if self.plan is not None:
             ws = paged_attn_prefix_workspace_bytes(self.num_seqs, num_q_heads, self.head_dim)
             self.plan_dev = plan_to_device(self.plan, device)
@@ -237,6 +262,11 @@ class DecodeBatch:
         if self.plan is not None and self.window == 0:
             self._decode_prefix(layer, q, None, None, stream)
             return
+        if self.l2_blocks is not None and self.window == 0:
+            paged_attn_decode_prefix_l2(self.cache.handle, layer, q, self.out, self.tables,
+                                        self.lens, self.scale, self.max_context_len,
+                                        self.l2_blocks, self.workspace, stream=stream)
+            return
         if self.window > 0:
             paged_attn_decode_window(self.cache.handle, layer, q,
                                      None if self.partition_size else self.out, self.tables,
@@ -256,6 +286,11 @@ class DecodeBatch:
             raise ValueError(f"new_k and new_v must be {want}")
         if self.plan is not None and self.window == 0:
             self._decode_prefix(layer, q, new_k, new_v, stream)
+            return
+        if self.l2_blocks is not None and self.window == 0:
+            paged_attn_decode_prefix_l2(self.cache.handle, layer, q, self.out, self.tables,
+                                        self.lens, self.scale, self.max_context_len,
+                                        self.l2_blocks, self.workspace, new_k, new_v, stream)
             return
         if self.window > 0:
             paged_attn_decode_window(self.cache.handle, layer, q,
@@ -431,6 +466,7 @@ class ContinuousBatcher:
         self.running = []
         self.iteration = 0
         self.prefix_groups_run = 0  # groups read once by paged_attn_decode_prefix, summed
+        self.prefix_l2_groups_run = 0  # groups whose shared blocks went through the L2 form
         self._specs = {}
 
     def submit(self, spec) -> None:
@@ -576,13 +612,17 @@ class ContinuousBatcher:
         lens = torch.from_numpy(plan.lens).to(dev)
         sc = (1.0 / math.sqrt(desc.head_dim)) if scale is None else scale
         max_ctx = int(plan.lens.max())
-        pre = None
+        pre = l2 = None
         if (shared_prefix and workspace is not None and self.window == 0
                 and desc.kv_dtype != PKV_FP8_E4M3):
-            pp = plan_shared_prefix(plan.tables, plan.lens, max_ctx, desc, shared_prefix)
-            if pp is not None and pp.num_groups > 0:
+            pp, form = shared_prefix_form(plan.tables, plan.lens, max_ctx, desc, shared_prefix)
+            if form == "kernel":
                 pre = (pp, plan_to_device(pp, dev))
                 self.prefix_groups_run += pp.num_groups
+            elif form == "l2":
+                l2 = torch.from_numpy(np.ascontiguousarray(pp.seq_prefix_blocks,
+                                                           dtype=np.int32)).to(dev)
+                self.prefix_l2_groups_run += pp.num_groups
         for layer in range(desc.num_layers):
             q, kn, vn = step_inputs(layer, len(plan.batch))
             out = torch.empty((len(plan.batch), num_q_heads, desc.head_dim), dtype=q.dtype,
@@ -595,6 +635,9 @@ class ContinuousBatcher:
                 paged_attn_decode_prefix(h, layer, q, out, tables, lens, sc, max_ctx, spb, offs,
                                          mem, blk, pp.num_groups, pp.max_group_size, workspace,
                                          kn, vn, stream)
+            elif l2 is not None:
+                paged_attn_decode_prefix_l2(h, layer, q, out, tables, lens, sc, max_ctx, l2,
+                                            workspace, kn, vn, stream)
             else:
                 paged_attn_decode_append(h, layer, kn, vn, q, out, tables, lens, sc, max_ctx, 0,
                                          workspace, k_scale, v_scale, stream)

@@ -57,11 +57,15 @@ def test_continuous_batching_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching
 # The loop with the shared-prefix pass on its balanced iterations: forked
 # samples share every full prompt block, and with prefix caching requests of
 # one group share a 48-token system prompt.
+# mode True: the prefix kernel; "l2": the shared blocks read through the L2 by
+# the balanced pass.
+@pytest.mark.parametrize("mode", [True, "l2"])
 @pytest.mark.parametrize("dt,hq,hkv,dim,num_blocks,max_gen,caching", [
     ("bf16", 8, 2, 128, 40, 12, True), ("f16", 2, 2, 64, 20, 12, True),
     ("f16", 4, 4, 128, 48, 12, False)])
-def test_continuous_batching_loop_shared_prefix(dt, hq, hkv, dim, num_blocks, max_gen, caching):
-    run_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching, 0, 0, shared_prefix=True)
+def test_continuous_batching_loop_shared_prefix(dt, hq, hkv, dim, num_blocks, max_gen, caching,
+                                                mode):
+    run_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching, 0, 0, shared_prefix=mode)
 
 
 def run_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching, swap_slots, window,
@@ -165,8 +169,8 @@ def run_loop(dt, hq, hkv, dim, num_blocks, max_gen, caching, swap_slots, window,
     if window:
         assert trimmed > 0
     if shared_prefix:
-        assert prod.prefix_groups_run > 0
+        assert (prod.prefix_l2_groups_run if shared_prefix == "l2" else prod.prefix_groups_run) > 0
     say(f"{name}: {steps} steps, {copies} copies, {preempted} preemptions, {swapped} swaps, "
         f"{reused} cached blocks, {trimmed} blocks released by the window, "
-        f"{prod.prefix_groups_run} prefix groups")
+        f"{prod.prefix_groups_run} prefix groups, {prod.prefix_l2_groups_run} through the L2")
     cache.close()

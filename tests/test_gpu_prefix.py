@@ -43,19 +43,27 @@ SHAPES = [(16, 2, 128, "bf16"), (4, 4, 64, "f16"), (8, 4, 128, "f16"), (16, 4, 6
           (6, 6, 128, "bf16")]
 
 
+@pytest.mark.parametrize("form", [True, "l2"])
 @pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("hq,hkv,dim,dt", SHAPES)
-def test_shared_prompt_workload(hq, hkv, dim, dt, fused):
+def test_shared_prompt_workload(hq, hkv, dim, dt, fused, form):
     """The GQA + shared-prefix workload scaled down (the even sequences fork one
-    512-token prompt), at several head shapes: whole pool bytewise after the
-    appends, every output against the oracle."""
+    512-token prompt), at several head shapes, with the prefix kernel (form
+    True) or with the shared blocks read through the L2 by the balanced pass
+    (form "l2"): whole pool bytewise after the appends, every output against
+    the oracle."""
     cfg = replace(W.scaled("gqa_prefix"), name=f"gqa_prefix_small_{hq}_{hkv}_{dim}_{dt}",
                   q_heads=hq, kv_heads=hkv, head_dim=dim, kv_dtype=dt, q_dtype=dt)
-    say(f"prefix workload Hq={hq} Hkv={hkv} D={dim} {dt} fused={fused}")
-    side = H.build_product(cfg, seed=0, fused=fused, shared_prefix=True)
+    say(f"prefix workload Hq={hq} Hkv={hkv} D={dim} {dt} fused={fused} form={form}")
+    side = H.build_product(cfg, seed=0, fused=fused, shared_prefix=form)
     torch.cuda.synchronize()
-    plan = side.batch.plan
-    assert plan is not None and plan.groups() == [(W.sharers(cfg), 32)]
+    if form == "l2":
+        assert side.batch.plan is None and side.batch.l2_blocks is not None
+        spb = side.batch.l2_blocks.cpu().numpy()
+        assert np.array_equal(np.flatnonzero(spb), W.sharers(cfg)) and set(spb[spb > 0]) == {32}
+    else:
+        plan = side.batch.plan
+        assert plan is not None and plan.groups() == [(W.sharers(cfg), 32)]
     o = H.oracle_bookkeeping(cfg, 0)
     check_bookkeeping(side, o)
     check_layers(cfg, side, o, list(range(cfg.batch)), range(cfg.layers), whole_pool=True)
@@ -196,16 +204,33 @@ def test_full_size_workload_sampled():
     check_layers(cfg, side, o, seqs, range(cfg.layers), whole_pool=False)
 
 
+def test_full_size_workload_l2_sampled():
+    """The full-size GQA + shared-prefix workload with its shared blocks read
+    through the L2 by the balanced pass (paged_attn_decode_prefix_l2), as
+    `bench.py --workload gqa_prefix --shared-prefix l2` launches it; sampled
+    sequences against the oracle, sharers included."""
+    cfg = W.CONFIGS["gqa_prefix"]
+    say("prefix l2 full size gqa_prefix")
+    side = H.build_product(cfg, seed=0, fused=True, shared_prefix="l2")
+    torch.cuda.synchronize()
+    assert side.batch.l2_blocks is not None
+    o = H.oracle_bookkeeping(cfg, 0)
+    seqs = sorted(set(H.sample_sequences(cfg, side, 8)) | {0, 2, 3, 126})
+    check_layers(cfg, side, o, seqs, range(cfg.layers), whole_pool=False)
+
+
 @pytest.mark.parametrize("prompt,expect_pass", [(512, False), (2048, True)])
 def test_auto_picks_the_pass_and_matches(prompt, expect_pass):
     """shared_prefix="auto" on the full-size GQA batch: the 512-token shared
-    prompt saves too little and runs the plain pass, a 2048-token one runs the
-    prefix pass; either way sampled outputs match the oracle."""
+    prompt saves too little for the prefix kernel and is read through the L2
+    by the balanced pass, a 2048-token one runs the prefix kernel; either way
+    sampled outputs match the oracle."""
     cfg = replace(W.CONFIGS["gqa_prefix"], share_prefix_tokens=prompt)
     say(f"prefix auto prompt={prompt}")
     side = H.build_product(cfg, seed=0, fused=True, shared_prefix="auto")
     torch.cuda.synchronize()
     assert (side.batch.plan is not None) == expect_pass
+    assert (side.batch.l2_blocks is not None) == (not expect_pass)
     o = H.oracle_bookkeeping(cfg, 0)
     seqs = sorted(set(H.sample_sequences(cfg, side, 6)) | {0, 2, 3})
     check_layers(cfg, side, o, seqs, range(cfg.layers), whole_pool=False)

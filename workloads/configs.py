@@ -19,7 +19,7 @@ class Config:
     share_prefix_tokens: int = 0        # > 0: even-indexed sequences share this many tokens
     partition_size: int = 0             # default split-K partition (0: one pass)
     balanced: bool = True               # single pass: balanced over waves (else per sequence)
-    shared_prefix: bool = False         # read blocks shared by several sequences once per step
+    shared_prefix: object = False       # False, True, "l2" or "auto" (see DecodeBatch)
 
     @property
     def group(self) -> int:
@@ -46,8 +46,11 @@ CONFIGS = {
     # GQA 64 query / 8 kv heads x 128 in bf16, batch 128, lengths log-normal
     # (median 1000) clipped to [16, 8192]; half the sequences share a 512-token
     # prefix through refcounted blocks.
+    # The batch reads the shared blocks in the form "auto" picks for it (here
+    # through the L2 by the balanced pass; the prefix kernel for long prompts).
     "gqa_prefix": Config("gqa_prefix", 1, 128, 64, 8, 128, "bf16", "bf16",
-                         ("lognormal", 1000.0, 1.0, 16, 8192), share_prefix_tokens=512),
+                         ("lognormal", 1000.0, 1.0, 16, 8192), share_prefix_tokens=512,
+                         shared_prefix="auto"),
     # Long-context split-K: batch 8, MHA 32 x 128, lengths U{16384..32768}, KV in
     # FP8 E4M3 with per-head fp32 scales, q fp16, partitions of 512 tokens.
     "longctx_fp8": Config("longctx_fp8", 1, 8, 32, 32, 128, "e4m3", "f16",
