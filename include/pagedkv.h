@@ -335,7 +335,9 @@ size_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                                           rounded up to a multiple of 256
  * For partition p of sequence i (tokens [p*PS, min((p+1)*PS, L))):
  *   m_p = max_t s_t, l_p = sum_t exp(s_t - m_p), o_p = sum_t exp(s_t - m_p) v_t / l_p,
- * with s_t = scale * <q, k_t> in natural-log units. */
+ * with s_t = scale * <q, k_t> in natural-log units. Exception: a fused step
+ * (paged_attn_decode_append) on an FP8 cache counts the new token at L - 1 in
+ * the first partition it reads instead of the last (the merge is the same). */
 
 /* Single-query decode attention over the paged cache of one layer ([P2]
  * "PagedAttention：...": the attention kernel reads KV from non-contiguous
@@ -381,12 +383,15 @@ pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, const void* q,
 /* One decode step of one layer in one call: kv_cache_append of each
  * sequence's new token, then paged_attn_decode ([P2] "PagedAttention：...":
  * the step appends the token produced last and attends over the whole
- * context, the new token included). On a 16-bit cache with one query head
- * per kv head, the per-sequence and split-K forms store the new tokens from
- * inside the decode kernel (the wave that reads a token's tile takes it from
- * new_k / new_v and writes its slot), which saves the append launch; every
- * other form (balanced single pass, grouped heads, FP8) runs the append as a
- * kernel of its own first, on the same stream.
+ * context, the new token included). The per-sequence and split-K forms store
+ * the new tokens from inside the decode kernel on a 16-bit cache with one
+ * query head per kv head (the wave that reads a token's tile takes its row
+ * from new_k / new_v and writes its slot) and on an FP8 cache with up to two
+ * (that wave attends over the positions before the token and then folds in
+ * the token's encoded K and V, which it writes to the slot), saving the
+ * append launch; every other form (balanced single pass, grouped heads on a
+ * 16-bit cache, FP8 with four or eight query heads per kv head) runs the
+ * append as a kernel of its own first, on the same stream.
  * new_k, new_v: device [num_seqs][num_kv_heads][head_dim] of src_dtype, which
  *   must equal q_dtype (for a 16-bit cache, also the cache dtype); 16-byte
  *   aligned.

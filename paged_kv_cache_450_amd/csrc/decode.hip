@@ -82,6 +82,13 @@ hipError_t launch(const DecodeParams& prm, dim3 grid, hipStream_t stream) {
         else
             hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, ring_depth<KV, D, G>()>), grid,
                                dim3(NW * 64), 0, stream, prm);
+    } else if constexpr (G <= 2) {
+        if (prm.new_k != nullptr)  // FP8: the new tokens folded in by the kernel
+            hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, ring_depth<KV, D, G>(), true>),
+                               grid, dim3(NW * 64), 0, stream, prm);
+        else
+            hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, ring_depth<KV, D, G>()>), grid,
+                               dim3(NW * 64), 0, stream, prm);
     } else {
         hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, ring_depth<KV, D, G>()>), grid,
                            dim3(NW * 64), 0, stream, prm);
@@ -425,10 +432,11 @@ pkv_status decode_impl(const char* fn, const pkv_pool* pool, int32_t layer, cons
     }
 
     // The fused step's new tokens: stored from inside the vector-ALU kernel
-    // on 16-bit caches with one query head per kv head; elsewhere (FP8, the
-    // matrix-core kernel), that code would cost the kernel more than the
-    // separate append launch does.
-    if (new_k != nullptr && !(pkv::is_16bit(d.kv_dtype) && G == 1)) {
+    // (16-bit caches with one query head per kv head, FP8 caches with up to
+    // two); for the matrix-core kernel, and for FP8 with four or eight query
+    // heads per kv head (whose kernels would lose a wave per SIMD), that code
+    // would cost more than the separate append launch does.
+    if (new_k != nullptr && (pkv::is_16bit(d.kv_dtype) ? G > 1 : G > 2)) {
         const pkv_status sa = append_first(fn, pool, layer, new_k, new_v, q_dtype, block_tables,
                                            max_blocks_per_seq, context_lens, num_seqs,
                                            max_context_len, k_scale, v_scale, stream);

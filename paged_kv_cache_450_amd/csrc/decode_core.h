@@ -217,9 +217,13 @@ __device__ __forceinline__ void combine_waves(const DecodeParams& p, int s, int 
 // the logical blocks b0 + w + k*NW for k < n (the partition's blocks from the
 // window's first on, dealt round robin to the NW waves of the workgroup).
 // newk: the index of the tile holding the token a fused append writes
-// (position L - 1), when this wave reads it; else -1.
+// (position L - 1), when this wave reads it; else -1. fold: this wave is the
+// first wave of the workgroup that reads the context's first attended block
+// (kFused calls; the FP8 kernel folds the new token in there, so the extra
+// work falls on a workgroup dispatched early).
 struct WaveWork {
     int s, L, lo, b0, n, newk;
+    bool fold;
 };
 
 // Grid (kv head, sequence, partition), kv head fastest. Workgroups are dealt
@@ -275,9 +279,11 @@ __device__ __forceinline__ bool locate_work(const DecodeParams& p, int g, int pa
     // The fused append writes position L - 1 only when the context is whole
     // here (not clamped): otherwise its last token lies outside this call.
     ww.newk = -1;
+    ww.fold = false;
     if constexpr (kFused) {
-        if (ww.n > 0 && ww.b0 + (ww.n - 1) * NW == nblk - 1 && p.context_lens[s] == L)
-            ww.newk = ww.n - 1;
+        const bool whole = p.context_lens[s] == L;
+        if (ww.n > 0 && ww.b0 + (ww.n - 1) * NW == nblk - 1 && whole) ww.newk = ww.n - 1;
+        ww.fold = whole && L > 0 && w == 0 && b0 == (lo >> 4);
     }
     return true;
 }

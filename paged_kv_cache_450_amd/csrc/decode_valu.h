@@ -219,17 +219,72 @@ __device__ __forceinline__ void store_result(const DecodeParams& p, int s, int q
     }
 }
 
+// Fused append on an FP8 cache: the new token of sequence s (kv head g, the
+// last position L - 1, offset off of block id) is folded into the lane's
+// softmax state after the wave's tile ring has drained. Its K and V source
+// rows (parked in lds, see NewSrc) are encoded exactly as kv_cache_append
+// encodes them, the codes go to the token's slot, and the attention uses the
+// decoded codes, so the result is the one over the stored bytes. Lane col
+// (= lane mod LPT) owns dims col*EPL .. +EPL, as in the tile loads.
+template <int QD, int D, int G>
+__device__ __forceinline__ void fold_new_token_fp8(const DecodeParams& p,
+                                                   SoftmaxState<PKV_FP8_E4M3, D, G>& st,
+                                                   const QSlice<PKV_FP8_E4M3, D> (&qs)[G],
+                                                   float sscale, const uint8_t* lds, int g,
+                                                   int id, int off, int lane) {
+    using Gm = Geo<PKV_FP8_E4M3, D>;
+    constexpr int EPL = Gm::kEpl, LPT = Gm::kLpt, TB = Gm::kTileBytes;
+    static_assert(EPL == 16, "one lane holds 16 codes: two 8-element source chunks");
+    const int col = lane % LPT;
+    const float ks = p.k_scale[g], vs = p.v_scale[g];
+    const uint2 k0 = quant_e4m3x8<QD>(new_chunk(lds, 0, 2 * col), ks);
+    const uint2 k1 = quant_e4m3x8<QD>(new_chunk(lds, 0, 2 * col + 1), ks);
+    const uint2 v0 = quant_e4m3x8<QD>(new_chunk(lds, 1, 2 * col), vs);
+    const uint2 v1 = quant_e4m3x8<QD>(new_chunk(lds, 1, 2 * col + 1), vs);
+    const uint4 kcode = make_uint4(k0.x, k0.y, k1.x, k1.y);
+    const uint4 vcode = make_uint4(v0.x, v0.y, v1.x, v1.y);
+    float kf[EPL], vf[EPL];
+    v_to_f32<PKV_FP8_E4M3, D>(kcode, kf);
+    v_to_f32<PKV_FP8_E4M3, D>(vcode, vf);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) part = fmaf(kf[e], qs[h].f[e], part);
+        const float sn = group_sum<LPT>(part) * sscale;
+        const float mx = fmaxf(st.m[h], sn);
+        const float a = fast_exp2(st.m[h] - mx), b = fast_exp2(sn - mx);
+        st.l[h] = st.l[h] * a + b;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) st.o[h][e] = fmaf(b, vf[e], st.o[h][e] * a);
+        st.m[h] = mx;
+    }
+    if (lane < LPT) {
+        const size_t at = (static_cast<size_t>(id) * p.num_kv_heads + g) * TB +
+                          static_cast<size_t>(off) * D + col * 16;
+        *reinterpret_cast<uint4*>(const_cast<uint8_t*>(p.k_plane) + at) = kcode;
+        *reinterpret_cast<uint4*>(const_cast<uint8_t*>(p.v_plane) + at) = vcode;
+    }
+}
+
 // Vector-ALU decode: one workgroup of NW wave64s per (kv head, sequence,
 // partition). Each wave streams its tiles through a ring of NBUF tiles held in
 // registers: after a tile is folded into the softmax state its registers are
 // refilled with the tile NBUF positions ahead, so every wave keeps NBUF tiles
 // of loads in flight from its first tile to its last. Used for FP8 caches and
 // for one query head per kv head.
-// kFused (16-bit caches): the call also stores each sequence's new token
-// (see NewSrc).
+// kFused: the call also stores each sequence's new token, taken from the
+// source rows (NewSrc). On 16-bit caches the wave reading the token's tile
+// patches the row into the tile inside the ring. On FP8 caches that wave
+// attends over the positions before the token, and the first wave of the
+// workgroup that reads the context's first attended block (dispatched early,
+// so its extra work stays off the kernel's tail) folds the token in after its
+// ring has drained and stores it (fold_new_token_fp8); with split-K the token
+// thus counts in that first partition's partial.
 template <int KV, int QD, int D, int G, int NW, int NBUF, bool kFused = false>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
-    static_assert(!kFused || KV != PKV_FP8_E4M3, "fused append: 16-bit caches");
+    constexpr bool kPatch = kFused && KV != PKV_FP8_E4M3;
+    constexpr bool kFold = kFused && KV == PKV_FP8_E4M3;
     using Gm = Geo<KV, D>;
     constexpr int EPL = Gm::kEpl, LPT = Gm::kLpt, NLD = Gm::kNld, TB = Gm::kTileBytes;
 
@@ -278,16 +333,25 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
     // ring's first tiles are in flight behind them).
     __shared__ __attribute__((aligned(16))) uint8_t new_rows[kFused ? NW : 1][kFused ? 512 : 16];
     NewSrc<D> ns;
-    if (kFused && ww.newk >= 0) ns.fetch(p, s, g, lane);
+    // kPatch: the wave reading the new token's tile takes its rows; kFold: the
+    // folding wave does, with the block id of the token's slot from the table.
+    const bool takes_new = kPatch ? ww.newk >= 0 : (kFold && ww.fold);
+    if (kFused && takes_new) ns.fetch(p, s, g, lane);
     int new_id = -1;
+    if constexpr (kFold) {
+        if (ww.fold)
+            new_id = p.block_tables[static_cast<size_t>(s) * p.max_blocks + ((L - 1) >> 4)];
+    }
     // Issue the loads of tile kn into a ring slot.
     auto issue = [&](Tile<KV, D>& tt, int& nvalid, int& nlo, int kn) {
         const int id = ids.next(kn);
-        const TileRef r =
-            tile_ref(p, kpl, vpl, bstride, TB, id, (ww.b0 + kn * NW) * 16, L, ww.lo);
+        // FP8 fused append: the new token (position L - 1) is folded in after
+        // the ring, so its tile attends over the positions before it.
+        const TileRef r = tile_ref(p, kpl, vpl, bstride, TB, id, (ww.b0 + kn * NW) * 16,
+                                   (kFold && kn == ww.newk) ? L - 1 : L, ww.lo);
         nvalid = r.nvalid;
         nlo = r.nlo;  // > 0 only on a sliding window's first tile
-        if (kFused && kn == ww.newk) new_id = id;
+        if (kPatch && kn == ww.newk) new_id = id;
 #pragma unroll
         for (int i = 0; i < NLD; ++i) tt.k[i] = rsrc_load16(r.k, voff + i * 1024);
 #pragma unroll
@@ -296,11 +360,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
 
 #pragma unroll
     for (int x = 0; x < NBUF; ++x) issue(t[x], nv[x], nl[x], x);
-    if (kFused && ww.newk >= 0) ns.stash(new_rows[w], lane);
+    if (kFused && takes_new) ns.stash(new_rows[w], lane);
     for (int k0 = 0; k0 < n; k0 += NBUF) {
 #pragma unroll
         for (int x = 0; x < NBUF; ++x) {
-            if (kFused && k0 + x == ww.newk && nv[x] > 0) {
+            if (kPatch && k0 + x == ww.newk && nv[x] > 0) {
                 // The new token (the last of the context): from the source
                 // rows into the tile and into its slot.
                 const int off = nv[x] - 1;
@@ -337,6 +401,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
             }
             st.m[h] = mx;
         }
+    }
+
+    if constexpr (kFold) {
+        if (ww.fold && static_cast<uint32_t>(new_id) < static_cast<uint32_t>(p.num_blocks))
+            fold_new_token_fp8<QD, D, G>(p, st, qs, sscale, new_rows[w], g, new_id, (L - 1) & 15,
+                                         lane);
     }
 
     float vscale = 1.0f;

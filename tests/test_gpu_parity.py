@@ -230,23 +230,26 @@ def test_table_narrower_than_context(ps, balanced):
     H.assert_close(H.out_f64(out, cfg.q_dtype), ref, cfg.kv_dtype, "narrow table")
 
 
+@pytest.mark.parametrize("kv", ["f16", "e4m3"])
 @pytest.mark.parametrize("clamp", ["table", "max_context_len"])
 @pytest.mark.parametrize("ps,balanced", [(0, False), (0, True), (32, None)])
 @pytest.mark.parametrize("hq", [2, 4])
-def test_fused_append_writes_only_inside_the_call(hq, ps, balanced, clamp):
+def test_fused_append_writes_only_inside_the_call(hq, ps, balanced, clamp, kv):
     """paged_attn_decode_append stores a sequence's new token only when its
     last position is inside what the call reads: not for a zero-length
     context, nor for one clamped by a narrow table or by max_context_len;
     those slots keep their poison byte. Outputs match the oracle over the
-    clamped contexts. One query head per kv head (hq 2) stores the tokens
-    from inside the vector kernel, two (hq 4) through the separate append
-    kernel; the balanced pass always through the latter."""
+    clamped contexts. On the 16-bit cache one query head per kv head (hq 2)
+    stores the tokens from inside the vector kernel, two (hq 4) through the
+    separate append kernel, and the balanced pass always through the latter;
+    on the FP8 cache the vector kernel stores them in both cases (it attends
+    over the earlier positions and folds the encoded token in)."""
     import paged_kv_cache_450_amd as P
     from oracle import attention as oattn
 
-    cfg = W.Config("fused_clamp", 1, 7, hq, 2, 64, "f16", "f16", ("uniform", 40, 300),
+    cfg = W.Config(f"fused_clamp_{kv}", 1, 7, hq, 2, 64, kv, "f16", ("uniform", 40, 300),
                    partition_size=ps)
-    say(f"fused clamp={clamp} hq={hq} ps={ps} balanced={balanced}")
+    say(f"fused clamp={clamp} kv={kv} hq={hq} ps={ps} balanced={balanced}")
     side = H.build_product(cfg, seed=8, balanced=balanced, run_step=False)
     b = side.batch
     o = H.oracle_bookkeeping(cfg, 8)
@@ -262,9 +265,10 @@ def test_fused_append_writes_only_inside_the_call(hq, ps, balanced, clamp):
         reach = max_ctx
     lens_dev = torch.from_numpy(lens).cuda()
     out = torch.full_like(b.out, float("nan"))
+    ks, vs = side.k_scale[0], side.v_scale[0]
     P.paged_attn_decode_append(side.cache.handle, 0, side.k_new[0], side.v_new[0], side.q[0],
                                None if ps else out, tables, lens_dev, b.scale, max_ctx, ps,
-                               b.workspace)
+                               b.workspace, ks, vs)
     if ps:
         P.paged_attn_reduce(b.workspace, out, lens_dev, max_ctx, ps)
     torch.cuda.synchronize()
@@ -282,8 +286,13 @@ def test_fused_append_writes_only_inside_the_call(hq, ps, balanced, clamp):
             assert np.all(got.view(np.uint8) == H.POISON), i
     q = H.q_f64(side.q[0], cfg.q_dtype)
     ref = oattn.paged_decode(p6, 0, q, o.tables, np.minimum(lens, reach),
-                             float(np.float32(b.scale)), cfg.kv_dtype)
-    H.assert_close(H.out_f64(out, cfg.q_dtype), ref, cfg.kv_dtype, "fused clamp")
+                             float(np.float32(b.scale)), cfg.kv_dtype,
+                             None if ks is None else ks.cpu().numpy(),
+                             None if vs is None else vs.cpu().numpy())
+    got = H.out_f64(out, cfg.q_dtype)
+    H.assert_close(got, ref, cfg.kv_dtype, "fused clamp")
+    if kv == "e4m3":
+        H.assert_tight(got, ref, cfg.q_dtype, what="fused clamp, FP8")
 
 
 @pytest.mark.parametrize("dt,dim,hq,ps", [("f16", 128, 4, 512), ("bf16", 64, 8, 16),
