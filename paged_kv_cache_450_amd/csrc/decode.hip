@@ -68,6 +68,12 @@ constexpr int ring_depth() {
     return (G <= 2) ? 4 : (G == 4 ? 2 : 1);
 }
 
+// Tile ring of the vector-ALU kernel: registers (false) or two tiles of LDS
+// filled by direct buffer-to-LDS loads (true), on 16-bit caches and on FP8
+// caches (up to two query heads per kv head).
+constexpr bool kLdsRing = true;
+constexpr bool kLdsRingFp8 = false;
+
 template <int KV, int QD, int D, int G, int NW>
 hipError_t launch(const DecodeParams& prm, dim3 grid, hipStream_t stream) {
     if constexpr (KV != PKV_FP8_E4M3 && G >= 2) {
@@ -76,18 +82,20 @@ hipError_t launch(const DecodeParams& prm, dim3 grid, hipStream_t stream) {
         hipLaunchKernelGGL((decode_mfma_kernel<KV, D, G, NW, (D == 128 ? 2 : 4)>), grid,
                            dim3(NW * 64), 0, stream, prm);
     } else if constexpr (KV != PKV_FP8_E4M3 && G == 1) {
+        constexpr int R = kLdsRing ? 2 : ring_depth<KV, D, G>();
         if (prm.new_k != nullptr)  // the new tokens stored from inside the kernel
-            hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, ring_depth<KV, D, G>(), true>),
-                               grid, dim3(NW * 64), 0, stream, prm);
+            hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, R, true, kLdsRing>), grid,
+                               dim3(NW * 64), 0, stream, prm);
         else
-            hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, ring_depth<KV, D, G>()>), grid,
+            hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, R, false, kLdsRing>), grid,
                                dim3(NW * 64), 0, stream, prm);
     } else if constexpr (G <= 2) {
+        constexpr int R = kLdsRingFp8 ? 2 : ring_depth<KV, D, G>();
         if (prm.new_k != nullptr)  // FP8: the new tokens folded in by the kernel
-            hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, ring_depth<KV, D, G>(), true>),
-                               grid, dim3(NW * 64), 0, stream, prm);
+            hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, R, true, kLdsRingFp8>), grid,
+                               dim3(NW * 64), 0, stream, prm);
         else
-            hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, ring_depth<KV, D, G>()>), grid,
+            hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, R, false, kLdsRingFp8>), grid,
                                dim3(NW * 64), 0, stream, prm);
     } else {
         hipLaunchKernelGGL((decode_kernel<KV, QD, D, G, NW, ring_depth<KV, D, G>()>), grid,

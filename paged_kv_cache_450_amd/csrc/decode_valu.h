@@ -281,8 +281,12 @@ __device__ __forceinline__ void fold_new_token_fp8(const DecodeParams& p,
 // so its extra work stays off the kernel's tail) folds the token in after its
 // ring has drained and stores it (fold_new_token_fp8); with split-K the token
 // thus counts in that first partition's partial.
-template <int KV, int QD, int D, int G, int NW, int NBUF, bool kFused = false>
+// kLds: the tile ring lives in LDS (two tiles per wave), filled by direct
+// buffer-to-LDS loads, and a tile is read into registers only when it is
+// consumed; otherwise (the default) the ring is NBUF tiles of registers.
+template <int KV, int QD, int D, int G, int NW, int NBUF, bool kFused = false, bool kLds = false>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
+    static_assert(!kLds || NBUF == 2, "LDS ring: two slots");
     constexpr bool kPatch = kFused && KV != PKV_FP8_E4M3;
     constexpr bool kFold = kFused && KV == PKV_FP8_E4M3;
     using Gm = Geo<KV, D>;
@@ -326,8 +330,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
     const size_t bstride = static_cast<size_t>(p.num_kv_heads) * TB;
     const int voff = lane * 16;
 
-    Tile<KV, D> t[NBUF];
+    Tile<KV, D> t[kLds ? 1 : NBUF];
     int nv[NBUF], nl[NBUF];
+    // LDS ring: one array per slot, so that reading a slot waits only for
+    // that slot's loads (the later slot's stay in flight).
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[kLds ? NW : 1][kLds ? 2 * TB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[kLds ? NW : 1][kLds ? 2 * TB : 16];
     // Fused append: the wave that reads the new token's tile fetches its
     // source rows first and parks them in LDS once they land (by then the
     // ring's first tiles are in flight behind them).
@@ -342,8 +350,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
         if (ww.fold)
             new_id = p.block_tables[static_cast<size_t>(s) * p.max_blocks + ((L - 1) >> 4)];
     }
-    // Issue the loads of tile kn into a ring slot.
-    auto issue = [&](Tile<KV, D>& tt, int& nvalid, int& nlo, int kn) {
+    // Issue the loads of tile kn into a ring slot (x: the slot, for the LDS ring).
+    auto issue = [&](Tile<KV, D>& tt, int& nvalid, int& nlo, int kn, int x) {
         const int id = ids.next(kn);
         // FP8 fused append: the new token (position L - 1) is folded in after
         // the ring, so its tile attends over the positions before it.
@@ -352,33 +360,64 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
         nvalid = r.nvalid;
         nlo = r.nlo;  // > 0 only on a sliding window's first tile
         if (kPatch && kn == ww.newk) new_id = id;
+        if constexpr (kLds) {
+            typedef __attribute__((address_space(3))) void* lds_ptr;
+            uint8_t* slot = x == 0 ? ring0[w] : ring1[w];
+            // The slot's earlier reads must have completed: the refill's LDS
+            // writes do not queue behind this wave's own LDS reads.
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) tt.k[i] = rsrc_load16(r.k, voff + i * 1024);
+            for (int i = 0; i < NLD; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r.k, (lds_ptr)(slot + i * 1024), 16,
+                                                         voff + i * 1024, 0, 0, kStreamPolicy);
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) tt.v[i] = rsrc_load16(r.v, voff + i * 1024);
+            for (int i = 0; i < NLD; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r.v, (lds_ptr)(slot + TB + i * 1024), 16,
+                                                         voff + i * 1024, 0, 0, kStreamPolicy);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) tt.k[i] = rsrc_load16(r.k, voff + i * 1024);
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) tt.v[i] = rsrc_load16(r.v, voff + i * 1024);
+        }
     };
 
 #pragma unroll
-    for (int x = 0; x < NBUF; ++x) issue(t[x], nv[x], nl[x], x);
+    for (int x = 0; x < NBUF; ++x) issue(t[kLds ? 0 : x], nv[x], nl[x], x, x);
     if (kFused && takes_new) ns.stash(new_rows[w], lane);
     for (int k0 = 0; k0 < n; k0 += NBUF) {
 #pragma unroll
         for (int x = 0; x < NBUF; ++x) {
+            Tile<KV, D>& tx = t[kLds ? 0 : x];
+            if constexpr (kLds) {
+                const uint8_t* slot = x == 0 ? ring0[w] : ring1[w];
+                // Wait for this slot's loads (the other slot's 2*NLD stay in
+                // flight) explicitly: the compiler's own wait for buffer-to-LDS
+                // loads missed a read it had split and hoisted.
+                static_assert(2 * NLD < 16, "vmcnt field");
+                __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NLD));  // vmcnt(2*NLD)
+#pragma unroll
+                for (int i = 0; i < NLD; ++i)
+                    tx.k[i] = *reinterpret_cast<const uint4*>(slot + i * 1024 + voff);
+#pragma unroll
+                for (int i = 0; i < NLD; ++i)
+                    tx.v[i] = *reinterpret_cast<const uint4*>(slot + TB + i * 1024 + voff);
+            }
             if (kPatch && k0 + x == ww.newk && nv[x] > 0) {
                 // The new token (the last of the context): from the source
                 // rows into the tile and into its slot.
                 const int off = nv[x] - 1;
                 const uint4 kc = new_chunk(new_rows[w], 0, col);
                 const uint4 vc = new_chunk(new_rows[w], 1, col);
-                patch_natural<LPT>(t[x].k, kc, off, lane);
-                patch_natural<LPT>(t[x].v, vc, off, lane);
+                patch_natural<LPT>(tx.k, kc, off, lane);
+                patch_natural<LPT>(tx.v, vc, off, lane);
                 store_new_row<LPT>(p, g, new_id, off, TB, kc, vc, lane);
             }
             if (nv[x] == 16 && nl[x] == 0)
-                consume_tile<KV, D, G, false>(st, t[x], 16, 0, qs, sscale, row);
+                consume_tile<KV, D, G, false>(st, tx, 16, 0, qs, sscale, row);
             else
-                consume_tile<KV, D, G, true>(st, t[x], nv[x], nl[x], qs, sscale, row);
-            issue(t[x], nv[x], nl[x], k0 + x + NBUF);
+                consume_tile<KV, D, G, true>(st, tx, nv[x], nl[x], qs, sscale, row);
+            issue(tx, nv[x], nl[x], k0 + x + NBUF, x);
         }
     }
 
