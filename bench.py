@@ -56,30 +56,26 @@ KERNEL_SOURCES = {
                                          "device.h", "common.h")),
 }
 MEASURED_TRAFFIC = {  # traffic_key -> counters of the decode call's streaming kernel
-    "llama13b_layer": {  # FETCH 367,298.7 KiB x 1.99988 + WRITE 960.0 KiB
-        "kernel": "valu", "bytes": 753_164_689,
-        "sources_sha256": "4c433fb86e79da107b4a2f1ffba567c5e9fef8ba727ce55b46766fe30d3f66b0",
+    "llama13b_layer": {  # FETCH 367,274.2 KiB x 1.99992 + WRITE 960.0 KiB
+        "kernel": "valu", "bytes": 753_129_040,
+        "sources_sha256": "2ade13fbe4e3465a5c62017d73ec394327a2df8a85a3e1c709e1216052dad356",
         "summary": "profiles/decode_kernel_llama13b_layer.md"},
-    "longctx_fp8": {  # FETCH 715,694.3 KiB x 1.99998 + WRITE 5,755.4 KiB
-        "kernel": "valu", "bytes": 1_471_617_403,
-        "sources_sha256": "4c433fb86e79da107b4a2f1ffba567c5e9fef8ba727ce55b46766fe30d3f66b0",
+    "longctx_fp8": {  # FETCH 715,839.1 KiB x 1.99998 + WRITE 5,818.4 KiB
+        "kernel": "valu", "bytes": 1_471_978_298,
+        "sources_sha256": "2ade13fbe4e3465a5c62017d73ec394327a2df8a85a3e1c709e1216052dad356",
         "summary": "profiles/decode_kernel_longctx_fp8.md"},
-    "gqa_prefix": {  # streaming kernel: FETCH 408,477.0 KiB x 1.99995 + WRITE 12,218.6 KiB
-        "kernel": "balanced", "bytes": 849_050_127,
-        "sources_sha256": "fb0e407c583d53f647f6619c9aa5a38c64868751379ae4f5af3d03d891d53849",
+    "gqa_prefix/shared_prefix_l2": {  # streaming kernel: FETCH 369,434.8 KiB x 1.99995 + WRITE 12,224.2 KiB
+        "kernel": "balanced", "bytes": 769_103_069,
+        "sources_sha256": "3fd87e013c90413ea4a59b975feee15cb2f34435c8a717880ae736795fbb6824",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
-    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 358,265.8 KiB x 1.99989 + WRITE 12,411.6 KiB
-        "kernel": "prefix", "bytes": 746_396_022,
-        "sources_sha256": "fd635a157ed1a8cea7607948a27cebaaa807559ce56cf220e33ab9b9d5556dc5",
+    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 358,288.6 KiB x 1.99992 + WRITE 12,413.5 KiB
+        "kernel": "prefix", "bytes": 746_457_042,
+        "sources_sha256": "25cec0b9e8ef04c5980bef970fcfeb0709303dba994c70ab7625e9eaaa52a7ba",
         "summary": "profiles/prefix_kernel_gqa_prefix.md"},
-    "gqa_prefix/shared_prefix/prompt2048": {  # streaming kernel: FETCH 262,190.6 KiB x 1.99992 + WRITE 12,448.0 KiB
-        "kernel": "prefix", "bytes": 549_690_992,
-        "sources_sha256": "fd635a157ed1a8cea7607948a27cebaaa807559ce56cf220e33ab9b9d5556dc5",
-        "summary": "profiles/prefix_kernel_gqa_prefix.md"},
-    "gqa_prefix/prompt2048": {  # streaming kernel: FETCH 471,493.9 KiB x 1.99992 + WRITE 12,326.9 KiB
-        "kernel": "balanced", "bytes": 978_203_484,
-        "sources_sha256": "fb0e407c583d53f647f6619c9aa5a38c64868751379ae4f5af3d03d891d53849",
-        "summary": "profiles/prefix_kernel_gqa_prefix.md"},
+    "7b_32layer": {  # streaming kernel: FETCH 1,049,128.5 KiB x 1.99998 + WRITE 512.0 KiB
+        "kernel": "balanced", "bytes": 2_149_112_831,
+        "sources_sha256": "3fd87e013c90413ea4a59b975feee15cb2f34435c8a717880ae736795fbb6824",
+        "summary": "profiles/decode_balanced_kernel_7b_32layer.md"},
 }
 
 
