@@ -144,6 +144,7 @@ struct ValuMath {
     using Gm = Geo<KV, D>;
     static constexpr int kG = 1;
     static constexpr bool kPrefetchQ = true;  // q is small: ride in the ring with its tile
+    static constexpr bool kSplit = false;     // the tile math is one piece (consume)
     static constexpr int kEpl = Gm::kEpl, kLpt = Gm::kLpt, kNld = Gm::kNld, kTB = Gm::kTileBytes;
     using TileT = Tile<KV, D>;
     using QT = QSlice<KV, D>;
@@ -239,6 +240,10 @@ struct MfmaMath {
     using Gm = MfmaGeo<D>;
     static constexpr int kG = G;
     static constexpr bool kPrefetchQ = false;  // fetched into LDS at segment start
+    // The tile math comes in two halves (front reads the tile's registers,
+    // back does the softmax and PV from LDS), so the ring slot is refilled
+    // between them.
+    static constexpr bool kSplit = true;
     static constexpr int kNk = Gm::kNk, kNv = Gm::kNv, kNd = Gm::kNd, kTB = Gm::kTileBytes;
     static constexpr int kQBytes = kNk * 1024;  // Q^T operand of one wave in LDS
     using TileT = MfmaTile<D>;
@@ -292,6 +297,15 @@ struct MfmaMath {
                                    float sscale, int lane) {
         mfma_consume<KV, D, kPartial>(t, nvalid, nlo, QLds<D>{x.qlds}, x.o, x.m, x.lsum, sscale,
                                       x.stage, lane);
+    }
+    template <bool kPartial>
+    __device__ static f32x4_t front(State& x, const TileT& t, int nvalid, int nlo, int lane) {
+        return mfma_front<KV, D, kPartial>(t, nvalid, nlo, QLds<D>{x.qlds}, x.stage, lane);
+    }
+    template <bool kPartial>
+    __device__ static void back(State& x, f32x4_t sacc, int nvalid, int nlo, float sscale,
+                                int lane) {
+        mfma_back<KV, D, kPartial>(sacc, nvalid, nlo, x.o, x.m, x.lsum, sscale, x.stage, lane);
     }
     __device__ static void finish(State& x) {
         x.lsum += __shfl_xor(x.lsum, 16);
@@ -453,10 +467,26 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
                 else
                     M::fetch_q_lds(p, st, cur.s, cur.g, lane);
             }
-            if (cur.nvalid == 16 && cur.nlo == 0)
-                M::template consume<false>(st, tr[x], 16, 0, q, p.scale_log2, lane);
-            else if (cur.nvalid > 0)
-                M::template consume<true>(st, tr[x], cur.nvalid, cur.nlo, q, p.scale_log2, lane);
+            const bool full = cur.nvalid == 16 && cur.nlo == 0;
+            if constexpr (M::kSplit) {
+                // First half, then the slot's refill, then the second half.
+                f32x4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (full)
+                    sacc = M::template front<false>(st, tr[x], 16, 0, lane);
+                else if (cur.nvalid > 0)
+                    sacc = M::template front<true>(st, tr[x], cur.nvalid, cur.nlo, lane);
+                issue(tr[x], si[x], qring[M::kPrefetchQ ? x : 0], k0 + x + NBUF);
+                if (full)
+                    M::template back<false>(st, sacc, 16, 0, p.scale_log2, lane);
+                else if (cur.nvalid > 0)
+                    M::template back<true>(st, sacc, cur.nvalid, cur.nlo, p.scale_log2, lane);
+            } else {
+                if (full)
+                    M::template consume<false>(st, tr[x], 16, 0, q, p.scale_log2, lane);
+                else if (cur.nvalid > 0)
+                    M::template consume<true>(st, tr[x], cur.nvalid, cur.nlo, q, p.scale_log2,
+                                              lane);
+            }
             if (cur.flags & 2) {
                 // End of a segment: write the output, or the partial of a split context.
                 M::finish(st);
@@ -473,7 +503,7 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
                 }
                 M::reset(st);
             }
-            issue(tr[x], si[x], qring[M::kPrefetchQ ? x : 0], k0 + x + NBUF);
+            if constexpr (!M::kSplit) issue(tr[x], si[x], qring[M::kPrefetchQ ? x : 0], k0 + x + NBUF);
         }
     }
 }

@@ -83,19 +83,41 @@ struct QLds {
     }
 };
 
-// Attended tokens of the tile: [nlo, nvalid) (kPartial: the masked form).
+// The first half of a tile's math, everything that reads the tile's
+// registers: the scores S^T = K Q^T of head hl for tokens 4*kg + r (returned),
+// and V staged in LDS (natural layout, padded rows; tokens outside
+// [nlo, nvalid) become zeros so that stale or NaN bytes never meet a zero
+// probability). Once it returns, the tile's registers may be refilled.
+// kPartial: the masked form.
 template <int KV, int D, bool kPartial, class QSrc>
-__device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid, int nlo,
-                                             const QSrc& qsrc,
-                                             f32x4_t (&o)[MfmaGeo<D>::kNd], float& m, float& lsum,
-                                             float sscale, uint8_t* stage, int lane) {
+__device__ __forceinline__ f32x4_t mfma_front(const MfmaTile<D>& t, int nvalid, int nlo,
+                                              const QSrc& qsrc, uint8_t* stage, int lane) {
     using Gm = MfmaGeo<D>;
-    const int kg = lane >> 4;   // this lane's tokens: 4*kg .. 4*kg + 3
-    const int hl = lane & 15;
-    // Scores of head hl for tokens 4*kg + r.
     f32x4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < Gm::kNk; ++c) sacc = mfma_qk<KV>(t.k[c], qsrc.get(c, lane), sacc);
+    constexpr int kLanesPerRow = Gm::kRowBytes / 16;
+#pragma unroll
+    for (int i = 0; i < Gm::kNv; ++i) {
+        const int tok = i * (64 / kLanesPerRow) + lane / kLanesPerRow;
+        uint4 v = t.v[i];
+        if constexpr (kPartial) {
+            if (tok >= nvalid || tok < nlo) v = make_uint4(0u, 0u, 0u, 0u);
+        }
+        *reinterpret_cast<uint4*>(stage + tok * Gm::kPitch + (lane % kLanesPerRow) * 16) = v;
+    }
+    return sacc;
+}
+
+// The second half: online softmax of the scores and O^T += V^T P^T from the
+// staged V. Attended tokens: [nlo, nvalid).
+template <int KV, int D, bool kPartial>
+__device__ __forceinline__ void mfma_back(f32x4_t sacc, int nvalid, int nlo,
+                                          f32x4_t (&o)[MfmaGeo<D>::kNd], float& m, float& lsum,
+                                          float sscale, const uint8_t* stage, int lane) {
+    using Gm = MfmaGeo<D>;
+    const int kg = lane >> 4;   // this lane's tokens: 4*kg .. 4*kg + 3
+    const int hl = lane & 15;
     float sc[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -142,19 +164,6 @@ __device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid, i
         pb_lo = __builtin_bit_cast(s16x4_t,
                                    make_uint2(pack2<KV>(rl[0], rl[1]), pack2<KV>(rl[2], rl[3])));
     }
-
-    // Stage V in LDS (natural layout, padded rows); tokens past nvalid become
-    // zeros so that stale or NaN bytes never meet a zero probability.
-    constexpr int kLanesPerRow = Gm::kRowBytes / 16;
-#pragma unroll
-    for (int i = 0; i < Gm::kNv; ++i) {
-        const int tok = i * (64 / kLanesPerRow) + lane / kLanesPerRow;
-        uint4 v = t.v[i];
-        if constexpr (kPartial) {
-            if (tok >= nvalid || tok < nlo) v = make_uint4(0u, 0u, 0u, 0u);
-        }
-        *reinterpret_cast<uint4*>(stage + tok * Gm::kPitch + (lane % kLanesPerRow) * 16) = v;
-    }
     // Transposed reads: lane (within its group of 16) j' supplies row
     // 4*kg + j'/4, dims 16*jd + 4*(j'%4); it receives dims 16*jd + j' of
     // tokens 4*kg .. 4*kg + 3.
@@ -167,6 +176,17 @@ __device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid, i
         o[jd] = mfma_pv<KV>(__builtin_bit_cast(s16x4_t, va), pb, o[jd]);
         if constexpr (KV == PKV_BF16) o[jd] = mfma_pv<KV>(__builtin_bit_cast(s16x4_t, va), pb_lo, o[jd]);
     }
+}
+
+// One tile's whole math. Attended tokens of the tile: [nlo, nvalid)
+// (kPartial: the masked form).
+template <int KV, int D, bool kPartial, class QSrc>
+__device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid, int nlo,
+                                             const QSrc& qsrc,
+                                             f32x4_t (&o)[MfmaGeo<D>::kNd], float& m, float& lsum,
+                                             float sscale, uint8_t* stage, int lane) {
+    const f32x4_t sacc = mfma_front<KV, D, kPartial>(t, nvalid, nlo, qsrc, stage, lane);
+    mfma_back<KV, D, kPartial>(sacc, nvalid, nlo, o, m, lsum, sscale, stage, lane);
 }
 
 template <int KV, int D, int G, int NW, int NBUF>

@@ -413,11 +413,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
                 patch_natural<LPT>(tx.v, vc, off, lane);
                 store_new_row<LPT>(p, g, new_id, off, TB, kc, vc, lane);
             }
-            if (nv[x] == 16 && nl[x] == 0)
+            // LDS ring: the tile is in registers now, so the slot is refilled
+            // before the math (two tiles stay in flight while it runs).
+            const int cnv = nv[x], cnl = nl[x];
+            if constexpr (kLds) issue(tx, nv[x], nl[x], k0 + x + NBUF, x);
+            if (cnv == 16 && cnl == 0)
                 consume_tile<KV, D, G, false>(st, tx, 16, 0, qs, sscale, row);
             else
-                consume_tile<KV, D, G, true>(st, tx, nv[x], nl[x], qs, sscale, row);
-            issue(tx, nv[x], nl[x], k0 + x + NBUF, x);
+                consume_tile<KV, D, G, true>(st, tx, cnv, cnl, qs, sscale, row);
+            if constexpr (!kLds) issue(tx, nv[x], nl[x], k0 + x + NBUF, x);
         }
     }
 
