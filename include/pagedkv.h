@@ -389,9 +389,13 @@ pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, const void* q,
  * from new_k / new_v and writes its slot) and on an FP8 cache with up to two
  * (that wave attends over the positions before the token and then folds in
  * the token's encoded K and V, which it writes to the slot), saving the
- * append launch; every other form (balanced single pass, grouped heads on a
- * 16-bit cache, FP8 with four or eight query heads per kv head) runs the
- * append as a kernel of its own first, on the same stream.
+ * append launch. The balanced single pass does the same for any group size:
+ * it reads each context's blocks without the new token's position and the
+ * token as one more tile from new_k / new_v, whose wave also writes its slot.
+ * The other forms (grouped heads on a 16-bit cache per sequence or split-K,
+ * FP8 with four or eight query heads per kv head, and the balanced pass with
+ * a shared-prefix pass, which reads the pool first) run the append as a
+ * kernel of its own first, on the same stream.
  * new_k, new_v: device [num_seqs][num_kv_heads][head_dim] of src_dtype, which
  *   must equal q_dtype (for a 16-bit cache, also the cache dtype); 16-byte
  *   aligned.

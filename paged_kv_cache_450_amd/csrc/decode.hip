@@ -176,7 +176,7 @@ size_t balanced_bytes(size_t group, size_t head_dim, size_t waves) {
     return waves * 2 * group * (head_dim + 4) * sizeof(float);
 }
 
-template <class M, int KV, int D, int NBUF, bool kPre, bool kKeep>
+template <class M, int KV, int D, int NBUF, bool kPre, bool kKeep, bool kFold>
 hipError_t launch_balanced_as(DecodeParams prm, int cus, hipStream_t st) {
     static int wgs_per_cu = -1;  // per kernel instance; the same on every gfx950 device
     if (wgs_per_cu < 0) {
@@ -184,13 +184,13 @@ hipError_t launch_balanced_as(DecodeParams prm, int cus, hipStream_t st) {
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
                 &nb,
                 reinterpret_cast<const void*>(
-                    &decode_balanced_kernel<M, KV, D, NBUF, kPre, kKeep>),
+                    &decode_balanced_kernel<M, KV, D, NBUF, kPre, kKeep, kFold>),
                 256, 0) != hipSuccess)
             return hipGetLastError();
         wgs_per_cu = std::max(1, std::min(nb, kBalancedWavesPerCu / 4));
     }
     prm.num_waves = cus * wgs_per_cu * 4;
-    hipLaunchKernelGGL((decode_balanced_kernel<M, KV, D, NBUF, kPre, kKeep>),
+    hipLaunchKernelGGL((decode_balanced_kernel<M, KV, D, NBUF, kPre, kKeep, kFold>),
                        dim3(prm.num_waves / 4), dim3(256), 0, st, prm);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -206,10 +206,12 @@ hipError_t launch_balanced_as(DecodeParams prm, int cus, hipStream_t st) {
 template <class M, int KV, int D, int NBUF>
 hipError_t launch_balanced(const DecodeParams& prm, int cus, hipStream_t st) {
     if (prm.pre_blocks != nullptr)
-        return launch_balanced_as<M, KV, D, NBUF, true, false>(prm, cus, st);
+        return launch_balanced_as<M, KV, D, NBUF, true, false, false>(prm, cus, st);
     if (prm.keep_blocks != nullptr)
-        return launch_balanced_as<M, KV, D, NBUF, false, true>(prm, cus, st);
-    return launch_balanced_as<M, KV, D, NBUF, false, false>(prm, cus, st);
+        return prm.fold_new ? launch_balanced_as<M, KV, D, NBUF, false, true, true>(prm, cus, st)
+                            : launch_balanced_as<M, KV, D, NBUF, false, true, false>(prm, cus, st);
+    return prm.fold_new ? launch_balanced_as<M, KV, D, NBUF, false, false, true>(prm, cus, st)
+                        : launch_balanced_as<M, KV, D, NBUF, false, false, false>(prm, cus, st);
 }
 
 // Ring depths keep two waves per SIMD (MFMA at D = 128 holds its O^T
@@ -407,7 +409,14 @@ pkv_status decode_impl(const char* fn, const pkv_pool* pool, int32_t layer, cons
                 prm.num_groups = pfx->num_groups;
                 prm.pre_slots = (pfx->max_group_size * G + 15) / 16;
             }
-            if (new_k != nullptr) {
+            // The fused step's new tokens: each is a tile of its own in the
+            // streaming kernel, whose wave also stores it (fold_new; the slot
+            // travels as block id * 16 + position in 31 bits); with a prefix
+            // pass, which reads the pool first, an append launch stores them
+            // ahead of it.
+            if (new_k != nullptr && !with_pre && d.num_blocks < (1 << 27)) {
+                prm.fold_new = 1;
+            } else if (new_k != nullptr) {
                 const pkv_status sa = append_first(
                     fn, pool, layer, new_k, new_v, q_dtype, block_tables, max_blocks_per_seq,
                     context_lens, num_seqs, max_context_len, k_scale, v_scale, stream);

@@ -43,7 +43,8 @@ using namespace pkv::dev;
 struct TileWalk {
     int s, g, j, nblk;   // current tile: sequence, kv head, block; blocks end at nblk
     int jlo, lo;         // first block read, first token attended (sliding window)
-    int L;               // tokens of sequence s as read here
+    int L;               // tokens of sequence s read from its blocks (kFold: without
+                         // the new token's position)
     int has_pre;         // sequence s has a shared-prefix partial
     int64_t a_sg;        // global index of tile (s, g, jlo)
     int chunk;           // sequences 64*chunk .. +63 have their lengths in lens
@@ -51,6 +52,9 @@ struct TileWalk {
     int pres;            // per lane: its leading blocks covered by the prefix pass
     int keeps;           // per lane: its leading shared blocks read through the L2
     int keep;            // sequence s: blocks below this are read with the caching policy
+    int news;            // per lane: 1 when its new token is a tile of its own (kFold)
+    int nend;            // tiles end at nend: nblk, plus the new token's tile
+    int last_id;         // kFold: id of the last block issued (the new token's block)
     int rbase;           // jlo rounded down to 64: row0_* start there
     int row0_a, row0_b;  // ids of blocks rbase .. +63 and +64 .. +127 of row s (per lane)
     int ids_a, ids_b;    // ids of blocks base .. base+127 (per lane, two chunks)
@@ -60,6 +64,7 @@ struct TileWalk {
 __device__ __forceinline__ void walk_set_seq(const DecodeParams& p, TileWalk& t, int L, int pre) {
     t.L = L;
     t.nblk = (L + 15) >> 4;
+    t.nend = t.nblk;
     t.lo = window_lo(p, L);
     t.jlo = first_block(p, L, pre);
     t.has_pre = pre > 0;
@@ -91,12 +96,13 @@ __device__ __forceinline__ int walk_id(const DecodeParams& p, TileWalk& t, int l
 }
 
 // Step to the next tile. kPre: sequences may begin after shared-prefix blocks;
-// kKeep: sequences have leading shared blocks read through the L2.
-template <bool kPre, bool kKeep>
+// kKeep: sequences have leading shared blocks read through the L2; kFold: a
+// sequence's new token is one more tile after its blocks.
+template <bool kPre, bool kKeep, bool kFold>
 __device__ __forceinline__ void walk_advance(const DecodeParams& p, TileWalk& t, int lane) {
-    if (++t.j < t.nblk) return;
+    if (++t.j < t.nend) return;
     t.j = t.jlo;
-    t.a_sg += t.nblk - t.jlo;
+    t.a_sg += t.nend - t.jlo;
     if (++t.g < p.num_kv_heads) {  // same row, next head: its first 128 blocks are at hand
         t.base = t.rbase;
         t.ids_a = t.row0_a;
@@ -115,22 +121,37 @@ __device__ __forceinline__ void walk_advance(const DecodeParams& p, TileWalk& t,
             t.lens = jj < p.num_seqs ? seq_tokens(p, jj) : 0;
             t.pres = kPre && jj < p.num_seqs ? pre_of(p, jj) : 0;
             if constexpr (kKeep) t.keeps = jj < p.num_seqs ? keep_of(p, jj) : 0;
+            if constexpr (kFold) t.news = jj < p.num_seqs ? new_of(p, jj) : 0;
         }
         walk_set_seq(p, t, __builtin_amdgcn_readlane(t.lens, t.s & 63),
                      __builtin_amdgcn_readlane(t.pres, t.s & 63));
         if constexpr (kKeep) t.keep = __builtin_amdgcn_readlane(t.keeps, t.s & 63);
+        if constexpr (kFold) {
+            const int nt = __builtin_amdgcn_readlane(t.news, t.s & 63);
+            t.nend = t.nblk + nt;
+            t.L -= nt;
+        }
     } while (t.jlo >= t.nblk && t.s + 1 < p.num_seqs);
     t.j = t.jlo;
     walk_enter_row(p, t, lane);
 }
 
-// Ring-slot description of an issued tile (all wave-uniform).
+// Ring-slot description of an issued tile (all wave-uniform, packed: a ring
+// of them lives in scalar registers beside the kernel's pointers).
 struct SlotInfo {
-    int nvalid, nlo;  // attended tokens of the tile: [nlo, nvalid) (nvalid 0 past the range)
-    int flags;        // bit 0: first tile of a segment, bit 1: last tile of a segment,
-                      // bit 2: its sequence has a shared-prefix partial
-    int s, g, ntiles; // its segment's sequence, kv head and tile count
-    int64_t a_sg;     // global index of the segment's first tile
+    // The tile's attended tokens [nlo, nvalid) (nvalid 0 past the range) in
+    // bits 0-4 and 5-9, then the flags below.
+    int bits;
+    int s, g;   // its segment's sequence and kv head
+    int vslot;  // a new token's tile: its slot, block id * 16 + position
+                // (-1: another tile, or no slot to store to)
+    static constexpr int kFirst = 1 << 10;   // first tile of a segment
+    static constexpr int kLast = 1 << 11;    // last tile of a segment
+    static constexpr int kHasPre = 1 << 12;  // its sequence has a shared-prefix partial
+    static constexpr int kWhole = 1 << 13;   // the segment is its context's every tile
+    static constexpr int kSlot1 = 1 << 14;   // a split context's piece that began in this range
+    __device__ int nvalid() const { return bits & 31; }
+    __device__ int nlo() const { return (bits >> 5) & 31; }
 };
 
 template <int D>
@@ -172,6 +193,14 @@ struct ValuMath {
         for (int i = 0; i < kNld; ++i) t.k[i] = rsrc_load16(r.k, lane * 16 + i * 1024);
 #pragma unroll
         for (int i = 0; i < kNld; ++i) t.v[i] = rsrc_load16(r.v, lane * 16 + i * 1024);
+    }
+    // A new token's tile holds the token in row 0 (lanes 0 .. D/8 - 1 of load
+    // 0, 16 bytes each, for K and for V): store it to the slot row at dst.
+    __device__ static void store_new(const DecodeParams& p, const TileT& t, int64_t dst,
+                                     int lane) {
+        if (lane >= 2 * D / 16) return;
+        *reinterpret_cast<uint4*>(const_cast<uint8_t*>(p.k_plane) + dst + lane * 16) = t.k[0];
+        *reinterpret_cast<uint4*>(const_cast<uint8_t*>(p.v_plane) + dst + lane * 16) = t.v[0];
     }
     __device__ static void reset(State& x) {
         x.st.m[0] = -INFINITY;
@@ -286,6 +315,20 @@ struct MfmaMath {
 #pragma unroll
         for (int i = 0; i < kNv; ++i) t.v[i] = rsrc_load16(r.v, lane * 16 + 1024 * i);
     }
+    // A new token's tile holds the token in row 0: K in lanes 0, 16, 32, 48
+    // (bytes 64c + 16 (lane / 16) of the row in load c), V in lanes
+    // 0 .. D/8 - 1 of load 0 (16 bytes each). Store it to the slot row at dst.
+    __device__ static void store_new(const DecodeParams& p, const TileT& t, int64_t dst,
+                                     int lane) {
+        if ((lane & 15) == 0) {
+#pragma unroll
+            for (int c = 0; c < kNk; ++c)
+                *reinterpret_cast<uint4*>(const_cast<uint8_t*>(p.k_plane) + dst + 64 * c +
+                                          16 * (lane >> 4)) = t.k[c];
+        }
+        if (lane < Gm::kRowBytes / 16)
+            *reinterpret_cast<uint4*>(const_cast<uint8_t*>(p.v_plane) + dst + lane * 16) = t.v[0];
+    }
     __device__ static void reset(State& x) {
 #pragma unroll
         for (int j = 0; j < kNd; ++j) x.o[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -343,10 +386,17 @@ struct MfmaMath {
 // (pre_blocks); without it that bookkeeping is compiled out, so its registers
 // cost the other forms nothing.
 // kKeep: some sequences begin with blocks that others of the batch share
-// (keep_blocks); those are loaded with the caching policy.
-template <class M, int KV, int D, int NBUF, bool kPre = false, bool kKeep = false>
+// (keep_blocks); those are loaded with the caching policy. kFold (fold_new):
+// a sequence's new token is one more tile of its context, read from the
+// source rows (16 bytes per lane of row 0; the other rows lie past the end of
+// the row's buffer descriptor and read as zeros), attended with weight like
+// any token and stored to its slot by the wave that reads it. The context's
+// blocks are read without that position (another wave may be storing it).
+template <class M, int KV, int D, int NBUF, bool kPre = false, bool kKeep = false,
+          bool kFold = false>
 __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodeParams p) {
     static_assert(!(kPre && kKeep), "one shared-prefix form at a time");
+    static_assert(!(kPre && kFold), "the prefix pass reads the pool before the new tokens");
     constexpr int G = M::kG;
     constexpr int SS = SlotGeoB<D>::kStride;
     const int lane = threadIdx.x & 63;
@@ -358,8 +408,10 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
     int64_t total = 0;
     for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
         const int jj = c0 + lane;
-        total += wave_sum(
-            jj < p.num_seqs ? pass_tiles(p, seq_tokens(p, jj), kPre ? pre_of(p, jj) : 0) : 0);
+        total += wave_sum(jj < p.num_seqs ? pass_tiles(p, seq_tokens(p, jj),
+                                                      kPre ? pre_of(p, jj) : 0) +
+                                                (kFold ? new_of(p, jj) : 0)
+                                          : 0);
     }
     total *= p.num_kv_heads;
     // R non-empty ranges: with fewer tiles than waves the surplus waves idle,
@@ -379,7 +431,8 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
             const int jj = c0 + lane;
             const int len = jj < p.num_seqs ? seq_tokens(p, jj) : 0;
             const int pre = kPre && jj < p.num_seqs ? pre_of(p, jj) : 0;
-            const int tiles = pass_tiles(p, len, pre) * p.num_kv_heads;
+            const int news = kFold && jj < p.num_seqs ? new_of(p, jj) : 0;
+            const int tiles = (pass_tiles(p, len, pre) + news) * p.num_kv_heads;
             const int incl = wave_incl_scan(tiles, lane);
             const uint64_t hit = __ballot(jj < p.num_seqs && carry + incl > t0);
             if (hit) {
@@ -394,7 +447,13 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
                     tw.keeps = jj < p.num_seqs ? keep_of(p, jj) : 0;
                     tw.keep = __builtin_amdgcn_readlane(tw.keeps, ln);
                 }
-                const int nt = tw.nblk - tw.jlo;  // tiles per head
+                if constexpr (kFold) {
+                    tw.news = news;
+                    const int nt = __builtin_amdgcn_readlane(news, ln);
+                    tw.nend = tw.nblk + nt;
+                    tw.L -= nt;
+                }
+                const int nt = tw.nend - tw.jlo;  // tiles per head
                 const int64_t a_s = carry + __builtin_amdgcn_readlane(incl - tiles, ln);
                 const int64_t off = t0 - a_s;
                 tw.g = static_cast<int>(off / nt);
@@ -428,30 +487,52 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
     // that starts there).
     auto issue = [&](typename M::TileT& tt, SlotInfo& info, typename M::QT& qq, int kn) {
         if (kn >= n) {
-            info.nvalid = 0;
-            info.nlo = 0;
-            info.flags = 0;
+            info.bits = 0;
+            info.s = info.g = 0;
+            info.vslot = -1;
             const TileRef r = tile_ref(p, p.k_plane, p.v_plane, bstride, M::kTB, -1, 0, 0, 0);
             M::issue(tt, r, lane);
             return;
         }
-        if (kn > 0) walk_advance<kPre, kKeep>(p, tw, lane);
+        if (kn > 0) walk_advance<kPre, kKeep, kFold>(p, tw, lane);
         const bool first = kn == 0 || tw.j == tw.jlo;
-        const bool last = kn == n - 1 || tw.j == tw.nblk - 1;
-        info.flags = (first ? 1 : 0) | (last ? 2 : 0) | (kPre && tw.has_pre ? 4 : 0);
+        const bool last = kn == n - 1 || tw.j == tw.nend - 1;
+        // Where the segment's result goes: its context lies wholly in this
+        // range, or it is a piece (slot 1 if it began in this range).
+        const bool whole = tw.a_sg >= t0 && tw.a_sg + (tw.nend - tw.jlo) <= t1;
+        const int flags = (first ? SlotInfo::kFirst : 0) | (last ? SlotInfo::kLast : 0) |
+                          (kPre && tw.has_pre ? SlotInfo::kHasPre : 0) |
+                          (whole ? SlotInfo::kWhole : 0) | (tw.a_sg > t0 ? SlotInfo::kSlot1 : 0);
         info.s = tw.s;
         info.g = tw.g;
-        info.ntiles = tw.nblk - tw.jlo;
-        info.a_sg = tw.a_sg;
+        info.vslot = -1;
         if constexpr (M::kPrefetchQ) {
             if (first) M::fetch_q(p, qq, tw.s, tw.g, lane);
         }
+        if (kFold && tw.j == tw.nblk) {
+            // The new token's tile. Its slot is in the last block, whose id the
+            // wave issued just before, unless its range starts here (then
+            // nothing is in flight yet to wait behind).
+            const int id = kn > 0 ? tw.last_id
+                                  : __builtin_amdgcn_readfirstlane(
+                                        p.block_tables[static_cast<size_t>(tw.s) * p.max_blocks +
+                                                       tw.nblk - 1]);
+            const bool ok = static_cast<uint32_t>(id) < static_cast<uint32_t>(p.num_blocks);
+            const size_t row = (static_cast<size_t>(tw.s) * p.num_kv_heads + tw.g) * (D * 2);
+            TileRef r;
+            r.k = tile_rsrc(p.new_k + row, ok ? D * 2 : 0);
+            r.v = tile_rsrc(p.new_v + row, ok ? D * 2 : 0);
+            info.bits = flags | (ok ? 1 : 0);  // no slot: the token is not in the context
+            info.vslot = ok ? id * 16 + (tw.L & 15) : -1;  // position L - 1 of the context
+            M::issue(tt, r, lane);
+            return;
+        }
         const uint8_t* kpl = p.k_plane + static_cast<size_t>(tw.g) * M::kTB;
         const uint8_t* vpl = p.v_plane + static_cast<size_t>(tw.g) * M::kTB;
-        const TileRef r = tile_ref(p, kpl, vpl, bstride, M::kTB, walk_id(p, tw, lane), tw.j * 16,
-                                   tw.L, tw.lo);
-        info.nvalid = r.nvalid;
-        info.nlo = r.nlo;
+        const int id = walk_id(p, tw, lane);
+        if constexpr (kFold) tw.last_id = id;
+        const TileRef r = tile_ref(p, kpl, vpl, bstride, M::kTB, id, tw.j * 16, tw.L, tw.lo);
+        info.bits = flags | r.nvalid | (r.nlo << 5);
         M::issue(tt, r, lane, kKeep && tw.j < tw.keep);
     };
 
@@ -461,44 +542,50 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
 #pragma unroll
         for (int x = 0; x < NBUF; ++x) {
             const SlotInfo cur = si[x];
-            if (cur.flags & 1) {
+            const int cnv = cur.nvalid(), cnl = cur.nlo();
+            if (cur.bits & SlotInfo::kFirst) {
                 if constexpr (M::kPrefetchQ)
                     q = qring[x];
                 else
                     M::fetch_q_lds(p, st, cur.s, cur.g, lane);
             }
-            const bool full = cur.nvalid == 16 && cur.nlo == 0;
+            if (kFold && cur.vslot >= 0)
+                M::store_new(p, tr[x],
+                             static_cast<int64_t>(cur.vslot >> 4) * bstride +
+                                 static_cast<int64_t>(cur.g) * M::kTB + (cur.vslot & 15) * (D * 2),
+                             lane);
+            const bool full = cnv == 16 && cnl == 0;
             if constexpr (M::kSplit) {
                 // First half, then the slot's refill, then the second half.
                 f32x4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
                 if (full)
                     sacc = M::template front<false>(st, tr[x], 16, 0, lane);
-                else if (cur.nvalid > 0)
-                    sacc = M::template front<true>(st, tr[x], cur.nvalid, cur.nlo, lane);
+                else if (cnv > 0)
+                    sacc = M::template front<true>(st, tr[x], cnv, cnl, lane);
                 issue(tr[x], si[x], qring[M::kPrefetchQ ? x : 0], k0 + x + NBUF);
                 if (full)
                     M::template back<false>(st, sacc, 16, 0, p.scale_log2, lane);
-                else if (cur.nvalid > 0)
-                    M::template back<true>(st, sacc, cur.nvalid, cur.nlo, p.scale_log2, lane);
+                else if (cnv > 0)
+                    M::template back<true>(st, sacc, cnv, cnl, p.scale_log2, lane);
             } else {
                 if (full)
                     M::template consume<false>(st, tr[x], 16, 0, q, p.scale_log2, lane);
-                else if (cur.nvalid > 0)
-                    M::template consume<true>(st, tr[x], cur.nvalid, cur.nlo, q, p.scale_log2,
+                else if (cnv > 0)
+                    M::template consume<true>(st, tr[x], cnv, cnl, q, p.scale_log2,
                                               lane);
             }
-            if (cur.flags & 2) {
+            if (cur.bits & SlotInfo::kLast) {
                 // End of a segment: write the output, or the partial of a split context.
                 M::finish(st);
-                if (cur.a_sg >= t0 && cur.a_sg + cur.ntiles <= t1) {
-                    if (kPre && (cur.flags & 4))  // the merge folds in the prefix partial
+                if (cur.bits & SlotInfo::kWhole) {
+                    if (kPre && (cur.bits & SlotInfo::kHasPre))  // the merge folds that in
                         M::store_partial(p.suf + static_cast<size_t>(cur.s * p.num_kv_heads + cur.g) *
                                                      G * SS,
                                          st, lane);
                     else
                         M::store_out(p, st, cur.s, cur.g, lane);
                 } else {  // split context: slot 0 if it began before this range, else 1
-                    const int slot = (cur.a_sg <= t0) ? 0 : 1;
+                    const int slot = (cur.bits & SlotInfo::kSlot1) ? 1 : 0;
                     M::store_partial(p.slots + static_cast<size_t>(w * 2 + slot) * G * SS, st, lane);
                 }
                 M::reset(st);
@@ -527,13 +614,15 @@ __global__ __launch_bounds__(256) void balanced_merge_kernel(const DecodeParams 
     int64_t total = 0, before = 0;  // tiles per head of the batch, and of sequences < s
     for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
         const int jj = c0 + lane;
-        const int nb = jj < p.num_seqs ? pass_tiles(p, seq_tokens(p, jj), pre_of(p, jj)) : 0;
+        const int nb = jj < p.num_seqs ? pass_tiles(p, seq_tokens(p, jj), pre_of(p, jj)) +
+                                             (p.fold_new ? new_of(p, jj) : 0)
+                                       : 0;
         total += wave_sum(nb);
         before += wave_sum(jj < s ? nb : 0);
     }
     const int pre = pre_of(p, s);
     const bool has_pre = pre > 0;
-    const int nblk = pass_tiles(p, seq_tokens(p, s), pre);
+    const int nblk = pass_tiles(p, seq_tokens(p, s), pre) + (p.fold_new ? new_of(p, s) : 0);
     uint16_t* out = static_cast<uint16_t*>(p.out) +
                     (static_cast<size_t>(s) * p.num_q_heads + g * G) * D;
     const int t = threadIdx.x;

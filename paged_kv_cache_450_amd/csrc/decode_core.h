@@ -62,7 +62,20 @@ struct DecodeParams {
     // other sequences of the batch share, with the caching load policy, so
     // that the sharers' repeated reads can hit the L2 instead of HBM.
     const int32_t* keep_blocks;    // [B]
+    // Balanced pass of a fused step (new_k / new_v set): a sequence whose
+    // last position is the new token reads its blocks without that position
+    // and the token itself as one more tile, taken from the source rows; the
+    // wave that reads that tile stores the rows to the token's slot.
+    int32_t fold_new;
 };
+
+// 1 when the last position of sequence j (its clamped length L) is the new
+// token a fused step stores: L >= 1 and the context is not clamped.
+__device__ __forceinline__ int new_of(const DecodeParams& p, int j) {
+    const int raw = p.context_lens[j];
+    const int L = min(max(raw, 0), min(p.max_ctx, p.max_blocks * 16));
+    return (L >= 1 && raw == L) ? 1 : 0;
+}
 
 // Leading blocks of sequence j to read with the caching policy (0 without a hint).
 __device__ __forceinline__ int keep_of(const DecodeParams& p, int j) {
