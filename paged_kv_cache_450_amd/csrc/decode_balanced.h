@@ -283,6 +283,7 @@ struct MfmaMath {
         float m, lsum;
         uint8_t* stage;
         uint8_t* qlds;
+        uint8_t* kst;  // K stage: tiles are loaded in their natural layout
     };
 
     __device__ static void fetch_q(const DecodeParams&, QT&, int, int, int) {}
@@ -301,33 +302,27 @@ struct MfmaMath {
             *reinterpret_cast<uint4*>(x.qlds + c * 1024 + lane * 16) =
                 hl < G ? v[c] : make_uint4(0u, 0u, 0u, 0u);
     }
+    // K and V in their natural layout: each load is 1 KiB of the tile.
     __device__ static void issue(TileT& t, const TileRef& r, int lane, bool kept = false) {
-        const int koff = (lane & 15) * Gm::kRowBytes + 16 * (lane >> 4);
         if (kept) {  // shared with other sequences: the caching policy (see ValuMath)
 #pragma unroll
-            for (int c = 0; c < kNk; ++c) t.k[c] = rsrc_load16_kept(r.k, koff + 64 * c);
+            for (int c = 0; c < kNk; ++c) t.k[c] = rsrc_load16_kept(r.k, lane * 16 + 1024 * c);
 #pragma unroll
             for (int i = 0; i < kNv; ++i) t.v[i] = rsrc_load16_kept(r.v, lane * 16 + 1024 * i);
             return;
         }
 #pragma unroll
-        for (int c = 0; c < kNk; ++c) t.k[c] = rsrc_load16(r.k, koff + 64 * c);
+        for (int c = 0; c < kNk; ++c) t.k[c] = rsrc_load16(r.k, lane * 16 + 1024 * c);
 #pragma unroll
         for (int i = 0; i < kNv; ++i) t.v[i] = rsrc_load16(r.v, lane * 16 + 1024 * i);
     }
-    // A new token's tile holds the token in row 0: K in lanes 0, 16, 32, 48
-    // (bytes 64c + 16 (lane / 16) of the row in load c), V in lanes
-    // 0 .. D/8 - 1 of load 0 (16 bytes each). Store it to the slot row at dst.
+    // A new token's tile holds the token in row 0: lanes 0 .. D/8 - 1 of load
+    // 0, 16 bytes each, for K and for V. Store it to the slot row at dst.
     __device__ static void store_new(const DecodeParams& p, const TileT& t, int64_t dst,
                                      int lane) {
-        if ((lane & 15) == 0) {
-#pragma unroll
-            for (int c = 0; c < kNk; ++c)
-                *reinterpret_cast<uint4*>(const_cast<uint8_t*>(p.k_plane) + dst + 64 * c +
-                                          16 * (lane >> 4)) = t.k[c];
-        }
-        if (lane < Gm::kRowBytes / 16)
-            *reinterpret_cast<uint4*>(const_cast<uint8_t*>(p.v_plane) + dst + lane * 16) = t.v[0];
+        if (lane >= Gm::kRowBytes / 16) return;
+        *reinterpret_cast<uint4*>(const_cast<uint8_t*>(p.k_plane) + dst + lane * 16) = t.k[0];
+        *reinterpret_cast<uint4*>(const_cast<uint8_t*>(p.v_plane) + dst + lane * 16) = t.v[0];
     }
     __device__ static void reset(State& x) {
 #pragma unroll
@@ -339,11 +334,11 @@ struct MfmaMath {
     __device__ static void consume(State& x, const TileT& t, int nvalid, int nlo, const QT&,
                                    float sscale, int lane) {
         mfma_consume<KV, D, kPartial>(t, nvalid, nlo, QLds<D>{x.qlds}, x.o, x.m, x.lsum, sscale,
-                                      x.stage, lane);
+                                      x.stage, lane, x.kst);
     }
     template <bool kPartial>
     __device__ static f32x4_t front(State& x, const TileT& t, int nvalid, int nlo, int lane) {
-        return mfma_front<KV, D, kPartial>(t, nvalid, nlo, QLds<D>{x.qlds}, x.stage, lane);
+        return mfma_front<KV, D, kPartial>(t, nvalid, nlo, QLds<D>{x.qlds}, x.stage, lane, x.kst);
     }
     template <bool kPartial>
     __device__ static void back(State& x, f32x4_t sacc, int nvalid, int nlo, float sscale,
@@ -470,10 +465,12 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
 
     __shared__ __attribute__((aligned(16))) uint8_t stage_all[4][MfmaGeo<D>::kStage];
     __shared__ __attribute__((aligned(16))) uint8_t q_all[4][G > 1 ? MfmaGeo<D>::kNk * 1024 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t kst_all[4][G > 1 ? MfmaGeo<D>::kStage : 16];
     typename M::State st;
     if constexpr (G > 1) {
         st.stage = stage_all[wv_in];
         st.qlds = q_all[wv_in];
+        st.kst = kst_all[wv_in];
     }
     M::reset(st);
     typename M::QT q;

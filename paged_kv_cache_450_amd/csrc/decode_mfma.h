@@ -83,19 +83,50 @@ struct QLds {
     }
 };
 
+// K loaded in its natural layout (lane l of load c: bytes 1024c + 16l of the
+// tile, as V is) into the QK product's A operand (token l % 16, dims
+// 32c + 8 (l / 16)) through the wave's LDS K stage: rows at pitch kPitch,
+// which keeps both the row writes and the column reads free of bank
+// conflicts. A load of natural K touches whole 128-byte lines (8 per load)
+// where the operand layout's own loads touch 64 bytes of 16 lines each.
+template <int D>
+__device__ __forceinline__ void k_operand(const MfmaTile<D>& t, uint8_t* kst,
+                                          uint4 (&a)[MfmaGeo<D>::kNk], int lane) {
+    using Gm = MfmaGeo<D>;
+#pragma unroll
+    for (int c = 0; c < Gm::kNk; ++c) {
+        const int byte = 1024 * c + 16 * lane;
+        *reinterpret_cast<uint4*>(kst + (byte / Gm::kRowBytes) * Gm::kPitch +
+                                  byte % Gm::kRowBytes) = t.k[c];
+    }
+#pragma unroll
+    for (int c = 0; c < Gm::kNk; ++c)
+        a[c] = *reinterpret_cast<const uint4*>(kst + (lane & 15) * Gm::kPitch + 64 * c +
+                                               16 * (lane >> 4));
+}
+
 // The first half of a tile's math, everything that reads the tile's
 // registers: the scores S^T = K Q^T of head hl for tokens 4*kg + r (returned),
 // and V staged in LDS (natural layout, padded rows; tokens outside
 // [nlo, nvalid) become zeros so that stale or NaN bytes never meet a zero
 // probability). Once it returns, the tile's registers may be refilled.
-// kPartial: the masked form.
+// kPartial: the masked form. kst: NULL when K was loaded in the operand
+// layout, else the wave's K stage (K loaded in its natural layout).
 template <int KV, int D, bool kPartial, class QSrc>
 __device__ __forceinline__ f32x4_t mfma_front(const MfmaTile<D>& t, int nvalid, int nlo,
-                                              const QSrc& qsrc, uint8_t* stage, int lane) {
+                                              const QSrc& qsrc, uint8_t* stage, int lane,
+                                              uint8_t* kst = nullptr) {
     using Gm = MfmaGeo<D>;
     f32x4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (kst != nullptr) {
+        uint4 a[Gm::kNk];
+        k_operand<D>(t, kst, a, lane);
 #pragma unroll
-    for (int c = 0; c < Gm::kNk; ++c) sacc = mfma_qk<KV>(t.k[c], qsrc.get(c, lane), sacc);
+        for (int c = 0; c < Gm::kNk; ++c) sacc = mfma_qk<KV>(a[c], qsrc.get(c, lane), sacc);
+    } else {
+#pragma unroll
+        for (int c = 0; c < Gm::kNk; ++c) sacc = mfma_qk<KV>(t.k[c], qsrc.get(c, lane), sacc);
+    }
     constexpr int kLanesPerRow = Gm::kRowBytes / 16;
 #pragma unroll
     for (int i = 0; i < Gm::kNv; ++i) {
@@ -184,8 +215,9 @@ template <int KV, int D, bool kPartial, class QSrc>
 __device__ __forceinline__ void mfma_consume(const MfmaTile<D>& t, int nvalid, int nlo,
                                              const QSrc& qsrc,
                                              f32x4_t (&o)[MfmaGeo<D>::kNd], float& m, float& lsum,
-                                             float sscale, uint8_t* stage, int lane) {
-    const f32x4_t sacc = mfma_front<KV, D, kPartial>(t, nvalid, nlo, qsrc, stage, lane);
+                                             float sscale, uint8_t* stage, int lane,
+                                             uint8_t* kst = nullptr) {
+    const f32x4_t sacc = mfma_front<KV, D, kPartial>(t, nvalid, nlo, qsrc, stage, lane, kst);
     mfma_back<KV, D, kPartial>(sacc, nvalid, nlo, o, m, lsum, sscale, stage, lane);
 }
 
