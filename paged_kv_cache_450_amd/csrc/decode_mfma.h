@@ -264,13 +264,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
     float m = -INFINITY, lsum = 0.0f;
 
     __shared__ __attribute__((aligned(16))) uint8_t stage_all[NW][Gm::kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t kst_all[NW][Gm::kStage];
     uint8_t* stage = stage_all[w];
+    uint8_t* kst = kst_all[w];
 
     const uint8_t* kpl = p.k_plane + static_cast<size_t>(g) * TB;
     const uint8_t* vpl = p.v_plane + static_cast<size_t>(g) * TB;
     const size_t bstride = static_cast<size_t>(p.num_kv_heads) * TB;
-    const int koff = hl * Gm::kRowBytes + 16 * kg;  // + 64*c: token hl, dims 32c + 8*kg
-    const int voff = lane * 16;                     // + 1024*i: natural rows
+    const int voff = lane * 16;  // + 1024*i: K and V in natural rows (K to its operand via kst)
 
     MfmaTile<D> t[NBUF];
     int nv[NBUF], nl[NBUF];
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
         nvalid = r.nvalid;
         nlo = r.nlo;
 #pragma unroll
-        for (int c = 0; c < NK; ++c) tt.k[c] = rsrc_load16(r.k, koff + 64 * c);
+        for (int c = 0; c < NK; ++c) tt.k[c] = rsrc_load16(r.k, voff + 1024 * c);
 #pragma unroll
         for (int i = 0; i < NV; ++i) tt.v[i] = rsrc_load16(r.v, voff + 1024 * i);
     };
@@ -291,9 +292,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeParams
 #pragma unroll
         for (int x = 0; x < NBUF; ++x) {
             if (nv[x] == 16 && nl[x] == 0)
-                mfma_consume<KV, D, false>(t[x], 16, 0, qr, o, m, lsum, sscale, stage, lane);
+                mfma_consume<KV, D, false>(t[x], 16, 0, qr, o, m, lsum, sscale, stage, lane, kst);
             else
-                mfma_consume<KV, D, true>(t[x], nv[x], nl[x], qr, o, m, lsum, sscale, stage, lane);
+                mfma_consume<KV, D, true>(t[x], nv[x], nl[x], qr, o, m, lsum, sscale, stage, lane,
+                                          kst);
             issue(t[x], nv[x], nl[x], k0 + x + NBUF);
         }
     }
