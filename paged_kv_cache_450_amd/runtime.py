@@ -121,12 +121,12 @@ class PagedKVCache:
 # shared_prefix="auto" takes the prefix kernel (paged_attn_decode_prefix);
 # below it, the shared blocks are read through the L2 by the balanced pass
 # (paged_attn_decode_prefix_l2). Measured on MI355X (64 sharers, 64 / 8 heads
-# x 128, bf16, per call): 132 MB repeated (512 shared tokens): plain pass
-# 157.0 us, L2 form 150.0 us, prefix kernel 160.9 us; 264 MB (1024): 163.6,
-# 153.7, 153.4 us; 528 MB (2048): L2 form 162.9, prefix kernel 143.8 us. The
-# prefix kernel costs about 10 us per call whatever it reads; the L2 form costs
-# nothing extra but its repeats still cross the fabric when they miss the L2.
-PREFIX_AUTO_BYTES = 250_000_000
+# x 128, bf16, fused step, per call), L2 form against prefix kernel: 264 MB
+# repeated (1024 shared tokens) 136.0 against 156.7 us; 528 MB (2048) 144.8
+# against 146.1 us; 1057 MB (4096) 194.2 against 148.8 us. The prefix kernel
+# costs 10-20 us per call whatever it reads; the L2 form costs nothing extra
+# but its repeats still cross the fabric when they miss the L2.
+PREFIX_AUTO_BYTES = 700_000_000
 
 
 def prefix_repeated_bytes(plan, desc) -> int:
