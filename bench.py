@@ -57,24 +57,24 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {  # traffic_key -> counters of the decode call's streaming kernel
     "llama13b_layer": {  # FETCH 367,274.2 KiB x 1.99992 + WRITE 960.0 KiB
-        "kernel": "valu", "bytes": 753_129_040,
-        "sources_sha256": "2ade13fbe4e3465a5c62017d73ec394327a2df8a85a3e1c709e1216052dad356",
+        "kernel": "valu", "bytes": 753_131_282,
+        "sources_sha256": "b7b39013729474c6e814d600f738568f4c04842e5db5b232bbc695a866c77cea",
         "summary": "profiles/decode_kernel_llama13b_layer.md"},
-    "longctx_fp8": {  # FETCH 715,839.1 KiB x 1.99998 + WRITE 5,818.4 KiB
-        "kernel": "valu", "bytes": 1_471_978_298,
-        "sources_sha256": "2ade13fbe4e3465a5c62017d73ec394327a2df8a85a3e1c709e1216052dad356",
+    "longctx_fp8": {  # FETCH 715,842.6 KiB x 1.99998 + WRITE 5,818.6 KiB
+        "kernel": "valu", "bytes": 1_471_985_629,
+        "sources_sha256": "b7b39013729474c6e814d600f738568f4c04842e5db5b232bbc695a866c77cea",
         "summary": "profiles/decode_kernel_longctx_fp8.md"},
-    "gqa_prefix/shared_prefix_l2": {  # streaming kernel: FETCH 369,434.8 KiB x 1.99995 + WRITE 12,224.2 KiB
-        "kernel": "balanced", "bytes": 769_103_069,
-        "sources_sha256": "3fd87e013c90413ea4a59b975feee15cb2f34435c8a717880ae736795fbb6824",
+    "gqa_prefix/shared_prefix_l2": {  # streaming kernel: FETCH 369,781.4 KiB x 1.99995 + WRITE 12,776.5 KiB
+        "kernel": "balanced", "bytes": 770_377_513,
+        "sources_sha256": "878c5fec664e94a050dde2e3359b0e3350d60ba693e24875de173a5ffaecbe35",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
-    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 358,288.6 KiB x 1.99992 + WRITE 12,413.5 KiB
-        "kernel": "prefix", "bytes": 746_457_042,
-        "sources_sha256": "25cec0b9e8ef04c5980bef970fcfeb0709303dba994c70ab7625e9eaaa52a7ba",
+    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 357,642.9 KiB x 1.99992 + WRITE 12,421.7 KiB
+        "kernel": "prefix", "bytes": 745_143_907,
+        "sources_sha256": "efe167476ef2621d07430e4dd5d3a469597dbef07715e8fb5b05f2a5bda695e3",
         "summary": "profiles/prefix_kernel_gqa_prefix.md"},
-    "7b_32layer": {  # streaming kernel: FETCH 1,049,128.5 KiB x 1.99998 + WRITE 512.0 KiB
-        "kernel": "balanced", "bytes": 2_149_112_831,
-        "sources_sha256": "3fd87e013c90413ea4a59b975feee15cb2f34435c8a717880ae736795fbb6824",
+    "7b_32layer": {  # streaming kernel: FETCH 1,049,675.0 KiB x 1.99998 + WRITE 1,536.0 KiB
+        "kernel": "balanced", "bytes": 2_151_280_612,
+        "sources_sha256": "878c5fec664e94a050dde2e3359b0e3350d60ba693e24875de173a5ffaecbe35",
         "summary": "profiles/decode_balanced_kernel_7b_32layer.md"},
 }
 
