@@ -158,8 +158,10 @@ def kv_pool_create(desc: PoolDesc, device_base, nbytes: int):
     return out
 
 
-def kv_pool_destroy(pool) -> None:
-    lib.kv_pool_destroy(pool)
+def kv_pool_destroy(pool, _destroy=lib.kv_pool_destroy) -> None:
+    # The library function is bound at definition: a pool finalised at
+    # interpreter exit may run after this module's globals are cleared.
+    _destroy(pool)
 
 
 def kv_pool_num_free(pool) -> int:
