@@ -22,7 +22,10 @@ using namespace pkv::dev;
 // PV product, so the probabilities never move between lanes; the running max
 // is shared by the four lanes of a head with two xor-shuffles, and the O^T
 // accumulator of a lane belongs to its own head, so rescaling is lane-local.
-// K is loaded straight into the A-operand layout (token l % 16, 8 dims).
+// The A operand of the QK product wants lane l to hold token l % 16, dims
+// 32c + 8 (l / 16): the streaming kernels load K in its natural layout (1 KiB
+// per load, whole 128-byte lines) and move it there through an LDS K stage
+// (k_operand); the prefix kernel loads it in the operand layout directly.
 // V^T, the A operand of the PV product, needs each lane to hold 4 tokens of
 // one dim: V goes through a per-wave LDS tile in its natural layout, and
 // ds_read_tr16_b64 returns the transposed 4 x 16-bit groups (one read per 16
