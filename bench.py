@@ -43,7 +43,8 @@ BS = 16
 # HBM bytes per decode launch from rocprofv3 counter passes: FETCH_SIZE x 2.000
 # + WRITE_SIZE x 1.000, the factors read off a copy of known size (1 GiB read
 # and written) in the same runs. A figure is reported only while the sources
-# of the kernel it was measured on hash to what they were then.
+# of the kernel it was measured on hash to what they were then (their code:
+# comments and whitespace are left out of the hash).
 _CSRC = "paged_kv_cache_450_amd/csrc/"
 KERNEL_SOURCES = {
     "valu": tuple(_CSRC + f for f in ("decode.hip", "decode_core.h", "decode_valu.h", "device.h",
@@ -58,25 +59,33 @@ KERNEL_SOURCES = {
 MEASURED_TRAFFIC = {  # traffic_key -> counters of the decode call's streaming kernel
     "llama13b_layer": {  # FETCH 367,274.2 KiB x 1.99992 + WRITE 960.0 KiB
         "kernel": "valu", "bytes": 753_131_282,
-        "sources_sha256": "b7b39013729474c6e814d600f738568f4c04842e5db5b232bbc695a866c77cea",
+        "sources_sha256": "7e49de652140bfcbfd46f430d1777b2635fb260c9202d62a45fc3e2c8adc309a",
         "summary": "profiles/decode_kernel_llama13b_layer.md"},
     "longctx_fp8": {  # FETCH 715,842.6 KiB x 1.99998 + WRITE 5,818.6 KiB
         "kernel": "valu", "bytes": 1_471_985_629,
-        "sources_sha256": "b7b39013729474c6e814d600f738568f4c04842e5db5b232bbc695a866c77cea",
+        "sources_sha256": "7e49de652140bfcbfd46f430d1777b2635fb260c9202d62a45fc3e2c8adc309a",
         "summary": "profiles/decode_kernel_longctx_fp8.md"},
     "gqa_prefix/shared_prefix_l2": {  # streaming kernel: FETCH 369,781.4 KiB x 1.99995 + WRITE 12,776.5 KiB
         "kernel": "balanced", "bytes": 770_377_513,
-        "sources_sha256": "878c5fec664e94a050dde2e3359b0e3350d60ba693e24875de173a5ffaecbe35",
+        "sources_sha256": "55502a9f10f58fd8bffe0b2a58d8cc09b3dd1af5cf2545f269eab6e77a2065ee",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
     "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 357,642.9 KiB x 1.99992 + WRITE 12,421.7 KiB
         "kernel": "prefix", "bytes": 745_143_907,
-        "sources_sha256": "efe167476ef2621d07430e4dd5d3a469597dbef07715e8fb5b05f2a5bda695e3",
+        "sources_sha256": "2cd592261635e3b6b099fa52850934a56d68841af626d2485bbfe4bc3d772796",
         "summary": "profiles/prefix_kernel_gqa_prefix.md"},
     "7b_32layer": {  # streaming kernel: FETCH 1,049,675.0 KiB x 1.99998 + WRITE 1,536.0 KiB
         "kernel": "balanced", "bytes": 2_151_280_612,
-        "sources_sha256": "878c5fec664e94a050dde2e3359b0e3350d60ba693e24875de173a5ffaecbe35",
+        "sources_sha256": "55502a9f10f58fd8bffe0b2a58d8cc09b3dd1af5cf2545f269eab6e77a2065ee",
         "summary": "profiles/decode_balanced_kernel_7b_32layer.md"},
 }
+
+
+def _code_only(text: str) -> str:
+    """C++ source without its comments, whitespace runs collapsed."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
 
 
 def sources_sha256(kernel: str) -> str:
@@ -84,8 +93,8 @@ def sources_sha256(kernel: str) -> str:
     root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(root, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(root, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
