@@ -392,10 +392,11 @@ pkv_status paged_attn_decode(const pkv_pool* pool, int32_t layer, const void* q,
  * append launch. The balanced single pass does the same for any group size:
  * it reads each context's blocks without the new token's position and the
  * token as one more tile from new_k / new_v, whose wave also writes its slot.
+ * (beside a shared-prefix pass too: a plan's shared blocks end before the
+ * block of each member's last token, so that pass never reads a new slot).
  * The other forms (grouped heads on a 16-bit cache per sequence or split-K,
- * FP8 with four or eight query heads per kv head, and the balanced pass with
- * a shared-prefix pass, which reads the pool first) run the append as a
- * kernel of its own first, on the same stream.
+ * FP8 with four or eight query heads per kv head) run the append as a kernel
+ * of its own first, on the same stream.
  * new_k, new_v: device [num_seqs][num_kv_heads][head_dim] of src_dtype, which
  *   must equal q_dtype (for a 16-bit cache, also the cache dtype); 16-byte
  *   aligned.

@@ -206,7 +206,8 @@ hipError_t launch_balanced_as(DecodeParams prm, int cus, hipStream_t st) {
 template <class M, int KV, int D, int NBUF>
 hipError_t launch_balanced(const DecodeParams& prm, int cus, hipStream_t st) {
     if (prm.pre_blocks != nullptr)
-        return launch_balanced_as<M, KV, D, NBUF, true, false, false>(prm, cus, st);
+        return prm.fold_new ? launch_balanced_as<M, KV, D, NBUF, true, false, true>(prm, cus, st)
+                            : launch_balanced_as<M, KV, D, NBUF, true, false, false>(prm, cus, st);
     if (prm.keep_blocks != nullptr)
         return prm.fold_new ? launch_balanced_as<M, KV, D, NBUF, false, true, true>(prm, cus, st)
                             : launch_balanced_as<M, KV, D, NBUF, false, true, false>(prm, cus, st);
@@ -411,10 +412,10 @@ pkv_status decode_impl(const char* fn, const pkv_pool* pool, int32_t layer, cons
             }
             // The fused step's new tokens: each is a tile of its own in the
             // streaming kernel, whose wave also stores it (fold_new; the slot
-            // travels as block id * 16 + position in 31 bits); with a prefix
-            // pass, which reads the pool first, an append launch stores them
-            // ahead of it.
-            if (new_k != nullptr && !with_pre && d.num_blocks < (1 << 27)) {
+            // travels as block id * 16 + position in 31 bits). A prefix pass
+            // never reads a new token's slot: a plan's shared blocks end
+            // before the block of each member's last token.
+            if (new_k != nullptr && d.num_blocks < (1 << 27)) {
                 prm.fold_new = 1;
             } else if (new_k != nullptr) {
                 const pkv_status sa = append_first(

@@ -391,7 +391,6 @@ template <class M, int KV, int D, int NBUF, bool kPre = false, bool kKeep = fals
           bool kFold = false>
 __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodeParams p) {
     static_assert(!(kPre && kKeep), "one shared-prefix form at a time");
-    static_assert(!(kPre && kFold), "the prefix pass reads the pool before the new tokens");
     constexpr int G = M::kG;
     constexpr int SS = SlotGeoB<D>::kStride;
     const int lane = threadIdx.x & 63;
