@@ -57,25 +57,25 @@ KERNEL_SOURCES = {
                                          "device.h", "common.h")),
 }
 MEASURED_TRAFFIC = {  # traffic_key -> counters of the decode call's streaming kernel
-    "llama13b_layer": {  # FETCH 367,274.2 KiB x 1.99992 + WRITE 960.0 KiB
-        "kernel": "valu", "bytes": 753_131_282,
-        "sources_sha256": "7e49de652140bfcbfd46f430d1777b2635fb260c9202d62a45fc3e2c8adc309a",
+    "llama13b_layer": {  # FETCH 367,280.2 KiB x 1.99991 + WRITE 960.0 KiB
+        "kernel": "valu", "bytes": 753_140_815,
+        "sources_sha256": "032b39f19f2d7049207454d8c0d5e9f62308114346691d549f90c7ce4399885f",
         "summary": "profiles/decode_kernel_llama13b_layer.md"},
-    "longctx_fp8": {  # FETCH 715,842.6 KiB x 1.99998 + WRITE 5,818.6 KiB
-        "kernel": "valu", "bytes": 1_471_985_629,
-        "sources_sha256": "7e49de652140bfcbfd46f430d1777b2635fb260c9202d62a45fc3e2c8adc309a",
+    "longctx_fp8": {  # FETCH 715,839.1 KiB x 1.99998 + WRITE 5,818.7 KiB
+        "kernel": "valu", "bytes": 1_471_978_577,
+        "sources_sha256": "032b39f19f2d7049207454d8c0d5e9f62308114346691d549f90c7ce4399885f",
         "summary": "profiles/decode_kernel_longctx_fp8.md"},
-    "gqa_prefix/shared_prefix_l2": {  # streaming kernel: FETCH 369,781.4 KiB x 1.99995 + WRITE 12,776.5 KiB
-        "kernel": "balanced", "bytes": 770_377_513,
-        "sources_sha256": "55502a9f10f58fd8bffe0b2a58d8cc09b3dd1af5cf2545f269eab6e77a2065ee",
+    "gqa_prefix/shared_prefix_l2": {  # streaming kernel: FETCH 369,781.5 KiB x 1.99995 + WRITE 12,776.6 KiB
+        "kernel": "balanced", "bytes": 770_378_449,
+        "sources_sha256": "12b34f65d1bfaaee01c52a66d0c3e58b538b6a4783548a75cef40bc953a8acb8",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
-    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 357,642.9 KiB x 1.99992 + WRITE 12,421.7 KiB
-        "kernel": "prefix", "bytes": 745_143_907,
-        "sources_sha256": "2cd592261635e3b6b099fa52850934a56d68841af626d2485bbfe4bc3d772796",
+    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 357,916.2 KiB x 1.99992 + WRITE 12,935.0 KiB
+        "kernel": "prefix", "bytes": 746_228_692,
+        "sources_sha256": "bf6319c4577c19cafb5bc86585ed360b9dd7f9d6fbbb0f16ab9a4ac47b8313e2",
         "summary": "profiles/prefix_kernel_gqa_prefix.md"},
-    "7b_32layer": {  # streaming kernel: FETCH 1,049,675.0 KiB x 1.99998 + WRITE 1,536.0 KiB
-        "kernel": "balanced", "bytes": 2_151_280_612,
-        "sources_sha256": "55502a9f10f58fd8bffe0b2a58d8cc09b3dd1af5cf2545f269eab6e77a2065ee",
+    "7b_32layer": {  # streaming kernel: FETCH 1,049,670.5 KiB x 1.99998 + WRITE 1,536.0 KiB
+        "kernel": "balanced", "bytes": 2_151_271_397,
+        "sources_sha256": "12b34f65d1bfaaee01c52a66d0c3e58b538b6a4783548a75cef40bc953a8acb8",
         "summary": "profiles/decode_balanced_kernel_7b_32layer.md"},
 }
 
