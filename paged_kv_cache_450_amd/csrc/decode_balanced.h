@@ -39,7 +39,7 @@ using namespace pkv::dev;
 // heads, later blocks rotate through a second pair of 64-id chunks. A
 // sequence's tiles are its blocks jlo .. nblk-1: jlo is 0, or a sliding
 // window's first block, or the first block after those a shared-prefix pass
-// covers.
+// covers; with kFold, the new token's tile (index nblk) follows them.
 struct TileWalk {
     int s, g, j, nblk;   // current tile: sequence, kv head, block; blocks end at nblk
     int jlo, lo;         // first block read, first token attended (sliding window)
