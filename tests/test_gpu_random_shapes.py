@@ -1,0 +1,91 @@
+"""Seeded random shapes through every decode form, against the oracle.
+
+Each case draws a batch (1-48 sequences, 1-2 layers), a head layout (kv heads
+1-8, group 1, 2, 4 or 8, head_dim 64 or 128), a cache dtype (fp16, bf16 or
+FP8 E4M3 with an fp16 or bf16 query), a length range, and a decode form the
+library offers for it: the per-sequence or the balanced single pass, split-K
+at 16-256 tokens, the shared-prefix kernel pass or the L2 form over even
+sequences that share a prompt, each as the fused step or as separate append
+and decode calls. The whole pool is compared byte for byte after the appends
+and every output of every layer against the oracle. The cases are fixed by
+their seeds, so a failure names a reproducible case."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests import harness as H
+
+def say(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture
+def _gpu(require_gpu):
+    yield
+    torch.cuda.synchronize()
+
+
+def draw_case(seed: int):
+    """One configuration and its decode form, from the seed alone."""
+    r = np.random.default_rng(np.random.PCG64(1_000_003 + seed))
+    kv = ["f16", "bf16", "e4m3"][r.integers(3)]
+    q = kv if kv != "e4m3" else ["f16", "bf16"][r.integers(2)]
+    hkv = int(r.choice([1, 2, 4, 8]))
+    g = int(r.choice([1, 2, 4, 8]))
+    dim = int(r.choice([64, 128]))
+    batch = int(r.integers(1, 49))
+    layers = int(r.integers(1, 3))
+    hi = int(r.choice([16, 40, 300, 1200]))
+    lo = int(r.integers(1, hi + 1)) if r.random() < 0.3 else 1
+    ps = 0 if r.random() < 0.5 else int(r.choice([16, 64, 256]))
+    balanced = kv != "e4m3" and ps == 0 and r.random() < 0.6
+    share = 0
+    shared = None
+    if balanced and batch >= 4 and r.random() < 0.5:
+        share = int(r.choice([16, 32, 64]))
+        shared = [True, "l2"][r.integers(2)]
+    fused = bool(r.random() < 0.7)
+    cfg = W.Config(f"rand{seed}", layers, batch, hkv * g, hkv, dim, kv, q, ("uniform", lo, hi),
+                   share_prefix_tokens=share, partition_size=ps, balanced=balanced)
+    return cfg, fused, shared
+
+
+CASES = list(range(64))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", CASES)
+def test_random_shape_matches_oracle(seed, _gpu):
+    from tests.test_gpu_parity import check_bookkeeping, check_layers
+
+    cfg, fused, shared = draw_case(seed)
+    say(f"random shape {seed}: B={cfg.batch} layers={cfg.layers} Hq={cfg.q_heads} "
+        f"Hkv={cfg.kv_heads} D={cfg.head_dim} kv={cfg.kv_dtype} q={cfg.q_dtype} "
+        f"lens={cfg.lengths} ps={cfg.partition_size} balanced={cfg.balanced} "
+        f"share={cfg.share_prefix_tokens} shared={shared} fused={fused}")
+    side = H.build_product(cfg, seed=seed, fused=fused, shared_prefix=shared)
+    torch.cuda.synchronize()
+    o = H.oracle_bookkeeping(cfg, seed)
+    check_bookkeeping(side, o)
+    check_layers(cfg, side, o, list(range(cfg.batch)), range(cfg.layers), whole_pool=True)
+
+
+def test_cases_cover_every_form():
+    """The fixed seeds reach each form at least once (host only)."""
+    forms = set()
+    for seed in CASES:
+        cfg, fused, shared = draw_case(seed)
+        forms.add(("fp8" if cfg.kv_dtype == "e4m3" else "16bit",
+                   "splitk" if cfg.partition_size else
+                   ("balanced" if cfg.balanced else "perseq")))
+        if shared is not None:
+            forms.add(("shared", str(shared)))
+        forms.add(("fused", fused))
+    need = {("16bit", "perseq"), ("16bit", "balanced"), ("16bit", "splitk"),
+            ("fp8", "perseq"), ("fp8", "splitk"), ("shared", "True"), ("shared", "l2"),
+            ("fused", True), ("fused", False)}
+    assert need <= forms, need - forms
