@@ -20,7 +20,6 @@ import numpy as np
 import torch
 
 import workloads as W
-from oracle import allocator as oalloc
 from oracle import attention as oattn
 from oracle import pool as opool
 
