@@ -114,6 +114,12 @@ def traffic_key(cfg, w, args=None) -> str:
         key += "/shared_prefix_l2"
     if args is not None and args.prefix_tokens:
         key += f"/prompt{args.prefix_tokens}"
+    import workloads as W
+    base = W.CONFIGS.get(cfg.name, cfg)
+    if cfg.q_heads != base.q_heads:
+        key += f"/hq{cfg.q_heads}"
+    if cfg.balanced != base.balanced:
+        key += "/balanced" if cfg.balanced else "/per-sequence"
     return key
 
 
@@ -908,6 +914,12 @@ def main(argv=None):
                     help="read blocks that several sequences share once per step with the prefix "
                          "kernel (paged_attn_decode_prefix; the default when given alone), or "
                          "through the L2 in the balanced pass (l2: paged_attn_decode_prefix_l2)")
+    ap.add_argument("--q-heads", type=int, default=0, metavar="HQ",
+                    help="run the workload with HQ query heads (a multiple of its kv heads) on "
+                         "the same pool, tables and lengths: another head grouping of the same "
+                         "KV bytes")
+    ap.add_argument("--single-pass", choices=["balanced", "per-sequence"], default=None,
+                    help="the single-pass form instead of the workload's own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gather-probe", action="store_true",
                     help="also measure the rate of the decode's access pattern alone (random "
@@ -940,6 +952,14 @@ def main(argv=None):
             print(f"--prefix-tokens: workload {cfg.name} has no shared prompt", file=sys.stderr)
             return 2
         cfg = replace(cfg, share_prefix_tokens=args.prefix_tokens)
+    if args.q_heads:
+        if args.q_heads % cfg.kv_heads or args.q_heads // cfg.kv_heads not in (1, 2, 4, 8):
+            print(f"--q-heads: {args.q_heads} query heads for {cfg.kv_heads} kv heads",
+                  file=sys.stderr)
+            return 2
+        cfg = replace(cfg, q_heads=args.q_heads)
+    if args.single_pass is not None:
+        cfg = replace(cfg, balanced=args.single_pass == "balanced")
     torch.cuda.set_device(0)
     fused = not args.unfused
     first = Workload(cfg, args.seed, "cuda", args.partition_size,
