@@ -196,7 +196,7 @@ hipError_t launch_balanced_as(DecodeParams prm, int cus, hipStream_t st) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((balanced_merge_kernel<KV, D, M::kG>),
                        dim3(static_cast<uint32_t>(prm.num_kv_heads), static_cast<uint32_t>(prm.num_seqs)),
-                       dim3(256), 0, st, prm);
+                       dim3(merge_threads<D, M::kG>()), 0, st, prm);
     return hipGetLastError();
 }
 

@@ -602,8 +602,17 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
 // and the running (max, sum, output) is rescaled when a group raises the
 // maximum, so a context split over up to eight waves costs one round trip to
 // memory after the lengths.
+// Threads per workgroup: one per 4 output dims of the G heads, rounded up to
+// whole waves (one wave for a single head).
+template <int D, int G>
+constexpr int merge_threads() {
+    return (G * D / 4 + 63) / 64 * 64 < 256 ? (G * D / 4 + 63) / 64 * 64 : 256;
+}
+
 template <int KV, int D, int G>
-__global__ __launch_bounds__(256) void balanced_merge_kernel(const DecodeParams p) {
+__global__ __launch_bounds__((merge_threads<D, G>())) void balanced_merge_kernel(
+    const DecodeParams p) {
+    constexpr int NT = merge_threads<D, G>();
     constexpr int SS = SlotGeoB<D>::kStride;
     constexpr int kGroup = 8;
     const int g = blockIdx.x, s = blockIdx.y, lane = threadIdx.x & 63;
@@ -623,7 +632,7 @@ __global__ __launch_bounds__(256) void balanced_merge_kernel(const DecodeParams 
                     (static_cast<size_t>(s) * p.num_q_heads + g * G) * D;
     const int t = threadIdx.x;
     if (nblk == 0 && !has_pre) {
-        for (int idx = t; idx < G * D; idx += 256) out[idx] = 0;
+        for (int idx = t; idx < G * D; idx += NT) out[idx] = 0;
         return;
     }
     // Waves wa .. wb read pieces of this context (none when the prefix pass
@@ -643,7 +652,7 @@ __global__ __launch_bounds__(256) void balanced_merge_kernel(const DecodeParams 
         // Wave wa's piece began before its range: slot 1; waves after it: slot 0.
         slot_a = (a_sg <= range_start(total, wa, R)) ? 0 : 1;
     }
-    for (int idx = t; idx < G * D / 4; idx += 256) {
+    for (int idx = t; idx < G * D / 4; idx += NT) {
         const int h = idx / (D / 4), d = (idx % (D / 4)) * 4;
         const float* base = p.slots + static_cast<size_t>(h) * SS;
         float run_m = -INFINITY, run_l = 0.0f;
