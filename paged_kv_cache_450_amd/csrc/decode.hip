@@ -194,9 +194,11 @@ hipError_t launch_balanced_as(DecodeParams prm, int cus, hipStream_t st) {
                        dim3(prm.num_waves / 4), dim3(256), 0, st, prm);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    constexpr int kHpw = merge_heads_per_wg<D, M::kG>();
     hipLaunchKernelGGL((balanced_merge_kernel<KV, D, M::kG>),
-                       dim3(static_cast<uint32_t>(prm.num_kv_heads), static_cast<uint32_t>(prm.num_seqs)),
-                       dim3(merge_threads<D, M::kG>()), 0, st, prm);
+                       dim3(static_cast<uint32_t>((prm.num_kv_heads + kHpw - 1) / kHpw),
+                            static_cast<uint32_t>(prm.num_seqs)),
+                       dim3(merge_threads<D, M::kG>() * kHpw), 0, st, prm);
     return hipGetLastError();
 }
 

@@ -602,20 +602,28 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
 // and the running (max, sum, output) is rescaled when a group raises the
 // maximum, so a context split over up to eight waves costs one round trip to
 // memory after the lengths.
-// Threads per workgroup: one per 4 output dims of the G heads, rounded up to
-// whole waves (one wave for a single head).
+// Threads per (kv head, sequence): one per 4 output dims of the G heads,
+// rounded up to whole waves. When that is one wave, a workgroup takes four kv
+// heads of the sequence, a wave each.
 template <int D, int G>
 constexpr int merge_threads() {
     return (G * D / 4 + 63) / 64 * 64 < 256 ? (G * D / 4 + 63) / 64 * 64 : 256;
 }
+template <int D, int G>
+constexpr int merge_heads_per_wg() {
+    return merge_threads<D, G>() == 64 ? 4 : 1;
+}
 
 template <int KV, int D, int G>
-__global__ __launch_bounds__((merge_threads<D, G>())) void balanced_merge_kernel(
-    const DecodeParams p) {
+__global__ __launch_bounds__((merge_threads<D, G>() * merge_heads_per_wg<D, G>())) void
+balanced_merge_kernel(const DecodeParams p) {
     constexpr int NT = merge_threads<D, G>();
+    constexpr int HPW = merge_heads_per_wg<D, G>();
     constexpr int SS = SlotGeoB<D>::kStride;
     constexpr int kGroup = 8;
-    const int g = blockIdx.x, s = blockIdx.y, lane = threadIdx.x & 63;
+    const int g = blockIdx.x * HPW + (HPW > 1 ? static_cast<int>(threadIdx.x >> 6) : 0);
+    const int s = blockIdx.y, lane = threadIdx.x & 63;
+    if (g >= p.num_kv_heads) return;  // a whole wave: the last workgroup's spare heads
     int64_t total = 0, before = 0;  // tiles per head of the batch, and of sequences < s
     for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
         const int jj = c0 + lane;
@@ -630,7 +638,7 @@ __global__ __launch_bounds__((merge_threads<D, G>())) void balanced_merge_kernel
     const int nblk = pass_tiles(p, seq_tokens(p, s), pre) + (p.fold_new ? new_of(p, s) : 0);
     uint16_t* out = static_cast<uint16_t*>(p.out) +
                     (static_cast<size_t>(s) * p.num_q_heads + g * G) * D;
-    const int t = threadIdx.x;
+    const int t = HPW > 1 ? lane : static_cast<int>(threadIdx.x);
     if (nblk == 0 && !has_pre) {
         for (int idx = t; idx < G * D; idx += NT) out[idx] = 0;
         return;
