@@ -49,8 +49,15 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ml
     const int np = L > 0 ? (L + PS - 1) / PS : 0;
     const size_t base = (static_cast<size_t>(s) * num_q_heads + h) * P;
 
-    float mloc = -INFINITY;
-    for (int p0 = 0; p0 < np; p0 += 64)
+    // The first 64 partitions' (m, l) stay in registers for the weights (one
+    // load of them for contexts of up to 64 partitions).
+    float m0 = -INFINITY, l0 = 0.0f;
+    if (lane < np) {
+        m0 = ml[(base + lane) * 2];
+        l0 = ml[(base + lane) * 2 + 1];
+    }
+    float mloc = m0;
+    for (int p0 = 64; p0 < np; p0 += 64)
         if (p0 + lane < np) mloc = fmaxf(mloc, ml[(base + p0 + lane) * 2]);
     const float M = wave_max(mloc);
 
@@ -62,24 +69,25 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ ml
         for (int p0 = 0; p0 < np; p0 += 64) {
             float wl = 0.0f;
             if (p0 + lane < np) {
-                const float mp = ml[(base + p0 + lane) * 2];
-                const float lp = ml[(base + p0 + lane) * 2 + 1];
+                const float mp = p0 == 0 ? m0 : ml[(base + p0 + lane) * 2];
+                const float lp = p0 == 0 ? l0 : ml[(base + p0 + lane) * 2 + 1];
                 wl = lp * expf(mp - M);
             }
             wsum += wl;
             const int cnt = min(64, np - p0);
-            // Eight partitions per round: their o loads are all issued before
+            // kRound partitions per round: their o loads are all issued before
             // the first is used (one memory latency per round, not per partition).
-            for (int k0 = 0; k0 < cnt; k0 += 8) {
-                float ov[8][DPL];
+            constexpr int kRound = 32;
+            for (int k0 = 0; k0 < cnt; k0 += kRound) {
+                float ov[kRound][DPL];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
+                for (int u = 0; u < kRound; ++u) {
                     const float* op = o + (base + p0 + min(k0 + u, cnt - 1)) * D + lane * DPL;
 #pragma unroll
                     for (int e = 0; e < DPL; ++e) ov[u][e] = op[e];
                 }
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
+                for (int u = 0; u < kRound; ++u) {
                     // partitions past cnt re-read the last one and get weight 0
                     const float wk = k0 + u < cnt
                                          ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
