@@ -57,25 +57,25 @@ KERNEL_SOURCES = {
                                          "device.h", "common.h")),
 }
 MEASURED_TRAFFIC = {  # traffic_key -> counters of the decode call's streaming kernel
-    "llama13b_layer": {  # FETCH 367,280.2 KiB x 1.99991 + WRITE 960.0 KiB
-        "kernel": "valu", "bytes": 753_140_815,
-        "sources_sha256": "032b39f19f2d7049207454d8c0d5e9f62308114346691d549f90c7ce4399885f",
+    "llama13b_layer": {  # FETCH 367,280.2 KiB x 1.99992 + WRITE 960.0 KiB
+        "kernel": "valu", "bytes": 753_142_802,
+        "sources_sha256": "c9dc5d7242b8006453dbc9d4421f27ee95c5775a0ec3be9a5ad3e8ade8a1754e",
         "summary": "profiles/decode_kernel_llama13b_layer.md"},
-    "longctx_fp8": {  # FETCH 715,839.1 KiB x 1.99998 + WRITE 5,818.7 KiB
-        "kernel": "valu", "bytes": 1_471_978_577,
-        "sources_sha256": "032b39f19f2d7049207454d8c0d5e9f62308114346691d549f90c7ce4399885f",
+    "longctx_fp8": {  # FETCH 715,842.6 KiB x 1.99998 + WRITE 5,818.5 KiB
+        "kernel": "valu", "bytes": 1_471_989_128,
+        "sources_sha256": "c9dc5d7242b8006453dbc9d4421f27ee95c5775a0ec3be9a5ad3e8ade8a1754e",
         "summary": "profiles/decode_kernel_longctx_fp8.md"},
-    "gqa_prefix/shared_prefix_l2": {  # streaming kernel: FETCH 369,781.5 KiB x 1.99995 + WRITE 12,776.6 KiB
-        "kernel": "balanced", "bytes": 770_378_449,
-        "sources_sha256": "12b34f65d1bfaaee01c52a66d0c3e58b538b6a4783548a75cef40bc953a8acb8",
+    "gqa_prefix/shared_prefix_l2": {  # streaming kernel: FETCH 369,815.7 KiB x 1.99995 + WRITE 12,776.6 KiB
+        "kernel": "balanced", "bytes": 770_446_857,
+        "sources_sha256": "feb6bde6dd54045d3729aa507b43915901b47bca04478feceaf3dd489046e3a7",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
-    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 357,916.2 KiB x 1.99992 + WRITE 12,935.0 KiB
-        "kernel": "prefix", "bytes": 746_228_692,
-        "sources_sha256": "bf6319c4577c19cafb5bc86585ed360b9dd7f9d6fbbb0f16ab9a4ac47b8313e2",
+    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 357,916.0 KiB x 1.99992 + WRITE 12,933.5 KiB
+        "kernel": "prefix", "bytes": 746_226_552,
+        "sources_sha256": "0d45623152ed752a11ca5e2583a96b480b9e459357ccf7c0e9205e6ab60bb501",
         "summary": "profiles/prefix_kernel_gqa_prefix.md"},
-    "7b_32layer": {  # streaming kernel: FETCH 1,049,670.5 KiB x 1.99998 + WRITE 1,536.0 KiB
-        "kernel": "balanced", "bytes": 2_151_271_397,
-        "sources_sha256": "12b34f65d1bfaaee01c52a66d0c3e58b538b6a4783548a75cef40bc953a8acb8",
+    "7b_32layer": {  # streaming kernel: FETCH 1,049,656.0 KiB x 1.99998 + WRITE 1,536.0 KiB
+        "kernel": "balanced", "bytes": 2_151_246_855,
+        "sources_sha256": "feb6bde6dd54045d3729aa507b43915901b47bca04478feceaf3dd489046e3a7",
         "summary": "profiles/decode_balanced_kernel_7b_32layer.md"},
 }
 
