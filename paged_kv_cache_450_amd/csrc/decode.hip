@@ -190,6 +190,9 @@ hipError_t launch_balanced_as(DecodeParams prm, int cus, hipStream_t st) {
         wgs_per_cu = std::max(1, std::min(nb, kBalancedWavesPerCu / 4));
     }
     prm.num_waves = cus * wgs_per_cu * 4;
+    // Four waves of a workgroup walk one range, one kv head each, when the heads
+    // come in fours (two, or one, otherwise).
+    prm.head_group = prm.num_kv_heads % 4 == 0 ? 4 : (prm.num_kv_heads % 2 == 0 ? 2 : 1);
     hipLaunchKernelGGL((decode_balanced_kernel<M, KV, D, NBUF, kPre, kKeep, kFold>),
                        dim3(prm.num_waves / 4), dim3(256), 0, st, prm);
     const hipError_t e = hipGetLastError();

@@ -16,11 +16,17 @@ using namespace pkv::dev;
 // Context lengths in a batch vary widely (16 to 8192 tokens in a log-normal
 // batch), so one workgroup per sequence, or per fixed-size partition, leaves
 // the GPU waiting on the longest items or paying a start-up per item. Here the
-// grid is exactly the waves the GPU holds at once, and the tiles of the whole
-// batch, ordered (sequence, kv head, block), are cut into R equal contiguous
-// ranges, one per wave. A wave streams its range through its tile ring
-// without a break: the ring runs across (sequence, head) boundaries. Each run
-// of tiles of one (sequence, kv head) inside a range is a segment. A segment
+// grid is exactly the waves the GPU holds at once. The kv heads are taken in
+// groups of hg (4 when the head count allows, else 2 or 1), and the units of
+// the whole batch, ordered (sequence, head group, block), are cut into R equal
+// contiguous ranges, one per group of hg waves of a workgroup: wave i of the
+// group reads head i of the head group of each unit, so the group's waves
+// stream the same blocks in step and their loads at any moment fall on hg
+// adjacent head tiles of one block (runs of hg x 4 KiB instead of scattered
+// 4 KiB tiles, which the HBM serves faster). A wave streams its range through
+// its tile ring without a break: the ring runs across (sequence, head)
+// boundaries. Each run of tiles of one (sequence, kv head) inside a range is a
+// segment. A segment
 // that covers its whole context writes the output directly; a context split
 // over several waves leaves one partial (o / l, m, l) per wave in the
 // workspace, and a second, small kernel on the same stream merges them with
@@ -33,8 +39,8 @@ using namespace pkv::dev;
 // by one wave goes to its own partial slot instead of the output, and the
 // merge folds the prefix partial in as one more piece.
 
-// Issue-side walker over the tiles of the batch in (sequence, kv head, block)
-// order, holding the block ids of the current sequence's table row: the first
+// Issue-side walker over one wave's tiles, in (sequence, head group, block)
+// order with the wave's own head of each group, holding the block ids of the current sequence's table row: the first
 // 128 blocks from the window's start stay in registers for the row's other
 // heads, later blocks rotate through a second pair of 64-id chunks. A
 // sequence's tiles are its blocks jlo .. nblk-1: jlo is 0, or a sliding
@@ -46,7 +52,7 @@ struct TileWalk {
     int L;               // tokens of sequence s read from its blocks (kFold: without
                          // the new token's position)
     int has_pre;         // sequence s has a shared-prefix partial
-    int64_t a_sg;        // global index of tile (s, g, jlo)
+    int64_t a_sg;        // global index of unit (s, g / hg, jlo)
     int chunk;           // sequences 64*chunk .. +63 have their lengths in lens
     int lens;            // per lane: tokens of sequence 64*chunk + lane
     int pres;            // per lane: its leading blocks covered by the prefix pass
@@ -103,13 +109,14 @@ __device__ __forceinline__ void walk_advance(const DecodeParams& p, TileWalk& t,
     if (++t.j < t.nend) return;
     t.j = t.jlo;
     t.a_sg += t.nend - t.jlo;
-    if (++t.g < p.num_kv_heads) {  // same row, next head: its first 128 blocks are at hand
+    // same row, the wave's head of the next group: its first 128 blocks are at hand
+    if ((t.g += p.head_group) < p.num_kv_heads) {
         t.base = t.rbase;
         t.ids_a = t.row0_a;
         t.ids_b = t.row0_b;
         return;
     }
-    t.g = 0;
+    t.g &= p.head_group - 1;  // the wave's head of the first group (hg is 1, 2 or 4)
     // Next sequence with tokens. A wave's range ends at or before the batch's
     // last tile, so a later non-empty sequence exists; the bound only keeps s
     // inside the batch should the lengths change under a running kernel.
@@ -396,9 +403,11 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
     const int lane = threadIdx.x & 63;
     const int wv_in = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int w = blockIdx.x * 4 + wv_in;
-    const int W = p.num_waves;
+    const int hg = p.head_group, hs = __builtin_ctz(hg);  // hg is 1, 2 or 4
+    const int rk = w >> hs, gi = w & (hg - 1);  // the wave's range, its head in each group
+    const int W = p.num_waves >> hs;            // ranges the launch can hold
 
-    // Total tiles of the batch, then this wave's range [t0, t1).
+    // Total units (tiles of a head group) of the batch, then this group's range [t0, t1).
     int64_t total = 0;
     for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
         const int jj = c0 + lane;
@@ -407,16 +416,16 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
                                                 (kFold ? new_of(p, jj) : 0)
                                           : 0);
     }
-    total *= p.num_kv_heads;
-    // R non-empty ranges: with fewer tiles than waves the surplus waves idle,
+    total *= p.num_kv_heads >> hs;
+    // R non-empty ranges: with fewer units than ranges the surplus waves idle,
     // so every wave of a split context really holds a piece of it.
     const int R = static_cast<int>(total < W ? total : W);
-    if (w >= R) return;
-    const int64_t t0 = range_start(total, w, R);
-    const int64_t t1 = range_start(total, w + 1, R);
+    if (rk >= R) return;
+    const int64_t t0 = range_start(total, rk, R);
+    const int64_t t1 = range_start(total, rk + 1, R);
     const int n = static_cast<int>(t1 - t0);
 
-    // Locate tile t0: the sequence holding it, then its head and block.
+    // Locate unit t0: the sequence holding it, then its head group and block.
     TileWalk tw;
     bool found = false;
     {
@@ -426,7 +435,7 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
             const int len = jj < p.num_seqs ? seq_tokens(p, jj) : 0;
             const int pre = kPre && jj < p.num_seqs ? pre_of(p, jj) : 0;
             const int news = kFold && jj < p.num_seqs ? new_of(p, jj) : 0;
-            const int tiles = (pass_tiles(p, len, pre) + news) * p.num_kv_heads;
+            const int tiles = (pass_tiles(p, len, pre) + news) * (p.num_kv_heads >> hs);
             const int incl = wave_incl_scan(tiles, lane);
             const uint64_t hit = __ballot(jj < p.num_seqs && carry + incl > t0);
             if (hit) {
@@ -450,9 +459,10 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
                 const int nt = tw.nend - tw.jlo;  // tiles per head
                 const int64_t a_s = carry + __builtin_amdgcn_readlane(incl - tiles, ln);
                 const int64_t off = t0 - a_s;
-                tw.g = static_cast<int>(off / nt);
+                const int grp = static_cast<int>(off / nt);
+                tw.g = grp * hg + gi;
                 tw.j = tw.jlo + static_cast<int>(off % nt);
-                tw.a_sg = a_s + static_cast<int64_t>(tw.g) * nt;
+                tw.a_sg = a_s + static_cast<int64_t>(grp) * nt;
                 found = true;
                 break;
             }
@@ -643,21 +653,26 @@ balanced_merge_kernel(const DecodeParams p) {
         for (int idx = t; idx < G * D; idx += NT) out[idx] = 0;
         return;
     }
-    // Waves wa .. wb read pieces of this context (none when the prefix pass
-    // covered all of it); whole: one wave read it all and left its partial in suf.
+    // Ranges wa .. wb hold pieces of this context, each read by wave gi of its
+    // range's head group (none when the prefix pass covered all of it); whole:
+    // one wave read it all and left its partial in suf.
+    const int hg = p.head_group, hs = __builtin_ctz(hg);  // hg is 1, 2 or 4
+    const int grp = g >> hs, gi = g & (hg - 1);
     int wa = 0, wb = -1, slot_a = 0;
     bool whole = false;
     if (nblk > 0) {
-        total *= p.num_kv_heads;
-        const int R = static_cast<int>(total < p.num_waves ? total : p.num_waves);
-        const int64_t a_sg = before * p.num_kv_heads + static_cast<int64_t>(g) * nblk;
+        total *= p.num_kv_heads >> hs;
+        const int Wr = p.num_waves >> hs;
+        const int R = static_cast<int>(total < Wr ? total : Wr);
+        const int64_t a_sg = before * (p.num_kv_heads >> hs) + static_cast<int64_t>(grp) * nblk;
         wa = wave_of(a_sg, total, R);
         wb = wave_of(a_sg + nblk - 1, total, R);
         if (wa == wb) {
             if (!has_pre) return;  // written whole by its wave
             whole = true;
         }
-        // Wave wa's piece began before its range: slot 1; waves after it: slot 0.
+        // A context that begins inside range wa (past its first unit) has its
+        // piece there in slot 1; every other piece is in slot 0.
         slot_a = (a_sg <= range_start(total, wa, R)) ? 0 : 1;
     }
     for (int idx = t; idx < G * D / 4; idx += NT) {
@@ -666,9 +681,9 @@ balanced_merge_kernel(const DecodeParams p) {
         float run_m = -INFINITY, run_l = 0.0f;
         float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         // Fold one partial (o normalised, m in log2 units, l).
-        auto fold = [&](const float* hs) {
-            const float4 ov = *reinterpret_cast<const float4*>(hs + d);
-            const float mv = hs[D], lv = hs[D + 1];
+        auto fold = [&](const float* src) {
+            const float4 ov = *reinterpret_cast<const float4*>(src + d);
+            const float mv = src[D], lv = src[D + 1];
             const float mx = fmaxf(run_m, mv);
             const float ms = (mx == -INFINITY) ? 0.0f : mx;
             const float a = fast_exp2(run_m - ms);
@@ -689,10 +704,10 @@ balanced_merge_kernel(const DecodeParams p) {
                 const int v = v0 + i;
                 if (v <= wb) {
                     const int slot = v == wa ? slot_a : 0;
-                    const float* hs = base + static_cast<size_t>(v * 2 + slot) * G * SS;
-                    ov[i] = *reinterpret_cast<const float4*>(hs + d);
-                    mv[i] = hs[D];
-                    lv[i] = hs[D + 1];
+                    const float* ps = base + static_cast<size_t>((v * hg + gi) * 2 + slot) * G * SS;
+                    ov[i] = *reinterpret_cast<const float4*>(ps + d);
+                    mv[i] = ps[D];
+                    lv[i] = ps[D + 1];
                 } else {
                     ov[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                     mv[i] = -INFINITY;

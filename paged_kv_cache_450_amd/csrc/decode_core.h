@@ -39,6 +39,7 @@ struct DecodeParams {
     // Balanced single pass (see decode_balanced_kernel).
     float* slots;             // [waves][2][G][D + 4] partials of split contexts
     int32_t num_waves;        // waves of the balanced launch
+    int32_t head_group;       // waves that walk one range in step, one kv head each
     int32_t num_seqs;
     // Fused append (NULL: none): the new token of every sequence, K and V rows
     // [B][Hkv][D] of the 16-bit source dtype (the q dtype).
