@@ -179,22 +179,26 @@ size_t balanced_bytes(size_t group, size_t head_dim, size_t waves) {
 template <class M, int KV, int D, int NBUF, bool kPre, bool kKeep, bool kFold>
 hipError_t launch_balanced_as(DecodeParams prm, int cus, hipStream_t st) {
     static int wgs_per_cu = -1;  // per kernel instance; the same on every gfx950 device
+    constexpr int kWpg = balanced_wpg<M>();
     if (wgs_per_cu < 0) {
         int nb = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
                 &nb,
                 reinterpret_cast<const void*>(
                     &decode_balanced_kernel<M, KV, D, NBUF, kPre, kKeep, kFold>),
-                256, 0) != hipSuccess)
+                kWpg * 64, 0) != hipSuccess)
             return hipGetLastError();
-        wgs_per_cu = std::max(1, std::min(nb, kBalancedWavesPerCu / 4));
+        wgs_per_cu = std::max(1, std::min(nb, kBalancedWavesPerCu / kWpg));
     }
-    prm.num_waves = cus * wgs_per_cu * 4;
-    // Four waves of a workgroup walk one range, one kv head each, when the heads
-    // come in fours (two, or one, otherwise).
-    prm.head_group = prm.num_kv_heads % 4 == 0 ? 4 : (prm.num_kv_heads % 2 == 0 ? 2 : 1);
+    prm.num_waves = cus * wgs_per_cu * kWpg;
+    // The waves of a workgroup walk one range, one kv head each: heads in groups
+    // of kWpg when the head count allows, else of the largest power of two
+    // dividing it.
+    int hg = kWpg;
+    while (prm.num_kv_heads % hg != 0) hg /= 2;
+    prm.head_group = hg;
     hipLaunchKernelGGL((decode_balanced_kernel<M, KV, D, NBUF, kPre, kKeep, kFold>),
-                       dim3(prm.num_waves / 4), dim3(256), 0, st, prm);
+                       dim3(prm.num_waves / kWpg), dim3(kWpg * 64), 0, st, prm);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int kHpw = merge_heads_per_wg<D, M::kG>();

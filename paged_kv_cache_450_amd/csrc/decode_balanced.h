@@ -17,7 +17,8 @@ using namespace pkv::dev;
 // batch), so one workgroup per sequence, or per fixed-size partition, leaves
 // the GPU waiting on the longest items or paying a start-up per item. Here the
 // grid is exactly the waves the GPU holds at once. The kv heads are taken in
-// groups of hg (4 when the head count allows, else 2 or 1), and the units of
+// groups of hg (as many as a workgroup has waves, 8 or 4, when the head count
+// allows, else the largest power of two that divides it), and the units of
 // the whole batch, ordered (sequence, head group, block), are cut into R equal
 // contiguous ranges, one per group of hg waves of a workgroup: wave i of the
 // group reads head i of the head group of each unit, so the group's waves
@@ -116,7 +117,7 @@ __device__ __forceinline__ void walk_advance(const DecodeParams& p, TileWalk& t,
         t.ids_b = t.row0_b;
         return;
     }
-    t.g &= p.head_group - 1;  // the wave's head of the first group (hg is 1, 2 or 4)
+    t.g &= p.head_group - 1;  // the wave's head of the first group (hg is a power of 2)
     // Next sequence with tokens. A wave's range ends at or before the batch's
     // last tile, so a later non-empty sequence exists; the bound only keeps s
     // inside the batch should the lengths change under a running kernel.
@@ -394,16 +395,27 @@ struct MfmaMath {
 // the row's buffer descriptor and read as zeros), attended with weight like
 // any token and stored to its slot by the wave that reads it. The context's
 // blocks are read without that position (another wave may be storing it).
+// Waves per workgroup of the streaming kernel, and so its largest head group:
+// eight for the vector math (7B layer, 32 heads: 325.5 against 326.7 us per
+// call with four), four for the matrix cores (GQA batch, 8 kv heads: 139.7
+// against 140.7 us with eight).
+template <class M>
+constexpr int balanced_wpg() {
+    return M::kG == 1 ? 8 : 4;
+}
+
 template <class M, int KV, int D, int NBUF, bool kPre = false, bool kKeep = false,
           bool kFold = false>
-__global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(balanced_wpg<M>() * 64, 8 / balanced_wpg<M>()) void
+decode_balanced_kernel(const DecodeParams p) {
+    constexpr int WPG = balanced_wpg<M>();
     static_assert(!(kPre && kKeep), "one shared-prefix form at a time");
     constexpr int G = M::kG;
     constexpr int SS = SlotGeoB<D>::kStride;
     const int lane = threadIdx.x & 63;
     const int wv_in = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int w = blockIdx.x * 4 + wv_in;
-    const int hg = p.head_group, hs = __builtin_ctz(hg);  // hg is 1, 2 or 4
+    const int w = blockIdx.x * WPG + wv_in;
+    const int hg = p.head_group, hs = __builtin_ctz(hg);  // hg is 1, 2, 4 or 8
     const int rk = w >> hs, gi = w & (hg - 1);  // the wave's range, its head in each group
     const int W = p.num_waves >> hs;            // ranges the launch can hold
 
@@ -472,9 +484,9 @@ __global__ __launch_bounds__(256, 2) void decode_balanced_kernel(const DecodePar
     if (!found) return;  // lengths changed between the two passes
     walk_enter_row(p, tw, lane);
 
-    __shared__ __attribute__((aligned(16))) uint8_t stage_all[4][MfmaGeo<D>::kStage];
-    __shared__ __attribute__((aligned(16))) uint8_t q_all[4][G > 1 ? MfmaGeo<D>::kNk * 1024 : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t kst_all[4][G > 1 ? MfmaGeo<D>::kStage : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_all[WPG][G > 1 ? MfmaGeo<D>::kStage : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t q_all[WPG][G > 1 ? MfmaGeo<D>::kNk * 1024 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t kst_all[WPG][G > 1 ? MfmaGeo<D>::kStage : 16];
     typename M::State st;
     if constexpr (G > 1) {
         st.stage = stage_all[wv_in];
@@ -656,7 +668,7 @@ balanced_merge_kernel(const DecodeParams p) {
     // Ranges wa .. wb hold pieces of this context, each read by wave gi of its
     // range's head group (none when the prefix pass covered all of it); whole:
     // one wave read it all and left its partial in suf.
-    const int hg = p.head_group, hs = __builtin_ctz(hg);  // hg is 1, 2 or 4
+    const int hg = p.head_group, hs = __builtin_ctz(hg);  // hg is 1, 2, 4 or 8
     const int grp = g >> hs, gi = g & (hg - 1);
     int wa = 0, wb = -1, slot_a = 0;
     bool whole = false;
