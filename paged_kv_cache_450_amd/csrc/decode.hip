@@ -124,16 +124,27 @@ pkv_status append_first(const char* fn, const pkv_pool* pool, int32_t layer, con
     return PKV_OK;
 }
 
-// Waves per workgroup: an item of up to 16 blocks (a partition, or the blocks
-// a sliding window touches: ceil(W / 16) + 1 at most) is one wave's stream,
-// up to 32 two waves'; longer ranges (big partitions, or the whole context)
-// are shared by four waves and merged through LDS. Few tiles split four ways
-// leave each wave's ring barely filled before it drains.
+// Waves per workgroup: the blocks a sliding window touches (ceil(W / 16) + 1
+// at most) are one wave's stream up to 17 blocks, two waves' up to 33; a
+// whole split-K partition is one wave's up to 8 blocks, two waves' up to 17;
+// longer ranges are shared by four waves and merged through LDS. Few tiles
+// split four ways leave each wave's ring barely filled before it drains.
 template <int KV, int QD, int D, int G>
 hipError_t by_waves(const DecodeParams& prm, dim3 grid, hipStream_t st) {
     const int span = prm.blocks_per_part > 0              ? prm.blocks_per_part
                      : prm.window > 0 && prm.window <= 1024 ? (prm.window + 15) / 16 + 1
                                                             : 0;
+    if (prm.blocks_per_part > 0 && prm.window <= 0) {
+        // Whole split-K partitions: one wave up to 8 blocks, two up to 17, four
+        // beyond (512-token partitions: FP8 long-context call 226.3 -> 223.6 us,
+        // 16-bit 13B layer 120.1 -> 119.3 us against two waves; 256-token
+        // partitions: 239.3 -> 238.0 and 121.2 -> 120.1 us against one). With a
+        // sliding window most of a partition's blocks fall outside it, and the
+        // spans below stay faster (FP8 long-context at W = 256: 26.2 against 28.2 us).
+        if (span <= 8) return launch<KV, QD, D, G, 1>(prm, grid, st);
+        if (span <= 17) return launch<KV, QD, D, G, 2>(prm, grid, st);
+        return launch<KV, QD, D, G, 4>(prm, grid, st);
+    }
     if (span > 0 && span <= 17) return launch<KV, QD, D, G, 1>(prm, grid, st);
     if (span > 0 && span <= 33) return launch<KV, QD, D, G, 2>(prm, grid, st);
     return launch<KV, QD, D, G, 4>(prm, grid, st);
