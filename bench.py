@@ -59,23 +59,23 @@ KERNEL_SOURCES = {
 MEASURED_TRAFFIC = {  # traffic_key -> counters of the decode call's streaming kernel
     "llama13b_layer": {  # FETCH 367,280.2 KiB x 1.99992 + WRITE 960.0 KiB
         "kernel": "valu", "bytes": 753_142_802,
-        "sources_sha256": "c9dc5d7242b8006453dbc9d4421f27ee95c5775a0ec3be9a5ad3e8ade8a1754e",
+        "sources_sha256": "cbab5cce16b02bf806b617d19602e4312c4326bd103a020cad4fadb8e17b96e4",
         "summary": "profiles/decode_kernel_llama13b_layer.md"},
-    "longctx_fp8": {  # FETCH 715,842.6 KiB x 1.99998 + WRITE 5,818.5 KiB
-        "kernel": "valu", "bytes": 1_471_989_128,
-        "sources_sha256": "c9dc5d7242b8006453dbc9d4421f27ee95c5775a0ec3be9a5ad3e8ade8a1754e",
+    "longctx_fp8": {  # FETCH 715,831.1 KiB x 1.99998 + WRITE 5,818.6 KiB
+        "kernel": "valu", "bytes": 1_471_965_679,
+        "sources_sha256": "cbab5cce16b02bf806b617d19602e4312c4326bd103a020cad4fadb8e17b96e4",
         "summary": "profiles/decode_kernel_longctx_fp8.md"},
-    "gqa_prefix/shared_prefix_l2": {  # streaming kernel: FETCH 369,815.7 KiB x 1.99995 + WRITE 12,776.6 KiB
-        "kernel": "balanced", "bytes": 770_446_857,
-        "sources_sha256": "feb6bde6dd54045d3729aa507b43915901b47bca04478feceaf3dd489046e3a7",
+    "gqa_prefix/shared_prefix_l2": {  # streaming kernel: FETCH 370,911.4 KiB x 1.99995 + WRITE 12,748.2 KiB
+        "kernel": "balanced", "bytes": 772_661_713,
+        "sources_sha256": "41fc6dd2f6170f68f834db582fca153be022e76942fdd25ddf2a2da46f89b81d",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
-    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 357,916.0 KiB x 1.99992 + WRITE 12,933.5 KiB
-        "kernel": "prefix", "bytes": 746_226_552,
-        "sources_sha256": "0d45623152ed752a11ca5e2583a96b480b9e459357ccf7c0e9205e6ab60bb501",
+    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 359,250.0 KiB x 1.99992 + WRITE 12,894.2 KiB
+        "kernel": "prefix", "bytes": 748_918_231,
+        "sources_sha256": "974dc92a09dcf38da6385890b1afaf71c4def494c22d184a3ba1e4ff8e317771",
         "summary": "profiles/prefix_kernel_gqa_prefix.md"},
-    "7b_32layer": {  # streaming kernel: FETCH 1,049,656.0 KiB x 1.99998 + WRITE 1,536.0 KiB
-        "kernel": "balanced", "bytes": 2_151_246_855,
-        "sources_sha256": "feb6bde6dd54045d3729aa507b43915901b47bca04478feceaf3dd489046e3a7",
+    "7b_32layer": {  # streaming kernel: FETCH 1,049,605.0 KiB x 1.99998 + WRITE 1,536.0 KiB
+        "kernel": "balanced", "bytes": 2_151_142_408,
+        "sources_sha256": "41fc6dd2f6170f68f834db582fca153be022e76942fdd25ddf2a2da46f89b81d",
         "summary": "profiles/decode_balanced_kernel_7b_32layer.md"},
 }
 
