@@ -121,12 +121,13 @@ class PagedKVCache:
 # shared_prefix="auto" takes the prefix kernel (paged_attn_decode_prefix);
 # below it, the shared blocks are read through the L2 by the balanced pass
 # (paged_attn_decode_prefix_l2). Measured on MI355X (64 sharers, 64 / 8 heads
-# x 128, bf16, fused step, per call), L2 form against prefix kernel: 264 MB
-# repeated (1024 shared tokens) 136.0 against 156.7 us; 528 MB (2048) 144.8
-# against 146.1 us; 1057 MB (4096) 194.2 against 148.8 us. The prefix kernel
-# costs 10-20 us per call whatever it reads; the L2 form costs nothing extra
-# but its repeats still cross the fabric when they miss the L2.
-PREFIX_AUTO_BYTES = 700_000_000
+# x 128, bf16, fused step, per call), L2 form against prefix kernel: 132 MB
+# repeated (512 shared tokens) 139.0 against 148.9 us; 264 MB (1024) 135.9
+# against 140.8 us; 528 MB (2048) 142.7 against 133.6 us; 1057 MB (4096) 191.4
+# against 137.9 us. The prefix kernel costs about 10 us per call whatever it
+# reads; the L2 form costs nothing extra but its repeats still cross the fabric
+# when they miss the L2.
+PREFIX_AUTO_BYTES = 400_000_000
 
 
 def prefix_repeated_bytes(plan, desc) -> int:

@@ -219,12 +219,13 @@ def test_full_size_workload_l2_sampled():
     check_layers(cfg, side, o, seqs, range(cfg.layers), whole_pool=False)
 
 
-@pytest.mark.parametrize("prompt,expect_pass", [(512, False), (2048, False), (4096, True)])
+@pytest.mark.parametrize("prompt,expect_pass",
+                         [(512, False), (1024, False), (2048, True), (4096, True)])
 def test_auto_picks_the_pass_and_matches(prompt, expect_pass):
-    """shared_prefix="auto" on the full-size GQA batch: the 512- and 2048-token
-    shared prompts (132 and 528 MB of repeated reads) are read through the L2
-    by the balanced pass, a 4096-token one (1057 MB) runs the prefix kernel;
-    either way sampled outputs match the oracle."""
+    """shared_prefix="auto" on the full-size GQA batch: the 512- and 1024-token
+    shared prompts (132 and 264 MB of repeated reads) are read through the L2
+    by the balanced pass, 2048- and 4096-token ones (528 and 1057 MB) run the
+    prefix kernel; either way sampled outputs match the oracle."""
     cfg = replace(W.CONFIGS["gqa_prefix"], share_prefix_tokens=prompt)
     say(f"prefix auto prompt={prompt}")
     side = H.build_product(cfg, seed=0, fused=True, shared_prefix="auto")

@@ -208,11 +208,11 @@ def test_auto_takes_the_prefix_pass_only_when_it_saves_enough():
         return DecodeBatch(cache, tables, lens, 64, None, device="cpu", shared_prefix=mode)
 
     per_block = 2 * 8 * 16 * 128 * 2  # K and V of one block, every kv head, bf16
-    small, large = batch(64, 128, "auto"), batch(64, 256, "auto")
-    assert small.plan is None  # 63 x 128 blocks x 64 KiB = 528 MB saved: the L2 form
+    small, large = batch(64, 64, "auto"), batch(64, 128, "auto")
+    assert small.plan is None  # 63 x 64 blocks x 64 KiB = 264 MB saved: the L2 form
     assert small.l2_blocks is not None
-    assert large.plan is not None and large.plan.groups()[0][1] == 256
-    assert large.repeated_bytes() == 63 * 256 * per_block >= DecodeBatch.PREFIX_AUTO_BYTES
+    assert large.plan is not None and large.plan.groups()[0][1] == 128
+    assert large.repeated_bytes() == 63 * 128 * per_block >= DecodeBatch.PREFIX_AUTO_BYTES
     forced = batch(64, 32, True)
     assert forced.plan is not None and forced.repeated_bytes() == 63 * 32 * per_block
     assert batch(64, 32, False).plan is None
