@@ -89,3 +89,28 @@ def test_cases_cover_every_form():
             ("fp8", "perseq"), ("fp8", "splitk"), ("shared", "True"), ("shared", "l2"),
             ("fused", True), ("fused", False)}
     assert need <= forms, need - forms
+
+
+# kv head counts that are not powers of two: the balanced pass takes them in
+# head groups of 4 (or 8 on the vector path), 2 or 1, with group sizes the
+# fixed seeds above never reach (3 heads: groups of 1; 6: of 2; 12: of 4; 40:
+# of 8 on the vector path). Batches small enough that waves outnumber tiles
+# (one tile per range) and large enough that ranges hold many.
+HEAD_COUNTS = [(3, 1, 4), (5, 1, 24), (6, 1, 24), (6, 8, 24), (12, 1, 24), (12, 2, 24),
+               (12, 8, 6), (10, 4, 24), (40, 1, 24)]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("hkv,g,batch", HEAD_COUNTS)
+def test_balanced_pass_with_any_head_count(hkv, g, batch, _gpu):
+    from tests.test_gpu_parity import check_bookkeeping, check_layers
+
+    seed = 500 + hkv * 10 + g
+    cfg = W.Config(f"heads{hkv}x{g}", 1, batch, hkv * g, hkv, 128, "bf16", "bf16",
+                   ("uniform", 1, 700), balanced=True)
+    say(f"balanced head count: Hkv={hkv} G={g} B={batch} seed={seed}")
+    side = H.build_product(cfg, seed=seed, fused=True)
+    torch.cuda.synchronize()
+    o = H.oracle_bookkeeping(cfg, seed)
+    check_bookkeeping(side, o)
+    check_layers(cfg, side, o, list(range(cfg.batch)), range(cfg.layers), whole_pool=True)
