@@ -361,8 +361,10 @@ size_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   - workspace == NULL (or an FP8 cache, or num_seqs > 4096): one workgroup
  *     per (sequence, kv head), sequences handed out longest first;
  *   - otherwise the balanced form: the tiles of the whole batch are cut into
- *     equal ranges, one per resident wave, so the work is even whatever the
- *     length mix; contexts split between waves leave partials in workspace
+ *     equal ranges, one per group of resident waves that read adjacent kv
+ *     heads of the same blocks in step (one wave per head), so the work is
+ *     even whatever the length mix; contexts split between ranges leave
+ *     partials in workspace
  *     (256-byte aligned, >= paged_attn_workspace_bytes(..., 0) bytes, no
  *     initial contents needed) that a second kernel of the same call merges.
  *     Calls that share a workspace must be ordered on one stream.
