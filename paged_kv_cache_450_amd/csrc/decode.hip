@@ -235,13 +235,23 @@ hipError_t launch_balanced(const DecodeParams& prm, int cus, hipStream_t st) {
                         : launch_balanced_as<M, KV, D, NBUF, false, false, false>(prm, cus, st);
 }
 
+// Tile ring of the balanced vector-ALU pass: two LDS slots per wave filled by
+// direct buffer-to-LDS loads (true), or four tiles of registers (false). The
+// LDS form measured 0.6% faster on the 7B layer (323.3-323.7 against
+// 325.4-325.7 us per call).
+constexpr bool kLdsRingBalanced = true;
+
 // Ring depths keep two waves per SIMD (MFMA at D = 128 holds its O^T
 // accumulators beside the ring, with Q^T in LDS: three tiles).
 template <int KV, int D>
 hipError_t balanced_by_group(int G, const DecodeParams& prm, int cus, hipStream_t st) {
     constexpr int R = (D == 128) ? 3 : 4;
     switch (G) {
-        case 1: return launch_balanced<ValuMath<KV, D>, KV, D, 4>(prm, cus, st);
+        case 1:
+            if constexpr (kLdsRingBalanced)
+                return launch_balanced<ValuLdsMath<KV, D>, KV, D, 2>(prm, cus, st);
+            else
+                return launch_balanced<ValuMath<KV, D>, KV, D, 4>(prm, cus, st);
         case 2: return launch_balanced<MfmaMath<KV, D, 2>, KV, D, R>(prm, cus, st);
         case 4: return launch_balanced<MfmaMath<KV, D, 4>, KV, D, R>(prm, cus, st);
         default: return launch_balanced<MfmaMath<KV, D, 8>, KV, D, R>(prm, cus, st);

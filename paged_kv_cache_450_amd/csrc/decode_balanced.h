@@ -174,6 +174,7 @@ struct ValuMath {
     static constexpr int kG = 1;
     static constexpr bool kPrefetchQ = true;  // q is small: ride in the ring with its tile
     static constexpr bool kSplit = false;     // the tile math is one piece (consume)
+    static constexpr bool kLds = false;       // the ring is NBUF tiles of registers
     static constexpr int kEpl = Gm::kEpl, kLpt = Gm::kLpt, kNld = Gm::kNld, kTB = Gm::kTileBytes;
     using TileT = Tile<KV, D>;
     using QT = QSlice<KV, D>;
@@ -271,6 +272,57 @@ struct ValuMath {
     }
 };
 
+// The same math with the tile ring in LDS: two slots per wave, filled by
+// direct buffer-to-LDS loads (no registers held for tiles in flight) and read
+// into one register tile when consumed.
+template <int KV, int D>
+struct ValuLdsMath : ValuMath<KV, D> {
+    using Base = ValuMath<KV, D>;
+    static constexpr bool kLds = true;
+    static constexpr int kNld = Base::kNld, kTB = Base::kTB;
+    static constexpr int kSlotBytes = 2 * kTB;  // K, then V
+    // Loads of one tile into a slot: 2 * kNld, the count the waits below rely on.
+    __device__ static void issue_lds(uint8_t* slot, const TileRef& r, int lane, bool kept) {
+        typedef __attribute__((address_space(3))) void* lds_ptr;
+        // The slot's earlier reads must have completed: the refill's LDS writes
+        // do not queue behind this wave's own LDS reads.
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        if (kept) {
+#pragma unroll
+            for (int i = 0; i < kNld; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r.k, (lds_ptr)(slot + i * 1024), 16,
+                                                         lane * 16 + i * 1024, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < kNld; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r.v, (lds_ptr)(slot + kTB + i * 1024), 16,
+                                                         lane * 16 + i * 1024, 0, 0, 0);
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < kNld; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r.k, (lds_ptr)(slot + i * 1024), 16,
+                                                     lane * 16 + i * 1024, 0, 0, kStreamPolicy);
+#pragma unroll
+        for (int i = 0; i < kNld; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r.v, (lds_ptr)(slot + kTB + i * 1024), 16,
+                                                     lane * 16 + i * 1024, 0, 0, kStreamPolicy);
+    }
+    // The slot's tile into registers. The other slot's 2 * kNld loads were
+    // issued after this slot's, and a wave's loads complete in order: once at
+    // most 2 * kNld operations are outstanding, this slot's loads have landed
+    // (stores and other loads issued in between only make the wait longer).
+    __device__ static void read_slot(typename Base::TileT& t, const uint8_t* slot, int lane) {
+        static_assert(2 * kNld < 16, "vmcnt field");
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kNld));  // vmcnt(2 * kNld)
+#pragma unroll
+        for (int i = 0; i < kNld; ++i)
+            t.k[i] = *reinterpret_cast<const uint4*>(slot + i * 1024 + lane * 16);
+#pragma unroll
+        for (int i = 0; i < kNld; ++i)
+            t.v[i] = *reinterpret_cast<const uint4*>(slot + kTB + i * 1024 + lane * 16);
+    }
+};
+
 // Matrix-core math for G grouped query heads (16-bit caches).
 template <int KV, int D, int G>
 struct MfmaMath {
@@ -281,6 +333,7 @@ struct MfmaMath {
     // back does the softmax and PV from LDS), so the ring slot is refilled
     // between them.
     static constexpr bool kSplit = true;
+    static constexpr bool kLds = false;
     static constexpr int kNk = Gm::kNk, kNv = Gm::kNv, kNd = Gm::kNd, kTB = Gm::kTileBytes;
     static constexpr int kQBytes = kNk * 1024;  // Q^T operand of one wave in LDS
     using TileT = MfmaTile<D>;
@@ -498,18 +551,30 @@ decode_balanced_kernel(const DecodeParams p) {
     typename M::QT qring[M::kPrefetchQ ? NBUF : 1];
 
     const size_t bstride = static_cast<size_t>(p.num_kv_heads) * M::kTB;
-    typename M::TileT tr[NBUF];
+    // The ring: NBUF tiles of registers, or (M::kLds) two LDS slots per wave,
+    // one array per slot, and one register tile the consumed slot is read into.
+    static_assert(!M::kLds || NBUF == 2, "LDS ring: two slots");
+    constexpr int kRingBytes = M::kLds ? 2 * M::kTB : 16;
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[M::kLds ? WPG : 1][kRingBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[M::kLds ? WPG : 1][kRingBytes];
+    typename M::TileT tr[M::kLds ? 1 : NBUF];
     SlotInfo si[NBUF];
+    auto load_tile = [&](typename M::TileT& tt, const TileRef& r, int x, bool kept) {
+        if constexpr (M::kLds)
+            M::issue_lds(x == 0 ? ring0[wv_in] : ring1[wv_in], r, lane, kept);
+        else
+            M::issue(tt, r, lane, kept);
+    };
 
-    // Issue tile kn of the range into a ring slot (and the q of a segment
+    // Issue tile kn of the range into ring slot x (and the q of a segment
     // that starts there).
-    auto issue = [&](typename M::TileT& tt, SlotInfo& info, typename M::QT& qq, int kn) {
+    auto issue = [&](typename M::TileT& tt, SlotInfo& info, typename M::QT& qq, int kn, int x) {
         if (kn >= n) {
             info.bits = 0;
             info.s = info.g = 0;
             info.vslot = -1;
             const TileRef r = tile_ref(p, p.k_plane, p.v_plane, bstride, M::kTB, -1, 0, 0, 0);
-            M::issue(tt, r, lane);
+            load_tile(tt, r, x, false);
             return;
         }
         if (kn > 0) walk_advance<kPre, kKeep, kFold>(p, tw, lane);
@@ -542,7 +607,7 @@ decode_balanced_kernel(const DecodeParams p) {
             r.v = tile_rsrc(p.new_v + row, ok ? D * 2 : 0);
             info.bits = flags | (ok ? 1 : 0);  // no slot: the token is not in the context
             info.vslot = ok ? id * 16 + (tw.L & 15) : -1;  // position L - 1 of the context
-            M::issue(tt, r, lane);
+            load_tile(tt, r, x, false);
             return;
         }
         const uint8_t* kpl = p.k_plane + static_cast<size_t>(tw.g) * M::kTB;
@@ -551,14 +616,16 @@ decode_balanced_kernel(const DecodeParams p) {
         if constexpr (kFold) tw.last_id = id;
         const TileRef r = tile_ref(p, kpl, vpl, bstride, M::kTB, id, tw.j * 16, tw.L, tw.lo);
         info.bits = flags | r.nvalid | (r.nlo << 5);
-        M::issue(tt, r, lane, kKeep && tw.j < tw.keep);
+        load_tile(tt, r, x, kKeep && tw.j < tw.keep);
     };
 
 #pragma unroll
-    for (int x = 0; x < NBUF; ++x) issue(tr[x], si[x], qring[M::kPrefetchQ ? x : 0], x);
+    for (int x = 0; x < NBUF; ++x)
+        issue(tr[M::kLds ? 0 : x], si[x], qring[M::kPrefetchQ ? x : 0], x, x);
     for (int k0 = 0; k0 < n; k0 += NBUF) {
 #pragma unroll
         for (int x = 0; x < NBUF; ++x) {
+            typename M::TileT& tx = tr[M::kLds ? 0 : x];
             const SlotInfo cur = si[x];
             const int cnv = cur.nvalid(), cnl = cur.nlo();
             if (cur.bits & SlotInfo::kFirst) {
@@ -567,8 +634,9 @@ decode_balanced_kernel(const DecodeParams p) {
                 else
                     M::fetch_q_lds(p, st, cur.s, cur.g, lane);
             }
+            if constexpr (M::kLds) M::read_slot(tx, x == 0 ? ring0[wv_in] : ring1[wv_in], lane);
             if (kFold && cur.vslot >= 0)
-                M::store_new(p, tr[x],
+                M::store_new(p, tx,
                              static_cast<int64_t>(cur.vslot >> 4) * bstride +
                                  static_cast<int64_t>(cur.g) * M::kTB + (cur.vslot & 15) * (D * 2),
                              lane);
@@ -577,20 +645,22 @@ decode_balanced_kernel(const DecodeParams p) {
                 // First half, then the slot's refill, then the second half.
                 f32x4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
                 if (full)
-                    sacc = M::template front<false>(st, tr[x], 16, 0, lane);
+                    sacc = M::template front<false>(st, tx, 16, 0, lane);
                 else if (cnv > 0)
-                    sacc = M::template front<true>(st, tr[x], cnv, cnl, lane);
-                issue(tr[x], si[x], qring[M::kPrefetchQ ? x : 0], k0 + x + NBUF);
+                    sacc = M::template front<true>(st, tx, cnv, cnl, lane);
+                issue(tx, si[x], qring[M::kPrefetchQ ? x : 0], k0 + x + NBUF, x);
                 if (full)
                     M::template back<false>(st, sacc, 16, 0, p.scale_log2, lane);
                 else if (cnv > 0)
                     M::template back<true>(st, sacc, cnv, cnl, p.scale_log2, lane);
             } else {
+                // LDS ring: the tile is in registers now, so the slot is
+                // refilled before the math (the other slot stays in flight).
+                if constexpr (M::kLds) issue(tx, si[x], qring[M::kPrefetchQ ? x : 0], k0 + x + NBUF, x);
                 if (full)
-                    M::template consume<false>(st, tr[x], 16, 0, q, p.scale_log2, lane);
+                    M::template consume<false>(st, tx, 16, 0, q, p.scale_log2, lane);
                 else if (cnv > 0)
-                    M::template consume<true>(st, tr[x], cnv, cnl, q, p.scale_log2,
-                                              lane);
+                    M::template consume<true>(st, tx, cnv, cnl, q, p.scale_log2, lane);
             }
             if (cur.bits & SlotInfo::kLast) {
                 // End of a segment: write the output, or the partial of a split context.
@@ -608,7 +678,8 @@ decode_balanced_kernel(const DecodeParams p) {
                 }
                 M::reset(st);
             }
-            if constexpr (!M::kSplit) issue(tr[x], si[x], qring[M::kPrefetchQ ? x : 0], k0 + x + NBUF);
+            if constexpr (!M::kSplit && !M::kLds)
+                issue(tx, si[x], qring[M::kPrefetchQ ? x : 0], k0 + x + NBUF, x);
         }
     }
 }
