@@ -57,25 +57,25 @@ KERNEL_SOURCES = {
                                          "device.h", "common.h")),
 }
 MEASURED_TRAFFIC = {  # traffic_key -> counters of the decode call's streaming kernel
-    "llama13b_layer": {  # FETCH 367,280.2 KiB x 1.99992 + WRITE 960.0 KiB
-        "kernel": "valu", "bytes": 753_142_802,
-        "sources_sha256": "cbab5cce16b02bf806b617d19602e4312c4326bd103a020cad4fadb8e17b96e4",
+    "llama13b_layer": {  # FETCH 367,277.7 KiB x 1.99992 + WRITE 960.0 KiB
+        "kernel": "valu", "bytes": 753_137_682,
+        "sources_sha256": "119c792cce40f5982a237eaf91cc3b1b8e22a7fbadf557f3aff8657e5d2a4363",
         "summary": "profiles/decode_kernel_llama13b_layer.md"},
-    "longctx_fp8": {  # FETCH 715,831.1 KiB x 1.99998 + WRITE 5,818.6 KiB
-        "kernel": "valu", "bytes": 1_471_965_679,
-        "sources_sha256": "cbab5cce16b02bf806b617d19602e4312c4326bd103a020cad4fadb8e17b96e4",
+    "longctx_fp8": {  # FETCH 715,843.1 KiB x 1.99998 + WRITE 5,818.3 KiB
+        "kernel": "valu", "bytes": 1_471_989_948,
+        "sources_sha256": "119c792cce40f5982a237eaf91cc3b1b8e22a7fbadf557f3aff8657e5d2a4363",
         "summary": "profiles/decode_kernel_longctx_fp8.md"},
-    "gqa_prefix/shared_prefix_l2": {  # streaming kernel: FETCH 370,911.4 KiB x 1.99995 + WRITE 12,748.2 KiB
-        "kernel": "balanced", "bytes": 772_661_713,
-        "sources_sha256": "41fc6dd2f6170f68f834db582fca153be022e76942fdd25ddf2a2da46f89b81d",
+    "gqa_prefix/shared_prefix_l2": {  # streaming kernel: FETCH 370,925.2 KiB x 1.99995 + WRITE 12,748.9 KiB
+        "kernel": "balanced", "bytes": 772_690_692,
+        "sources_sha256": "f62bfc6f2a1af97a77860cb808630ee9eb70c636de886a2265a5abc04888ed1d",
         "summary": "profiles/decode_balanced_kernel_gqa_prefix.md"},
-    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 359,250.0 KiB x 1.99992 + WRITE 12,894.2 KiB
-        "kernel": "prefix", "bytes": 748_918_231,
-        "sources_sha256": "974dc92a09dcf38da6385890b1afaf71c4def494c22d184a3ba1e4ff8e317771",
+    "gqa_prefix/shared_prefix": {  # streaming kernel: FETCH 359,241.7 KiB x 1.99992 + WRITE 12,895.4 KiB
+        "kernel": "prefix", "bytes": 748_902_462,
+        "sources_sha256": "43a8fd5c11a8653a8e9a8aa76c83349133a9ac87a08a409b583219ec59ba6e0c",
         "summary": "profiles/prefix_kernel_gqa_prefix.md"},
-    "7b_32layer": {  # streaming kernel: FETCH 1,049,605.0 KiB x 1.99998 + WRITE 1,536.0 KiB
-        "kernel": "balanced", "bytes": 2_151_142_408,
-        "sources_sha256": "41fc6dd2f6170f68f834db582fca153be022e76942fdd25ddf2a2da46f89b81d",
+    "7b_32layer": {  # streaming kernel: FETCH 1,049,534.5 KiB x 1.99998 + WRITE 1,536.0 KiB
+        "kernel": "balanced", "bytes": 2_150_998_026,
+        "sources_sha256": "f62bfc6f2a1af97a77860cb808630ee9eb70c636de886a2265a5abc04888ed1d",
         "summary": "profiles/decode_balanced_kernel_7b_32layer.md"},
 }
 
