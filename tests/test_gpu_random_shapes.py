@@ -114,3 +114,26 @@ def test_balanced_pass_with_any_head_count(hkv, g, batch, _gpu):
     o = H.oracle_bookkeeping(cfg, seed)
     check_bookkeeping(side, o)
     check_layers(cfg, side, o, list(range(cfg.batch)), range(cfg.layers), whole_pool=True)
+
+
+# The vector-ALU balanced pass (one query head per kv head: the LDS tile ring)
+# in each of its instances: fused step or not, head_dim 64 or 128, plain,
+# shared blocks through the L2, or after the prefix kernel.
+VALU_FORMS = [(fused, dim, shared, kv) for fused in (True, False) for dim in (64, 128)
+              for shared, kv in ((None, "f16"), ("l2", "bf16"), (True, "f16"))]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("fused,dim,shared,kv", VALU_FORMS)
+def test_vector_balanced_pass_forms(fused, dim, shared, kv, _gpu):
+    from tests.test_gpu_parity import check_bookkeeping, check_layers
+
+    seed = 900 + dim + (7 if fused else 0) + (3 if shared == "l2" else 5 if shared else 0)
+    cfg = W.Config(f"valu{dim}", 2, 20, 6, 6, dim, kv, kv, ("uniform", 1, 900),
+                   share_prefix_tokens=48 if shared is not None else 0, balanced=True)
+    say(f"vector balanced: fused={fused} D={dim} shared={shared} kv={kv} seed={seed}")
+    side = H.build_product(cfg, seed=seed, fused=fused, shared_prefix=shared)
+    torch.cuda.synchronize()
+    o = H.oracle_bookkeeping(cfg, seed)
+    check_bookkeeping(side, o)
+    check_layers(cfg, side, o, list(range(cfg.batch)), range(cfg.layers), whole_pool=True)
