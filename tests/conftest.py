@@ -25,3 +25,18 @@ def gpu_available() -> bool:
 def require_gpu():
     if not gpu_available():
         pytest.fail("GPU test selected but no GPU is visible")
+
+
+@pytest.fixture(autouse=True)
+def _release_device_memory():
+    """After each test that used the GPU, hand torch's cached device memory
+    back to the driver. The driver reclaims released memory in the background
+    (about 35 s per 100 GB on MI355X, during which bandwidth-bound kernels run
+    about 3% slower), so a session that held tens of GB until its exit would
+    leave that work to whatever runs next on the GPU; released test by test, it
+    overlaps the rest of the session."""
+    yield
+    torch = sys.modules.get("torch")
+    if torch is not None and torch.cuda.is_initialized():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
